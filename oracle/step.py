@@ -1,0 +1,61 @@
+"""One whole step: draft -> confidence -> [schedule] -> verify, float64.
+
+[blog] "整体架构" and "硬件感知前缀调度器", [summary] sections 3-4: the parallel
+backbone's outputs (U_k, h_k) enter a sequential head that drafts gamma tokens,
+the confidence head scores them, the scheduler picks each request's verify
+length K_b, and the target's scores decide acceptance.  Without a scheduler
+every request verifies all gamma positions.
+
+``rows`` restricts the computation to a subset of requests (all steps but the
+scheduler are independent per request); it is refused when a scheduler runs,
+since the scheduler needs every request's survival values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .markov import draft_markov, DraftResult
+from .confidence import confidence, ConfidenceResult
+from .schedule import schedule, ScheduleResult
+from .verify import verify, VerifyResult
+
+
+@dataclasses.dataclass
+class StepResult:
+    rows: np.ndarray
+    draft: DraftResult
+    conf: Optional[ConfidenceResult]
+    sched: Optional[ScheduleResult]
+    ver: VerifyResult
+
+
+def run_step(inp: dict, seed: int, rows: Optional[Sequence[int]] = None) -> StepResult:
+    wl = inp["wl"]
+    B = inp["U"].shape[0]
+    rows = np.arange(B) if rows is None else np.asarray(rows, dtype=np.int64)
+    has_sched = inp.get("sps") is not None
+    if has_sched and len(rows) != B:
+        raise ValueError("a scheduled step needs every request")
+
+    def sel(x):
+        return x if len(rows) == B else x[rows]
+
+    T = inp["temperature"]
+    d = draft_markov(sel(inp["U"]), inp["W1"], inp["W2"], sel(inp["anchor"]),
+                     sel(inp["req_ids"]), T, seed, wl.gamma)
+    c = None
+    if inp.get("h") is not None:
+        c = confidence(sel(inp["h"]), inp["E"], sel(inp["anchor"]), d.tokens, inp["wc"],
+                       inp["bc"], inp.get("sts_T"))
+    s = None
+    K = None
+    if has_sched:
+        # the scheduler consumes the survival values as the fp32 the boundary carries
+        s = schedule(c.surv.astype(np.float32), inp["sps"])
+        K = s.K
+    v = verify(sel(inp["target"]), d.tokens, d.lse, d.ytok, sel(inp["U"]), inp["W1"], inp["W2"],
+               sel(inp["anchor"]), K, sel(inp["req_ids"]), T, seed, wl.gamma)
+    return StepResult(rows, d, c, s, v)
