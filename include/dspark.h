@@ -1,0 +1,192 @@
+/*
+ * libdspark -- the per-step draft/verify hot path of DSpark's
+ * confidence-scheduled speculative decoding, for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [blog]     "DSpark：半自回归生成与置信度调度的投机解码"
+ *              (pinghaoyang.com.cn/aigc/posts/dspark/)
+ *   [teardown] "拒绝盲猜与算力空转：深度拆解 DeepSeek 开源投机采样方案 DeepSpec & DSpark"
+ *              (val213.github.io/2026/06/28/DSpark&DSpec/)
+ *   [summary]  "DeepSeek-AI与北京大学联手破局：AI聊天机器人'慢速打字'的终极解决方案"
+ *              (techwalker.com/2026/0716/3193540.shtml)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor argument is a device pointer to caller-owned memory on the
+ *    context's device.  The library never frees, keeps or reallocates it.
+ *  - Calls are asynchronous on `stream`: they enqueue kernels and return.
+ *    Outputs are valid once the stream reaches the call.  Calls on one
+ *    context must not run concurrently on different streams (the context's
+ *    workspace is shared); a context is used by one host thread at a time.
+ *  - Row-major layouts; strides are in elements.  Logit rows (U, target) are
+ *    contiguous over the vocabulary and 16-byte aligned.
+ *  - Tokens and request ids are 32-bit.  Request ids are read as unsigned.
+ *  - Random numbers come from a counter-based hash keyed on
+ *    (seed, request id, 1-based position, purpose): SplitMix64's output
+ *    function builds the 64-bit row key, MurmurHash3's fmix32 mixes each
+ *    vocabulary index, u = (2*(h>>9)+1)*2^-24.  Results are therefore a
+ *    deterministic function of the inputs and the seed (bitwise repeatable).
+ *  - temperature == 0 selects greedy (argmax) drafting and verification.
+ *  - Return codes: DSPARK_OK, or DSPARK_EINVAL (bad argument, checked on the
+ *    host before anything is enqueued), DSPARK_EHIP (a HIP call failed),
+ *    DSPARK_ENOMEM (workspace could not grow).  The message is available
+ *    from dspark_last_error.  Kernels that meet an out-of-range token id or
+ *    verify length clamp it and raise a device error flag, reported as
+ *    DSPARK_EDEVICE by dspark_check.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dspark_ctx dspark_ctx;
+
+enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = 1,
+  DSPARK_EHIP = 2,
+  DSPARK_ENOMEM = 3,
+  DSPARK_EDEVICE = 4
+};
+
+/* Weight element types of the Markov head. */
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+/* Library ABI version (major * 100 + minor). */
+int dspark_version(void);
+
+/* Create a context bound to HIP device `device`.  It owns a growable device
+ * workspace (cross-block partial results, scheduler scratch), a cache of
+ * instantiated HIP graphs for the draft loop, and a device error flag.
+ * Returns DSPARK_EINVAL for a null `out`, DSPARK_EHIP if the device cannot be
+ * used.  On failure *out is set to NULL. */
+int dspark_create(dspark_ctx** out, int device);
+
+/* Release everything the context owns.  Waits for the device first.  NULL is
+ * accepted. */
+void dspark_destroy(dspark_ctx* ctx);
+
+/* Message of the last failing call on this context ("" if none).  The
+ * pointer stays valid until the next call on the context. */
+const char* dspark_last_error(const dspark_ctx* ctx);
+
+/* Synchronise `stream`, read and clear the device error flag.  Returns
+ * DSPARK_EDEVICE if any kernel since the last check met an out-of-range
+ * token id or verify length (the message names which), DSPARK_EHIP on a HIP
+ * error, else DSPARK_OK. */
+int dspark_check(dspark_ctx* ctx, hipStream_t stream);
+
+/* Semi-autoregressive draft with the Markov head.
+ *
+ * [blog] "形式化定义", "整体架构" and "Markov Head：一阶转移偏置"; [teardown]
+ * "DSpark 的解法": for k = 1..gamma and every request b,
+ *     h      = W1[x_{k-1}]                 (x_0 = anchor[b])
+ *     z_v    = U[b][k-1][v] + sum_i h_i * W2col_v[i]
+ *     y_v    = z_v / T                     (T = temperature; y = z if T == 0)
+ *     x_k    = argmin-index argmax_v z_v                     if T == 0
+ *            = argmin-index argmax_v (y_v + G(seed, req_b, k, DRAFT, v))  else
+ * where G is a standard Gumbel variate, so x_k ~ softmax(y) (Gumbel-max).
+ * x_k feeds position k+1.  Outputs per (b, k):
+ *     tokens[b][k-1] = x_k
+ *     lse[b][k-1]    = ln sum_v exp(y_v)      (of z when T == 0)
+ *     ytok[b][k-1]   = y_{x_k}
+ * so that ln p_d(x_k) = ytok - lse.
+ *
+ * B >= 1; 1 <= gamma <= 32; V >= 16, V % 16 == 0; r in {32, 64, 128, 256}.
+ * U:      float [B][>= gamma][V] at U + b*u_stride_b + (k-1)*u_stride_k;
+ *         strides are multiples of 4 and the pointer 16-byte aligned.
+ * W1:     [V][r] row-major (token -> rank-r vector), dtype wdtype.
+ * W2:     the r x V matrix W2 stored column-major, i.e. an array [V][r] whose
+ *         row v is column v (an LM-head layout), dtype wdtype.  Both weight
+ *         pointers 16-byte aligned.
+ * anchor: int32 [B]; req_ids: uint32 [B] or NULL (then req = b).
+ * tokens: int32 [B][gamma]; lse, ytok: float [B][gamma].
+ * Logits must be finite.  Errors: DSPARK_EINVAL for shapes/pointers/
+ * alignment/temperature < 0 or non-finite. */
+int dspark_draft_markov(dspark_ctx* ctx, hipStream_t stream,
+                        int B, int gamma, int V, int r, dspark_dtype wdtype,
+                        const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                        const void* W1, const void* W2,
+                        const int32_t* anchor, const uint32_t* req_ids,
+                        float temperature, uint64_t seed,
+                        int32_t* tokens, float* lse, float* ytok);
+
+/* Confidence head with sequential temperature scaling and survival products.
+ *
+ * [blog] "置信度头：预测自己的命运" and "校准问题：原始置信度不可靠"; [summary]
+ * section 4; [teardown] "硬件感知前缀调度器" (survival product):
+ *     l_k   = sum_i wc[i] h[b][k-1][i] + sum_j wc[d_h + j] E[x_{k-1}][j] + bc
+ *     c_k   = 1 / (1 + exp(-l_k / T_k))        (T_k = sts_T[k-1], or 1)
+ *     a_k   = c_1 * c_2 * ... * c_k
+ * with x_0 = anchor[b], x_k = tokens[b][k-1].
+ * h: bf16 [B][gamma][d_h]; E: bf16 [V][d_e]; wc: bf16 [d_h + d_e];
+ * d_h, d_e multiples of 8, >= 8; h, E, wc 16-byte aligned.
+ * sts_T: float [gamma] or NULL; conf, surv: float [B][gamma]. */
+int dspark_confidence(dspark_ctx* ctx, hipStream_t stream,
+                      int B, int gamma, int V, int d_h, int d_e,
+                      const void* h, const void* E,
+                      const int32_t* anchor, const int32_t* tokens,
+                      const void* wc, float bc, const float* sts_T,
+                      float* conf, float* surv);
+
+/* Hardware-aware prefix scheduler: greedy admission with early stop.
+ *
+ * [blog] "硬件感知前缀调度器" (steps 1-4); [summary] sections 4-5.  All (b, j)
+ * candidates are sorted by (surv[b][j-1] descending, b ascending, j
+ * ascending) and admitted one at a time; after admitting n of them
+ *     Theta_n = (B + S_n) * sps[B + n - 1],   S_n = sum of admitted survivals,
+ *     Theta_0 = B * sps[B - 1];
+ * admission stops at the first n with Theta_n <= Theta_{n-1} or with
+ * B + n > n_sps.  K[b] = number of admitted candidates of request b (always
+ * a prefix 1..K[b]).  Sums and Theta are formed in float64.
+ * surv: float [B][gamma], values in [0, 1] (non-finite or negative read as
+ * 0); sps: float [n_sps], sps[N-1] the verify steps/s at N tokens.
+ * 1 <= B <= n_sps; B * gamma <= 4096.
+ * K: int32 [B]; n_selected: int32 [1]; theta: double [1] (Theta at the
+ * admitted set). */
+int dspark_schedule(dspark_ctx* ctx, hipStream_t stream,
+                    int B, int gamma, const float* surv,
+                    const float* sps, int n_sps,
+                    int32_t* K, int32_t* n_selected, double* theta);
+
+/* Lossless speculative verification with residual resampling and a bonus.
+ *
+ * [blog] "形式化定义"; [summary] sections 1 and 4.  For request b with verify
+ * length K_b (K[b], or gamma if K is NULL), positions k = 1..K_b in order:
+ *     T == 0: keep x_k iff x_k == argmin-index argmax_v target[b][k-1][v];
+ *             otherwise emit that argmax and stop.
+ *     T  > 0: p_t = softmax(target[b][k-1] / T), p_d from the draft
+ *             (ln p_d(x_k) = ytok - lse); keep x_k iff
+ *             u(seed, req_b, k, ACCEPT, 0) < p_t(x_k) / p_d(x_k);
+ *             at the first rejection emit
+ *             argmax_{v: r_v > 0} (ln r_v + G(seed, req_b, k, RESID, v)),
+ *             r_v = max(0, p_t(v) - p_d(v)), recomputing the draft row from
+ *             U, W1, W2 (if no r_v > 0, sample p_t with the same stream).
+ * If all K_b drafts are kept, emit the bonus token from target row K_b + 1
+ * (its argmax, or a Gumbel-max sample with purpose BONUS at position K_b+1).
+ * Outputs: accept_len[b] = number kept; out_tokens[b][0..accept_len] = the
+ * kept drafts followed by the emitted token, then -1 up to gamma.
+ * target: float [B][>= gamma+1][V] (same stride rules as U).  The other
+ * arguments are those given to / returned by dspark_draft_markov; K: int32
+ * [B] or NULL (values outside 0..gamma are clamped and flagged).
+ * accept_len: int32 [B]; out_tokens: int32 [B][gamma+1]. */
+int dspark_verify(dspark_ctx* ctx, hipStream_t stream,
+                  int B, int gamma, int V, int r, dspark_dtype wdtype,
+                  const float* target, int64_t t_stride_b, int64_t t_stride_k,
+                  const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                  const void* W1, const void* W2, const int32_t* anchor,
+                  const int32_t* tokens, const float* lse, const float* ytok,
+                  const int32_t* K, const uint32_t* req_ids,
+                  float temperature, uint64_t seed,
+                  int32_t* accept_len, int32_t* out_tokens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

@@ -1,0 +1,580 @@
+// C ABI of libdspark: context, argument checks, workspace, launch plans and
+// the HIP-graph cache of the sequential draft loop.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dspark.h"
+#include "common.hpp"
+#include "internal.hpp"
+
+using namespace dspark;
+
+namespace {
+
+constexpr int kVersion = 100;
+constexpr int kMaxGamma = 32;
+
+struct KernelNode {
+  const void* fn;
+  dim3 grid, block;
+  // argument storage: the largest argument block
+  alignas(16) unsigned char args[sizeof(SweepArgs) > sizeof(CombineArgs) ? sizeof(SweepArgs)
+                                                                        : sizeof(CombineArgs)];
+};
+
+// Instantiated graph of one draft loop shape; node parameters are rewritten
+// before each launch, so one graph serves every buffer set and seed.
+struct DraftGraph {
+  int B = 0, gamma = 0, V = 0, r = 0, wdtype = -1, mode = -1, grid = 0, n_vc = 0;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  std::vector<hipGraphNode_t> nodes;
+};
+
+}  // namespace
+
+struct dspark_ctx {
+  int device = 0;
+  int cu_count = 256;
+  std::string err;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int32_t* dev_err = nullptr;
+  bool use_graph = true;
+  std::vector<DraftGraph> graphs;
+};
+
+namespace {
+
+int fail(dspark_ctx* c, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (c) c->err = buf;
+  return code;
+}
+
+#define DSPARK_HIP(c, call)                                                             \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail((c), DSPARK_EHIP, "%s failed: %s", #call, hipGetErrorString(e_));     \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+// Grow the workspace to at least `bytes`.  Growing waits for the device so
+// that no enqueued kernel still uses the old buffer.
+int ensure_ws(dspark_ctx* c, size_t bytes) {
+  if (bytes <= c->ws_bytes) return DSPARK_OK;
+  DSPARK_HIP(c, hipDeviceSynchronize());
+  if (c->ws) (void)hipFree(c->ws);
+  c->ws = nullptr;
+  c->ws_bytes = 0;
+  size_t want = bytes + bytes / 4;
+  if (hipMalloc(&c->ws, want) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, DSPARK_ENOMEM, "workspace allocation of %zu bytes failed", want);
+  }
+  c->ws_bytes = want;
+  return DSPARK_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Vocabulary-sweep plan: aim at eight waves per CU, at least four 16-wide
+// tiles per wave, and a grid that is a multiple of the XCD count.
+struct SweepPlan {
+  int n_rg, n_vc, n_tiles, grid;
+};
+
+SweepPlan plan_sweep(const dspark_ctx* c, int B, int V) {
+  SweepPlan p;
+  p.n_rg = (B + kRowsPerWave - 1) / kRowsPerWave;
+  p.n_tiles = V / kTileV;
+  const int target_waves = 8 * c->cu_count;
+  int n_vc = target_waves / p.n_rg;
+  const int max_vc = p.n_tiles / 4 > 0 ? p.n_tiles / 4 : 1;
+  if (n_vc > max_vc) n_vc = max_vc;
+  if (n_vc < 1) n_vc = 1;
+  p.n_vc = n_vc;
+  const long waves = (long)p.n_rg * p.n_vc;
+  long grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  grid = (grid + 7) / 8 * 8;
+  p.grid = (int)grid;
+  return p;
+}
+
+int plan_rows_chunks(int rows, int V) {
+  int n = (2048 + rows - 1) / rows;
+  const int by_len = (V / 4) / 1024;      // at least ~1024 float4 per chunk
+  if (n > by_len) n = by_len;
+  if (n > 64) n = 64;
+  if (n < 1) n = 1;
+  return n;
+}
+
+int check_stream_rows(dspark_ctx* c, const char* name, const float* p, int64_t sb, int64_t sk, int rows,
+                      int V) {
+  if (!p) return fail(c, DSPARK_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(c, DSPARK_EINVAL, "%s must be 16-byte aligned", name);
+  if ((sb & 3) || (sk & 3)) return fail(c, DSPARK_EINVAL, "%s strides must be multiples of 4", name);
+  if (sk < V) return fail(c, DSPARK_EINVAL, "%s position stride %lld < V", name, (long long)sk);
+  if (sb < (int64_t)rows * sk) return fail(c, DSPARK_EINVAL, "%s request stride too small", name);
+  return DSPARK_OK;
+}
+
+int check_markov_shape(dspark_ctx* c, int B, int gamma, int V, int r, int wdtype, float T) {
+  if (B < 1) return fail(c, DSPARK_EINVAL, "B must be >= 1 (got %d)", B);
+  if (gamma < 1 || gamma > kMaxGamma) return fail(c, DSPARK_EINVAL, "gamma must be in 1..%d", kMaxGamma);
+  if (V < kTileV || V % kTileV) return fail(c, DSPARK_EINVAL, "V must be a positive multiple of 16");
+  if (wdtype != DSPARK_F32 && wdtype != DSPARK_BF16) return fail(c, DSPARK_EINVAL, "unknown weight dtype");
+  if (!sweep_kernel(wdtype, r, kModeDraftGreedy))
+    return fail(c, DSPARK_EINVAL, "r must be one of 32, 64, 128, 256 (got %d)", r);
+  if (!(T >= 0.0f) || !std::isfinite(T)) return fail(c, DSPARK_EINVAL, "temperature must be finite and >= 0");
+  return DSPARK_OK;
+}
+
+hipError_t launch(const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t s) {
+  void* params[] = {arg};
+  return hipLaunchKernel(fn, grid, block, params, 0, s);
+}
+
+template <typename A>
+void set_node(KernelNode& n, const void* fn, dim3 grid, dim3 block, const A& a) {
+  static_assert(sizeof(A) <= sizeof(n.args), "argument block too large");
+  n.fn = fn;
+  n.grid = grid;
+  n.block = block;
+  memcpy(n.args, &a, sizeof(A));
+}
+
+hipKernelNodeParams node_params(KernelNode& n, void** holder) {
+  hipKernelNodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.func = const_cast<void*>(n.fn);
+  p.gridDim = n.grid;
+  p.blockDim = n.block;
+  p.sharedMemBytes = 0;
+  holder[0] = n.args;
+  p.kernelParams = holder;
+  p.extra = nullptr;
+  return p;
+}
+
+// Run a chain of kernel nodes on `stream`, through a cached graph when
+// enabled.
+int run_chain(dspark_ctx* c, hipStream_t stream, std::vector<KernelNode>& nodes, int B, int gamma, int V,
+              int r, int wdtype, int mode, int grid, int n_vc) {
+  if (!c->use_graph) {
+    for (auto& n : nodes) DSPARK_HIP(c, launch(n.fn, n.grid, n.block, n.args, stream));
+    return DSPARK_OK;
+  }
+  DraftGraph* g = nullptr;
+  for (auto& x : c->graphs)
+    if (x.B == B && x.gamma == gamma && x.V == V && x.r == r && x.wdtype == wdtype && x.mode == mode &&
+        x.grid == grid && x.n_vc == n_vc && x.nodes.size() == nodes.size())
+      g = &x;
+  if (!g) {
+    DraftGraph ng;
+    ng.B = B;
+    ng.gamma = gamma;
+    ng.V = V;
+    ng.r = r;
+    ng.wdtype = wdtype;
+    ng.mode = mode;
+    ng.grid = grid;
+    ng.n_vc = n_vc;
+    DSPARK_HIP(c, hipGraphCreate(&ng.graph, 0));
+    hipGraphNode_t prev = nullptr;
+    for (auto& n : nodes) {
+      void* holder[1];
+      hipKernelNodeParams p = node_params(n, holder);
+      hipGraphNode_t node;
+      hipError_t e = hipGraphAddKernelNode(&node, ng.graph, prev ? &prev : nullptr, prev ? 1 : 0, &p);
+      if (e != hipSuccess) {
+        (void)hipGraphDestroy(ng.graph);
+        return fail(c, DSPARK_EHIP, "hipGraphAddKernelNode failed: %s", hipGetErrorString(e));
+      }
+      ng.nodes.push_back(node);
+      prev = node;
+    }
+    hipError_t e = hipGraphInstantiate(&ng.exec, ng.graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+      (void)hipGraphDestroy(ng.graph);
+      return fail(c, DSPARK_EHIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+    }
+    c->graphs.push_back(std::move(ng));
+    g = &c->graphs.back();
+  } else {
+    for (size_t i = 0; i < nodes.size(); ++i) {
+      void* holder[1];
+      hipKernelNodeParams p = node_params(nodes[i], holder);
+      DSPARK_HIP(c, hipGraphExecKernelNodeSetParams(g->exec, g->nodes[i], &p));
+    }
+  }
+  DSPARK_HIP(c, hipGraphLaunch(g->exec, stream));
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_version(void) { return kVersion; }
+
+int dspark_create(dspark_ctx** out, int device) {
+  if (!out) return DSPARK_EINVAL;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) {
+    (void)hipGetLastError();
+    return DSPARK_EHIP;
+  }
+  DeviceGuard dg(device);
+  if (!dg.ok) return DSPARK_EHIP;
+  dspark_ctx* c = new dspark_ctx();
+  c->device = device;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
+    c->cu_count = prop.multiProcessorCount;
+  if (hipMalloc(&c->dev_err, 256) != hipSuccess || hipMemset(c->dev_err, 0, 256) != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return DSPARK_EHIP;
+  }
+  const char* g = getenv("DSPARK_GRAPH");
+  if (g && g[0] == '0') c->use_graph = false;
+  *out = c;
+  return DSPARK_OK;
+}
+
+void dspark_destroy(dspark_ctx* c) {
+  if (!c) return;
+  {
+    DeviceGuard dg(c->device);
+    (void)hipDeviceSynchronize();
+    for (auto& g : c->graphs) {
+      if (g.exec) (void)hipGraphExecDestroy(g.exec);
+      if (g.graph) (void)hipGraphDestroy(g.graph);
+    }
+    if (c->ws) (void)hipFree(c->ws);
+    if (c->dev_err) (void)hipFree(c->dev_err);
+  }
+  delete c;
+}
+
+const char* dspark_last_error(const dspark_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+int dspark_check(dspark_ctx* c, hipStream_t stream) {
+  if (!c) return DSPARK_EINVAL;
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  DSPARK_HIP(c, hipStreamSynchronize(stream));
+  int32_t flag = 0;
+  DSPARK_HIP(c, hipMemcpy(&flag, c->dev_err, sizeof(flag), hipMemcpyDeviceToHost));
+  if (flag) {
+    DSPARK_HIP(c, hipMemset(c->dev_err, 0, sizeof(int32_t)));
+    return fail(c, DSPARK_EDEVICE, "device error flag 0x%x:%s%s", flag,
+                (flag & kErrToken) ? " token id out of range" : "",
+                (flag & kErrK) ? " verify length out of range" : "");
+  }
+  c->err.clear();
+  return DSPARK_OK;
+}
+
+int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r,
+                        dspark_dtype wdtype, const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                        const void* W1, const void* W2, const int32_t* anchor, const uint32_t* req_ids,
+                        float temperature, uint64_t seed, int32_t* tokens, float* lse, float* ytok) {
+  if (!c) return DSPARK_EINVAL;
+  int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
+  if (rc) return rc;
+  if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, gamma, V))) return rc;
+  if (!W1 || !W2 || !anchor || !tokens || !lse || !ytok)
+    return fail(c, DSPARK_EINVAL, "null pointer argument");
+  if (!aligned16(W1) || !aligned16(W2)) return fail(c, DSPARK_EINVAL, "W1/W2 must be 16-byte aligned");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+
+  const bool greedy = temperature == 0.0f;
+  const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
+  const SweepPlan pl = plan_sweep(c, B, V);
+  const size_t npart = (size_t)B * pl.n_vc;
+  const size_t off_pi = align256(npart * sizeof(float4));
+  if ((rc = ensure_ws(c, off_pi + align256(npart * sizeof(int2))))) return rc;
+  float4* pf = reinterpret_cast<float4*>(c->ws);
+  int2* pi = reinterpret_cast<int2*>(static_cast<char*>(c->ws) + off_pi);
+
+  SweepArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.B = B;
+  sa.gamma = gamma;
+  sa.V = V;
+  sa.n_rg = pl.n_rg;
+  sa.n_vc = pl.n_vc;
+  sa.n_tiles = pl.n_tiles;
+  sa.xcd_remap = 1;
+  sa.U = U;
+  sa.usb = u_stride_b;
+  sa.usk = u_stride_k;
+  sa.W1 = W1;
+  sa.W2 = W2;
+  sa.anchor = anchor;
+  sa.tokens = tokens;
+  sa.req = req_ids;
+  sa.invT = greedy ? 1.0f : 1.0f / temperature;
+  sa.s2 = greedy ? kLog2e : kLog2e / temperature;
+  sa.seed = seed;
+  sa.pf = pf;
+  sa.pi = pi;
+  sa.err = c->dev_err;
+  CombineArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.B = B;
+  ca.gamma = gamma;
+  ca.V = V;
+  ca.n_vc = pl.n_vc;
+  ca.greedy = greedy;
+  ca.invT = sa.invT;
+  ca.pf = pf;
+  ca.pi = pi;
+  ca.tokens = tokens;
+  ca.lse = lse;
+  ca.ytok = ytok;
+  ca.err = c->dev_err;
+
+  const void* kfn = sweep_kernel((int)wdtype, r, mode);
+  std::vector<KernelNode> nodes(2 * gamma);
+  for (int k = 1; k <= gamma; ++k) {
+    sa.k = k;
+    ca.k = k;
+    set_node(nodes[2 * (k - 1)], kfn, dim3(pl.grid), dim3(256), sa);
+    set_node(nodes[2 * (k - 1) + 1], combine_draft_kernel(), dim3(B), dim3(64), ca);
+  }
+  return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode, pl.grid, pl.n_vc);
+}
+
+int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int d_h, int d_e,
+                      const void* h, const void* E, const int32_t* anchor, const int32_t* tokens,
+                      const void* wc, float bc, const float* sts_T, float* conf, float* surv) {
+  if (!c) return DSPARK_EINVAL;
+  if (B < 1 || gamma < 1 || gamma > kMaxGamma || V < 1)
+    return fail(c, DSPARK_EINVAL, "bad shape B=%d gamma=%d V=%d", B, gamma, V);
+  if (d_h < 8 || d_e < 8 || (d_h & 7) || (d_e & 7))
+    return fail(c, DSPARK_EINVAL, "d_h and d_e must be positive multiples of 8");
+  if (!h || !E || !anchor || !tokens || !wc || !conf || !surv)
+    return fail(c, DSPARK_EINVAL, "null pointer argument");
+  if (!aligned16(h) || !aligned16(E) || !aligned16(wc))
+    return fail(c, DSPARK_EINVAL, "h, E and wc must be 16-byte aligned");
+  if (!std::isfinite(bc)) return fail(c, DSPARK_EINVAL, "bc must be finite");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  ConfArgs a;
+  memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.dh = d_h;
+  a.de = d_e;
+  a.h = static_cast<const uint16_t*>(h);
+  a.E = static_cast<const uint16_t*>(E);
+  a.anchor = anchor;
+  a.tokens = tokens;
+  a.wc = static_cast<const uint16_t*>(wc);
+  a.bc = bc;
+  a.sts = sts_T;
+  a.conf = conf;
+  a.surv = surv;
+  a.err = c->dev_err;
+  DSPARK_HIP(c, launch(confidence_kernel(), dim3(B * gamma), dim3(256), &a, stream));
+  DSPARK_HIP(c, launch(survival_kernel(), dim3((B + 255) / 256), dim3(256), &a, stream));
+  return DSPARK_OK;
+}
+
+int dspark_schedule(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv,
+                    const float* sps, int n_sps, int32_t* K, int32_t* n_selected, double* theta) {
+  if (!c) return DSPARK_EINVAL;
+  if (B < 1 || gamma < 1 || gamma > kMaxGamma) return fail(c, DSPARK_EINVAL, "bad shape B=%d gamma=%d", B, gamma);
+  if ((long)B * gamma > 4096) return fail(c, DSPARK_EINVAL, "B * gamma must be <= 4096");
+  if (n_sps < B) return fail(c, DSPARK_EINVAL, "n_sps (%d) must be >= B (%d)", n_sps, B);
+  if (!surv || !sps || !K || !n_selected || !theta) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  SchedArgs a;
+  a.B = B;
+  a.gamma = gamma;
+  a.n_sps = n_sps;
+  a.surv = surv;
+  a.sps = sps;
+  a.K = K;
+  a.n_selected = n_selected;
+  a.theta = theta;
+  DSPARK_HIP(c, launch(schedule_kernel(), dim3(1), dim3(kSchedThreads), &a, stream));
+  return DSPARK_OK;
+}
+
+int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
+                  const float* target, int64_t t_stride_b, int64_t t_stride_k, const float* U,
+                  int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
+                  const int32_t* anchor, const int32_t* tokens, const float* lse, const float* ytok,
+                  const int32_t* K, const uint32_t* req_ids, float temperature, uint64_t seed,
+                  int32_t* accept_len, int32_t* out_tokens) {
+  if (!c) return DSPARK_EINVAL;
+  int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
+  if (rc) return rc;
+  if ((rc = check_stream_rows(c, "target", target, t_stride_b, t_stride_k, gamma + 1, V))) return rc;
+  const bool greedy = temperature == 0.0f;
+  if (!greedy && (rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, gamma, V))) return rc;
+  if (!tokens || !accept_len || !out_tokens) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  if (!greedy && (!W1 || !W2 || !anchor || !lse || !ytok))
+    return fail(c, DSPARK_EINVAL, "sampling verification needs U, W1, W2, anchor, lse and ytok");
+  if (!greedy && (!aligned16(W1) || !aligned16(W2)))
+    return fail(c, DSPARK_EINVAL, "W1/W2 must be 16-byte aligned");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+
+  const int rows = B * (gamma + 1);
+  const int n_chunks = plan_rows_chunks(rows, V);
+  const SweepPlan pl = plan_sweep(c, B, V);
+  const size_t n_rowpart = (size_t)rows * n_chunks;
+  const size_t n_respart = (size_t)B * pl.n_vc;
+  size_t off = 0;
+  const size_t off_rpf = off;
+  off += align256(n_rowpart * sizeof(float4));
+  const size_t off_rpi = off;
+  off += align256(n_rowpart * sizeof(int));
+  const size_t off_spf = off;
+  off += align256(n_respart * sizeof(float4));
+  const size_t off_spi = off;
+  off += align256(n_respart * sizeof(int2));
+  const size_t off_rk = off;
+  off += align256((size_t)B * sizeof(int32_t));
+  const size_t off_rlt = off;
+  off += align256((size_t)B * sizeof(float));
+  if ((rc = ensure_ws(c, off))) return rc;
+  char* ws = static_cast<char*>(c->ws);
+  float4* rpf = reinterpret_cast<float4*>(ws + off_rpf);
+  int* rpi = reinterpret_cast<int*>(ws + off_rpi);
+  float4* spf = reinterpret_cast<float4*>(ws + off_spf);
+  int2* spi = reinterpret_cast<int2*>(ws + off_spi);
+  int32_t* resid_k = reinterpret_cast<int32_t*>(ws + off_rk);
+  float* resid_lt = reinterpret_cast<float*>(ws + off_rlt);
+
+  const float invT = greedy ? 1.0f : 1.0f / temperature;
+  RowsArgs ra;
+  memset(&ra, 0, sizeof(ra));
+  ra.B = B;
+  ra.gamma = gamma;
+  ra.V = V;
+  ra.n_chunks = n_chunks;
+  ra.greedy = greedy;
+  ra.T = target;
+  ra.tsb = t_stride_b;
+  ra.tsk = t_stride_k;
+  ra.K = K;
+  ra.req = req_ids;
+  ra.s2 = greedy ? kLog2e : kLog2e / temperature;
+  ra.seed = seed;
+  ra.pf = rpf;
+  ra.pi = rpi;
+  ra.err = c->dev_err;
+  DSPARK_HIP(c, launch(verify_rows_kernel(), dim3(n_chunks, rows), dim3(256), &ra, stream));
+
+  DecideArgs da;
+  memset(&da, 0, sizeof(da));
+  da.B = B;
+  da.gamma = gamma;
+  da.V = V;
+  da.n_chunks = n_chunks;
+  da.greedy = greedy;
+  da.T = target;
+  da.tsb = t_stride_b;
+  da.tsk = t_stride_k;
+  da.K = K;
+  da.req = req_ids;
+  da.tokens = tokens;
+  da.lse = lse;
+  da.ytok = ytok;
+  da.invT = invT;
+  da.seed = seed;
+  da.pf = rpf;
+  da.pi = rpi;
+  da.accept_len = accept_len;
+  da.out_tokens = out_tokens;
+  da.resid_k = resid_k;
+  da.resid_lt = resid_lt;
+  da.err = c->dev_err;
+  DSPARK_HIP(c, launch(verify_decide_kernel(), dim3(B), dim3(64), &da, stream));
+  if (greedy) return DSPARK_OK;
+
+  SweepArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.B = B;
+  sa.gamma = gamma;
+  sa.V = V;
+  sa.k = 0;
+  sa.n_rg = pl.n_rg;
+  sa.n_vc = pl.n_vc;
+  sa.n_tiles = pl.n_tiles;
+  sa.xcd_remap = 1;
+  sa.U = U;
+  sa.usb = u_stride_b;
+  sa.usk = u_stride_k;
+  sa.T = target;
+  sa.tsb = t_stride_b;
+  sa.tsk = t_stride_k;
+  sa.W1 = W1;
+  sa.W2 = W2;
+  sa.anchor = anchor;
+  sa.tokens = tokens;
+  sa.req = req_ids;
+  sa.resid_k = resid_k;
+  sa.lse = lse;
+  sa.resid_lt = resid_lt;
+  sa.invT = invT;
+  sa.s2 = kLog2e / temperature;
+  sa.seed = seed;
+  sa.pf = spf;
+  sa.pi = spi;
+  sa.err = c->dev_err;
+  DSPARK_HIP(c, launch(sweep_kernel((int)wdtype, r, kModeResidual), dim3(pl.grid), dim3(256), &sa, stream));
+
+  CombineArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.B = B;
+  ca.gamma = gamma;
+  ca.V = V;
+  ca.n_vc = pl.n_vc;
+  ca.pf = spf;
+  ca.pi = spi;
+  ca.resid_k = resid_k;
+  ca.accept_len = accept_len;
+  ca.out_tokens = out_tokens;
+  ca.err = c->dev_err;
+  DSPARK_HIP(c, launch(combine_resid_kernel(), dim3(B), dim3(64), &ca, stream));
+  return DSPARK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// Shared device helpers of libdspark: counter-based hash, bf16 fragments,
+// base-2 online softmax and arg-max merge rules.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// Purposes of the random streams.
+constexpr uint32_t kDraft = 1, kAccept = 2, kResid = 3, kBonus = 4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Device error flag bits.
+constexpr int kErrToken = 1;    // a token id outside [0, V)
+constexpr int kErrK = 2;        // a verify length outside [0, gamma]
+
+// ---------------------------------------------------------------------------
+// Counter-based random numbers.
+//
+// Row key: the output function of SplitMix64 (Steele, Lea & Flood, 2014) is
+// applied three times, folding in the request id, then (position << 8 |
+// purpose).  Element v of a row: MurmurHash3's 32-bit finalizer of
+// ((v * 0x9E3779B9) ^ lo(key)) + hi(key).  Uniform: (2 * (h >> 9) + 1) * 2^-24.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__host__ __device__ __forceinline__ uint64_t stream_key(uint64_t seed, uint32_t req, uint32_t pos,
+                                                        uint32_t purpose) {
+  uint64_t k = sm64_mix(seed + 0x9E3779B97F4A7C15ull);
+  k = sm64_mix(k ^ (uint64_t)req);
+  return sm64_mix(k ^ (((uint64_t)pos << 8) | (uint64_t)purpose));
+}
+
+__device__ __forceinline__ uint32_t murmur_fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+
+__device__ __forceinline__ uint32_t elem_hash(uint32_t klo, uint32_t khi, uint32_t v) {
+  return murmur_fmix32(((v * 0x9E3779B9u) ^ klo) + khi);
+}
+
+// (2 * (h >> 9) + 1) * 2^-24, exact in fp32 (a single rounding of an exact value).
+__device__ __forceinline__ float hash_uniform(uint32_t h) {
+  return __builtin_fmaf((float)(h >> 9), 0x1.0p-23f, 0x1.0p-24f);
+}
+
+// log2(-log2(u)).  Gumbel-max on natural logits y uses key y - ln(-ln u); in
+// base-2 units (y2 = y * log2 e) the key y2 - log2(-log2 u) is an increasing
+// affine function of it, so every arg-max is unchanged.
+__device__ __forceinline__ float gumbel_log2_term(float u) {
+  return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------------------
+// Merge rules (deterministic: fixed order, lowest index wins ties).
+// ---------------------------------------------------------------------------
+struct SoftmaxState {
+  float m;   // running max of y2 (base-2 scaled logits)
+  float s;   // sum of exp2(y2 - m)
+};
+
+__device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, float s2) {
+  float mn = fmaxf(m, m2);
+  float a = (m == mn) ? s : s * fast_exp2(m - mn);
+  float b = (m2 == mn) ? s2 : s2 * fast_exp2(m2 - mn);
+  m = mn;
+  s = a + b;
+}
+
+// true if (k2, i2) beats (k1, i1): larger key, or equal key and lower index.
+__device__ __forceinline__ bool key_beats(float k2, int i2, float k1, int i1) {
+  return (k2 > k1) || (k2 == k1 && i2 < i1);
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) {
+  return __shfl_xor(v, m, 64);
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8_t*>(p);
+}
+
+__device__ __forceinline__ bf16x8_t zero_bf16x8() {
+  bf16x8_t z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+}  // namespace dspark

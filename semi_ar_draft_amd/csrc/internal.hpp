@@ -1,0 +1,128 @@
+// Kernel argument blocks and kernel lookup shared by the translation units of
+// libdspark.  Every kernel takes one argument block by value, so a launch (or
+// a HIP graph kernel node) is described by (function, grid, block, &args).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// Work decomposition of the vocabulary sweeps that carry the Markov bias:
+// waves own 32 request rows (two 16-row MFMA blocks) and a contiguous range
+// of 16-wide vocabulary tiles; four waves per 256-thread workgroup.
+constexpr int kRowsPerWave = 32;
+constexpr int kTileV = 16;
+constexpr int kWavesPerBlock = 4;
+
+enum SweepMode : int { kModeDraftGreedy = 0, kModeDraftSample = 1, kModeResidual = 2 };
+
+struct SweepArgs {
+  int B, gamma, V, k;            // k: 1-based draft position (draft modes)
+  int n_rg, n_vc, n_tiles;       // row groups, vocabulary chunks, 16-wide tiles
+  int xcd_remap;                 // map blocks sharing a chunk onto one XCD
+  const float* U;
+  int64_t usb, usk;
+  const float* T;                // target logits (residual mode)
+  int64_t tsb, tsk;
+  const void* W1;
+  const void* W2;
+  const int32_t* anchor;
+  const int32_t* tokens;         // [B][gamma]
+  const uint32_t* req;           // nullable
+  const int32_t* resid_k;        // residual mode: 1-based position or 0
+  const float* lse;              // residual mode: draft log-normalisers [B][gamma]
+  const float* resid_lt;         // residual mode: target log-normaliser per request
+  float invT, s2;                // 1/T and log2(e)/T (greedy: 1 and log2 e)
+  uint64_t seed;
+  float4* pf;                    // partials [B][n_vc]
+  int2* pi;
+  int32_t* err;
+};
+
+struct CombineArgs {
+  int B, gamma, V, k, n_vc, greedy;
+  float invT;
+  const float4* pf;
+  const int2* pi;
+  int32_t* tokens;               // draft: [B][gamma]
+  float* lse;
+  float* ytok;
+  // residual combine
+  const int32_t* resid_k;
+  const int32_t* accept_len;
+  int32_t* out_tokens;           // [B][gamma+1]
+  int32_t* err;
+};
+
+struct RowsArgs {
+  int B, gamma, V, n_chunks, greedy;
+  const float* T;
+  int64_t tsb, tsk;
+  const int32_t* K;
+  const uint32_t* req;
+  float s2;
+  uint64_t seed;
+  float4* pf;                    // [B*(gamma+1)][n_chunks]: m2, s, key, -
+  int* pi;
+  int32_t* err;
+};
+
+struct DecideArgs {
+  int B, gamma, V, n_chunks, greedy;
+  const float* T;
+  int64_t tsb, tsk;
+  const int32_t* K;
+  const uint32_t* req;
+  const int32_t* tokens;
+  const float* lse;
+  const float* ytok;
+  float invT;
+  uint64_t seed;
+  const float4* pf;
+  const int* pi;
+  int32_t* accept_len;
+  int32_t* out_tokens;
+  int32_t* resid_k;
+  float* resid_lt;
+  int32_t* err;
+};
+
+struct ConfArgs {
+  int B, gamma, V, dh, de;
+  const uint16_t* h;
+  const uint16_t* E;
+  const int32_t* anchor;
+  const int32_t* tokens;
+  const uint16_t* wc;
+  float bc;
+  const float* sts;
+  float* conf;
+  float* surv;
+  int32_t* err;
+};
+
+struct SchedArgs {
+  int B, gamma, n_sps;
+  const float* surv;
+  const float* sps;
+  int32_t* K;
+  int32_t* n_selected;
+  double* theta;
+};
+
+// Kernel lookup (host stubs usable with hipLaunchKernel and graph nodes).
+// `wdtype`: 0 = fp32, 1 = bf16.  Returns nullptr for unsupported r.
+const void* sweep_kernel(int wdtype, int r, int mode);
+const void* combine_draft_kernel();
+const void* combine_resid_kernel();
+const void* verify_rows_kernel();
+const void* verify_decide_kernel();
+const void* confidence_kernel();
+const void* survival_kernel();
+const void* schedule_kernel();
+
+constexpr int kSchedMaxKeys = 8192;
+constexpr int kSchedThreads = 1024;
+
+}  // namespace dspark

@@ -1,0 +1,236 @@
+"""GPU parity: libdspark (through its C ABI) against the CPU oracle.
+
+Small cases run the oracle on every request and span several 16-wide tiles,
+several 32-row groups with a ragged tail, and several vocabulary chunks.  The
+full-size cases use the launch configuration bench.py times and compare a
+sample of requests the oracle computes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import semi_ar_draft_amd as dk
+from parity import Report, compare_draft, compare_confidence, compare_verify, TIE
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = dk.Context(0)
+    yield c
+    c.close()
+
+
+def to_dev(inp):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def gpu_step(ctx, d, seed, K=None, schedule=False):
+    wl = d["wl"]
+    G = wl.gamma
+    tok, lse, ytok = ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"],
+                                      d["temperature"], seed, G)
+    res = dict(tok=tok, lse=lse, ytok=ytok)
+    if d.get("h") is not None:
+        res["conf"], res["surv"] = ctx.confidence(d["h"], d["E"], d["anchor"], tok, d["wc"], d["bc"],
+                                                  d.get("sts_T"))
+    if schedule:
+        res["K"], res["nsel"], res["theta"] = ctx.schedule(res["surv"], d["sps"])
+        K = res["K"]
+    res["acc"], res["out"] = ctx.verify(d["target"], d["U"], d["W1"], d["W2"], d["anchor"], tok, lse,
+                                        ytok, K, d["req_ids"], d["temperature"], seed)
+    ctx.check()
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def oracle_step(inp, seed, rows=None, K=None):
+    wl = inp["wl"]
+    sel = (lambda x: x) if rows is None else (lambda x: x[rows])
+    T = inp["temperature"]
+    d = oracle.draft_markov(sel(inp["U"]), inp["W1"], inp["W2"], sel(inp["anchor"]), sel(inp["req_ids"]),
+                            T, seed, wl.gamma)
+    c = None
+    if inp.get("h") is not None:
+        c = oracle.confidence(sel(inp["h"]), inp["E"], sel(inp["anchor"]), d.tokens, inp["wc"], inp["bc"],
+                              inp.get("sts_T"))
+    v = oracle.verify(sel(inp["target"]), d.tokens, d.lse, d.ytok, sel(inp["U"]), inp["W1"], inp["W2"],
+                      sel(inp["anchor"]), K, sel(inp["req_ids"]), T, seed, wl.gamma)
+    return d, c, v
+
+
+def check_chain(g, inp, seed, rows=None, K=None, min_compared=1):
+    d, c, v = oracle_step(inp, seed, rows, K)
+    rep, taint = compare_draft(g["tok"], g["lse"], g["ytok"], d, rows)
+    if c is not None:
+        compare_confidence(g["conf"], g["surv"], c, taint, rows, rep)
+    acc = g["acc"] if rows is None else g["acc"]
+    compare_verify(acc, g["out"], v, taint, K, rows, rep)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert rep.compared >= min_compared
+    return rep, (d, c, v)
+
+
+# ---------------------------------------------------------------------------
+# small cases: whole batch against the oracle
+# ---------------------------------------------------------------------------
+SMALL = [
+    # name, workload overrides
+    ("tiny_greedy_f32", "tiny", {}),
+    ("tiny_sample_f32", "tiny", dict(temperature=1.0)),
+    ("tiny_sample_f32_r64", "tiny", dict(temperature=0.8, r=64, B=5)),
+    ("bf16_greedy_ragged", "greedy", dict(B=40, V=5008, peak=None)),
+    ("bf16_greedy_peak", "greedy", dict(B=33, V=4096)),
+    ("bf16_sample", "sample", dict(B=40, V=5008, d_h=64, d_e=64)),
+    ("bf16_sample_T07_r128", "sample", dict(B=70, V=3008, r=128, temperature=0.7, d_h=32, d_e=96, sts=True)),
+    ("bf16_sample_r32_gamma3", "sample", dict(B=17, gamma=3, V=2000, r=32, d_h=16, d_e=16)),
+    ("bf16_sample_B1_gamma1", "sample", dict(B=1, gamma=1, V=160, d_h=8, d_e=8)),
+]
+
+
+@pytest.mark.parametrize("name,base,over", SMALL, ids=[s[0] for s in SMALL])
+def test_small_chain(ctx, name, base, over):
+    wl = synth.WORKLOADS[base].with_(**over)
+    inp = synth.make_inputs(wl, seed=wl.seed + 17)
+    print(f"case {name}: B={wl.B} gamma={wl.gamma} V={wl.V} r={wl.r} T={wl.temperature}", flush=True)
+    g = gpu_step(ctx, to_dev(inp), seed=12345)
+    check_chain(g, inp, 12345)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_small_verify_with_variable_K(ctx, seed):
+    wl = synth.WORKLOADS["sample"].with_(B=50, V=2048, d_h=16, d_e=16)
+    inp = synth.make_inputs(wl, seed=seed)
+    rs = np.random.default_rng(seed)
+    K = rs.integers(0, wl.gamma + 1, size=wl.B).astype(np.int32)
+    K[:3] = [0, wl.gamma, 1]
+    print(f"variable K seed={seed} K={K[:10]}", flush=True)
+    g = gpu_step(ctx, to_dev(inp), seed=seed, K=torch.from_numpy(K).cuda())
+    check_chain(g, inp, seed, K=K)
+
+
+def test_small_scheduled_chain(ctx):
+    wl = synth.WORKLOADS["sched"].with_(B=96, V=4096, r=64, d_h=64, d_e=64, n_sps=640)
+    inp = synth.make_inputs(wl, seed=77)
+    print(f"scheduled chain B={wl.B} V={wl.V} n_sps={wl.n_sps}", flush=True)
+    g = gpu_step(ctx, to_dev(inp), seed=9, schedule=True)
+    d, c, _ = oracle_step(inp, 9)
+    rep, taint = compare_draft(g["tok"], g["lse"], g["ytok"], d)
+    compare_confidence(g["conf"], g["surv"], c, taint, rep=rep)
+    s = oracle.schedule(c.surv.astype(np.float32), inp["sps"])
+    clean = bool(np.all(taint > wl.gamma)) and s.min_rel_step > TIE
+    print(f"schedule: oracle n={s.n_selected} gpu n={int(g['nsel'][0])} clean={clean}", flush=True)
+    if clean:
+        assert np.array_equal(g["K"], s.K)
+        assert int(g["nsel"][0]) == s.n_selected
+        assert abs(float(g["theta"][0]) - s.theta) <= 1e-3 * s.theta
+    K = s.K if clean else g["K"]
+    v = oracle.verify(inp["target"], d.tokens, d.lse, d.ytok, inp["U"], inp["W1"], inp["W2"], inp["anchor"],
+                      K, inp["req_ids"], wl.temperature, 9, wl.gamma)
+    compare_verify(g["acc"], g["out"], v, taint, K, rep=rep)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
+    assert 0 < s.n_selected < wl.B * wl.gamma      # the early stop did cut
+
+
+# ---------------------------------------------------------------------------
+# scheduler alone on synthetic survivals (identical fp32 inputs on both sides)
+# ---------------------------------------------------------------------------
+SCHED = [
+    (4, 3, 20, False), (64, 7, 4096, True), (512, 7, 4096, False), (512, 8, 4096, True),
+    (256, 16, 4096, False), (100, 7, 150, False), (33, 5, 33, True), (1, 1, 1, False),
+    (1, 32, 40, False), (128, 7, 1000, True),
+]
+
+
+@pytest.mark.parametrize("B,G,n_sps,ties", SCHED)
+def test_schedule_kernel(ctx, B, G, n_sps, ties):
+    surv = synth.survival_rows(B, G, seed=B * 31 + G, ties=ties)
+    sps = synth.sps_table(n_sps)
+    print(f"schedule B={B} gamma={G} n_sps={n_sps} ties={ties}", flush=True)
+    K, nsel, theta = ctx.schedule(surv.cuda(), sps.cuda())
+    torch.cuda.synchronize()
+    s = oracle.schedule(surv, sps)
+    assert np.array_equal(K.cpu().numpy(), s.K)
+    assert int(nsel.item()) == s.n_selected
+    assert float(theta.item()) == s.theta
+
+
+def test_schedule_kernel_flat_and_steep_tables(ctx):
+    surv = synth.survival_rows(200, 7, seed=5)
+    for sps in (torch.full((4096,), 3.0), torch.linspace(100.0, 1.0, 4096),
+                torch.tensor([10.0] * 200 + [1.0] * 3896)):
+        K, nsel, theta = ctx.schedule(surv.cuda(), sps.cuda())
+        s = oracle.schedule(surv, sps)
+        assert np.array_equal(K.cpu().numpy(), s.K)
+        assert int(nsel.item()) == s.n_selected
+        assert float(theta.item()) == s.theta
+
+
+# ---------------------------------------------------------------------------
+# full sizes in the benchmark's launch configuration, sampled requests
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def full_sample():
+    wl = synth.WORKLOADS["sample"]
+    inp = synth.make_inputs(wl)
+    return inp, to_dev(inp)
+
+
+def test_full_greedy_all_requests(ctx):
+    wl = synth.WORKLOADS["greedy"]
+    inp = synth.make_inputs(wl)
+    print(f"full greedy B={wl.B} V={wl.V}", flush=True)
+    g = gpu_step(ctx, to_dev(inp), seed=3)
+    rep, _ = check_chain(g, inp, 3, min_compared=wl.B * wl.gamma)
+
+
+def test_full_sample_sampled_requests(ctx, full_sample):
+    inp, d = full_sample
+    wl = inp["wl"]
+    rows = [0, 1, 31, 32, 63, 64, 97, 127]
+    print(f"full sample B={wl.B} V={wl.V} rows={rows}", flush=True)
+    g = gpu_step(ctx, d, seed=2024)
+    check_chain(g, inp, 2024, rows=rows, min_compared=len(rows))
+
+
+def test_full_sample_is_bitwise_deterministic(ctx, full_sample):
+    _, d = full_sample
+    a = gpu_step(ctx, d, seed=99)
+    b = gpu_step(ctx, d, seed=99)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    c = gpu_step(ctx, d, seed=100)
+    assert not np.array_equal(a["tok"], c["tok"])
+
+
+def test_full_sched_shape_sampled(ctx):
+    wl = synth.WORKLOADS["sched"]
+    inp = synth.make_inputs(wl)
+    d = to_dev(inp)
+    rows = [0, 5, 255, 256, 300, 511]
+    rs = np.random.default_rng(4)
+    K = rs.integers(0, wl.gamma + 1, size=wl.B).astype(np.int32)
+    print(f"full sched shape B={wl.B} V={wl.V} rows={rows}", flush=True)
+    g = gpu_step(ctx, d, seed=5, K=torch.from_numpy(K).cuda())
+    check_chain(g, inp, 5, rows=rows, K=K[rows], min_compared=len(rows))
+
+
+def test_graph_and_direct_launch_agree(ctx, full_sample):
+    _, d = full_sample
+    a = gpu_step(ctx, d, seed=7)
+    os.environ["DSPARK_GRAPH"] = "0"
+    try:
+        c2 = dk.Context(0)
+    finally:
+        del os.environ["DSPARK_GRAPH"]
+    b = gpu_step(c2, d, seed=7)
+    c2.close()
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
