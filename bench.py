@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Throughput of one DSpark draft/verify step on one MI355X.
+
+One step = dspark_draft_markov (gamma sequential Markov-head positions) ->
+dspark_confidence -> [dspark_schedule] -> dspark_verify, on seeded synthetic
+inputs already resident in HBM.  The headline workload is B=128 requests,
+gamma=7, V=151936, r=256, temperature 1 with the confidence head (d=4096);
+every request verifies all gamma positions, so one step verifies B*gamma
+draft positions.
+
+Prints one JSON line (see the fields below).  Usage:
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload sample]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "verified draft positions/sec at B=128,γ=7,V=152k; % of HBM roofline"
+HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sample", choices=["tiny", "greedy", "sample", "sched"])
+    ap.add_argument("--seed", type=int, default=0x5EED)
+    ap.add_argument("--cpu-sample", type=int, default=64,
+                    help="requests of the same batch the CPU oracle runs for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-timing-pass", action="store_true",
+                    help="skip the per-kernel event pass (used under a profiler)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB buffer a few times: the reference kernel of known "
+                         "traffic used to scale the FETCH_SIZE / WRITE_SIZE counters")
+    return ap.parse_args()
+
+
+def copy_calibration(n_iter: int = 3):
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n_iter):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                      "iterations": n_iter}))
+
+
+def sweep_bytes(B, V, r, wbytes):
+    """Algorithmic HBM bytes of one vocabulary sweep with the Markov bias:
+    U rows (4 B per logit), the whole W2, the gathered W1 rows."""
+    return 4 * B * V + wbytes * r * V + wbytes * B * r
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by request; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import semi_ar_draft_amd as dk
+
+    wl = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = synth.make_inputs(wl)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    print(f"[bench] inputs {wl.name} B={wl.B} gamma={wl.gamma} V={wl.V} r={wl.r} "
+          f"generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    B, G, V, r = wl.B, wl.gamma, wl.V, wl.r
+    dev = torch.device("cuda", 0)
+    ctx = dk.Context(0)
+    # outputs allocated once, outside the timed region
+    tok = torch.empty((B, G), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, G), dtype=torch.float32, device=dev)
+    ytok = torch.empty((B, G), dtype=torch.float32, device=dev)
+    conf = torch.empty((B, G), dtype=torch.float32, device=dev)
+    surv = torch.empty((B, G), dtype=torch.float32, device=dev)
+    Ksch = torch.empty((B,), dtype=torch.int32, device=dev)
+    nsel = torch.empty((1,), dtype=torch.int32, device=dev)
+    theta = torch.empty((1,), dtype=torch.float64, device=dev)
+    acc = torch.empty((B,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    n_steps_max = max(args.steps, 1)
+    K_log = torch.zeros((n_steps_max, B), dtype=torch.int32, device=dev)
+    A_log = torch.zeros((n_steps_max, B), dtype=torch.int32, device=dev)
+    T = d["temperature"]
+    has_conf = d.get("h") is not None
+    sched = d.get("sps") is not None
+
+    def step(i, log=None):
+        seed = args.seed ^ i
+        ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, seed, G,
+                         out=(tok, lse, ytok))
+        if has_conf:
+            ctx.confidence(d["h"], d["E"], d["anchor"], tok, d["wc"], d["bc"], d.get("sts_T"),
+                           out=(conf, surv))
+        K = None
+        if sched:
+            ctx.schedule(surv, d["sps"], out=(Ksch, nsel, theta))
+            K = Ksch
+        ctx.verify(d["target"], d["U"], d["W1"], d["W2"], d["anchor"], tok, lse, ytok, K,
+                   d["req_ids"], T, seed, out=(acc, out))
+        if log is not None:
+            if K is not None:
+                K_log[log].copy_(K, non_blocking=True)
+            A_log[log].copy_(acc, non_blocking=True)
+
+    for i in range(args.warmup):
+        step(1000 + i)
+    ctx.check()
+    torch.cuda.synchronize()
+
+    # ---- timed region: production launch path (graph for the draft loop) ----
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i, log=i)
+    e1.record()
+    torch.cuda.synchronize()
+    ctx.check()
+    elapsed_ms = e0.elapsed_time(e1)
+    ms_per_step = elapsed_ms / args.steps
+    if sched:
+        positions = int(K_log[:args.steps].sum().item())
+        Ks = K_log[:args.steps].cpu()
+    else:
+        positions = B * G * args.steps
+        Ks = torch.full((args.steps, B), G, dtype=torch.int32)
+    A = A_log[:args.steps].cpu()
+    value = positions / (elapsed_ms / 1e3)
+    needed_rows = float(torch.where(A < Ks, A + 1, Ks + 1).sum().item()) / args.steps
+    read_rows = float((torch.clamp(Ks + 1, max=2) + torch.where((A >= 2) & (Ks >= 2), Ks - 1,
+                                                                  torch.zeros_like(Ks))).sum().item()) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, "
+          f"{value / 1e6:.3f} M positions/s", file=sys.stderr, flush=True)
+
+    # ---- per-kernel event pass: same steps, every kernel bracketed by events ----
+    per_kernel = {}
+    roofline = None
+    ms_per_step_timed_pass = None
+    if not args.no_timing_pass:
+        ctx.timing(True)
+        ctx.read_timing()
+        torch.cuda.synchronize()
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for i in range(args.steps):
+            step(i)
+        f1.record()
+        torch.cuda.synchronize()
+        ms_per_step_timed_pass = f0.elapsed_time(f1) / args.steps
+        tk = ctx.read_timing()
+        ctx.timing(False)
+        for name, (ms, n) in tk.items():
+            if n:
+                per_kernel[name] = {"launches_per_step": n / args.steps, "avg_us": 1e3 * ms / n,
+                                    "us_per_step": 1e3 * ms / args.steps}
+        wbytes = 2 if d["W1"].dtype == torch.bfloat16 else 4
+        # dominant kernel: the draft sweep (gamma launches per step)
+        sw = per_kernel["draft_sweep"]
+        b_sweep = sweep_bytes(B, V, r, wbytes)
+        sw["alg_bytes"] = b_sweep
+        sw["alg_GBps"] = b_sweep / (sw["avg_us"] * 1e-6) / 1e9
+        sw["mfma_TFLOPs"] = 2.0 * B * r * V / (sw["avg_us"] * 1e-6) / 1e12
+        if "verify_rows" in per_kernel:
+            # rows the accept decisions need: up to the first rejection, or K_b + 1
+            vb = 4.0 * V * needed_rows
+            vr = per_kernel["verify_rows"]
+            vr["alg_bytes_per_step"] = vb
+            vr["needed_rows_per_step"] = needed_rows
+            vr["read_rows_per_step"] = read_rows
+            vr["alg_GBps"] = vb / (vr["us_per_step"] * 1e-6) / 1e9
+        if "resid_sweep" in per_kernel:
+            n_rej = float((A < Ks).sum().item()) / args.steps
+            rb = 8.0 * V * n_rej + wbytes * r * V + wbytes * n_rej * r
+            per_kernel["resid_sweep"]["alg_bytes"] = rb
+            per_kernel["resid_sweep"]["rows"] = n_rej
+            per_kernel["resid_sweep"]["alg_GBps"] = rb / (per_kernel["resid_sweep"]["avg_us"] * 1e-6) / 1e9
+        if "confidence" in per_kernel:
+            cb = 2.0 * B * G * (wl.d_h + wl.d_e)
+            per_kernel["confidence"]["alg_bytes"] = cb
+            per_kernel["confidence"]["alg_GBps"] = cb / (per_kernel["confidence"]["avg_us"] * 1e-6) / 1e9
+        achieved = sw["alg_GBps"]
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "kernel": "draft_sweep (MFMA Markov bias + vocabulary sweep, one position)",
+                    "alg_bytes_per_launch": b_sweep, "avg_launch_us": round(sw["avg_us"], 2),
+                    "mfma_util": round(sw["mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 5)}
+        print(f"[bench] kernels: " + ", ".join(f"{k} {v['avg_us']:.1f}us x{v['launches_per_step']:.0f}"
+                                             for k, v in per_kernel.items()), file=sys.stderr, flush=True)
+
+    # step-level algorithmic bytes (what one step must move at least)
+    wbytes = 2 if d["W1"].dtype == torch.bfloat16 else 4
+    n_rej_all = float((A < Ks).sum().item()) / args.steps
+    step_bytes = (G * sweep_bytes(B, V, r, wbytes)
+                  + (2.0 * B * G * (wl.d_h + wl.d_e) if has_conf else 0.0)
+                  + 4.0 * V * needed_rows
+                  + (8.0 * V * n_rej_all + wbytes * r * V if (T > 0 and n_rej_all > 0) else 0.0))
+
+    cpu = None
+    if not args.no_cpu_baseline and not sched:
+        import numpy as np
+        import oracle
+        from threadpoolctl import threadpool_info
+        n = min(args.cpu_sample, B)
+        rows = list(range(n))
+        t = time.time()
+        oracle.run_step(inp, seed=args.seed, rows=rows)
+        dt = time.time() - t
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        cpu = {"value": round(n * G / dt, 2), "unit": "verified draft positions/s", "cores": threads,
+               "kind": "oracle", "sample": f"{n} of the {B} requests of one step (all {G} positions, "
+               f"draft+confidence+verify), float64 numpy, {dt:.1f}s"}
+        print(f"[bench] cpu oracle: {cpu['value']} positions/s on {threads} threads", file=sys.stderr,
+              flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 weights, bf16 MFMA with f32 accumulation)",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={B} gamma={G} V={V} r={r} T={T}"
+                               + (f" confidence d_h={wl.d_h} d_e={wl.d_e}" if has_conf else "")
+                               + (" scheduled" if sched else " K_b=gamma"),
+                   "B": B, "gamma": G, "V": V, "r": r, "temperature": T,
+                   "positions_per_step": positions / args.steps,
+                   "parallelism": "single GPU"},
+        "step_alg_bytes": step_bytes,
+        "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "accepted_per_step": float(A.sum().item()) / args.steps,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_kernel": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                       for k, v in per_kernel.items()},
+        "ms_per_step_event_pass": None if ms_per_step_timed_pass is None else round(ms_per_step_timed_pass, 4),
+    }
+    ctx.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -81,6 +81,28 @@ const char* dspark_last_error(const dspark_ctx* ctx);
  * error, else DSPARK_OK. */
 int dspark_check(dspark_ctx* ctx, hipStream_t stream);
 
+/* Kernel timing for benchmarks (not needed for correct use).
+ * While enabled, every kernel the context launches is bracketed by a pair of
+ * HIP events recorded on the launch stream, and the draft loop is launched
+ * kernel by kernel instead of through its graph.  dspark_timing_read waits
+ * for the recorded events, writes per-kernel-class totals (milliseconds) and
+ * launch counts into arrays of DSPARK_K_COUNT entries, and forgets them.
+ * Errors: DSPARK_EINVAL for null arguments, DSPARK_EHIP if an event fails. */
+enum {
+  DSPARK_K_DRAFT_SWEEP = 0,    /* MFMA bias + vocabulary sweep of one position */
+  DSPARK_K_DRAFT_COMBINE = 1,  /* cross-chunk merge of one position */
+  DSPARK_K_CONFIDENCE = 2,
+  DSPARK_K_SURVIVAL = 3,
+  DSPARK_K_SCHEDULE = 4,
+  DSPARK_K_VERIFY_ROWS = 5,    /* streaming pass over target rows */
+  DSPARK_K_VERIFY_DECIDE = 6,
+  DSPARK_K_RESID_SWEEP = 7,    /* MFMA residual sweep */
+  DSPARK_K_RESID_COMBINE = 8,
+  DSPARK_K_COUNT = 9
+};
+int dspark_timing_enable(dspark_ctx* ctx, int enable);
+int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
+
 /* Semi-autoregressive draft with the Markov head.
  *
  * [blog] "形式化定义", "整体架构" and "Markov Head：一阶转移偏置"; [teardown]

@@ -23,7 +23,10 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
     "dspark_draft_markov", "dspark_confidence", "dspark_schedule", "dspark_verify",
+    "dspark_timing_enable", "dspark_timing_read",
 )
+KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
+                  "verify_rows", "verify_decide", "resid_sweep", "resid_combine")
 
 _lib = None
 _vp, _i32, _i64, _u64, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
@@ -54,6 +57,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_last_error.argtypes = [_vp]
     lib.dspark_check.restype = _i32
     lib.dspark_check.argtypes = [_vp, _vp]
+    lib.dspark_timing_enable.restype = _i32
+    lib.dspark_timing_enable.argtypes = [_vp, _i32]
+    lib.dspark_timing_read.restype = _i32
+    lib.dspark_timing_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
     lib.dspark_draft_markov.restype = _i32
     lib.dspark_draft_markov.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -152,6 +159,18 @@ class Context:
     def check(self, stream=None):
         """Synchronise the stream and raise if a kernel flagged bad data."""
         self._rc(self.lib.dspark_check(self._h, _stream(self.device, stream)))
+
+    # -- kernel timing ------------------------------------------------------
+    def timing(self, enable: bool):
+        self._rc(self.lib.dspark_timing_enable(self._h, 1 if enable else 0))
+
+    def read_timing(self) -> dict:
+        """{kernel class: (total ms, launches)} since the last read."""
+        n = len(KERNEL_CLASSES)
+        ms = (ctypes.c_double * n)()
+        cnt = (_i32 * n)()
+        self._rc(self.lib.dspark_timing_read(self._h, ms, cnt))
+        return {name: (ms[i], cnt[i]) for i, name in enumerate(KERNEL_CLASSES)}
 
     # -- dspark_draft_markov ------------------------------------------------
     def draft_markov(self, U, W1, W2, anchor, req_ids, temperature: float, seed: int, gamma: int,
@@ -269,6 +288,6 @@ class Context:
         return acc, toks
 
 
-__all__ = ["Context", "DSparkError", "load_library", "LIB_PATH", "EXPORTS",
+__all__ = ["Context", "DSparkError", "load_library", "LIB_PATH", "EXPORTS", "KERNEL_CLASSES",
            "DSPARK_OK", "DSPARK_EINVAL", "DSPARK_EHIP", "DSPARK_ENOMEM", "DSPARK_EDEVICE",
            "DSPARK_F32", "DSPARK_BF16"]

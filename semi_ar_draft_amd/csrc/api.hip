@@ -22,6 +22,7 @@ constexpr int kVersion = 100;
 constexpr int kMaxGamma = 32;
 
 struct KernelNode {
+  int cls;
   const void* fn;
   dim3 grid, block;
   // argument storage: the largest argument block
@@ -49,6 +50,14 @@ struct dspark_ctx {
   int32_t* dev_err = nullptr;
   bool use_graph = true;
   std::vector<DraftGraph> graphs;
+  // kernel timing (benchmarks): event pairs around every launch while enabled
+  bool timing = false;
+  struct Pending {
+    int cls;
+    hipEvent_t a, b;
+  };
+  std::vector<hipEvent_t> ev_free;
+  std::vector<Pending> pending;
 };
 
 namespace {
@@ -106,21 +115,35 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Vocabulary-sweep plan: aim at eight waves per CU, at least four 16-wide
 // tiles per wave, and a grid that is a multiple of the XCD count.
 struct SweepPlan {
-  int n_rg, n_vc, n_tiles, grid;
+  int n_rg, n_vc, n_tiles, grid, shared;
 };
 
-SweepPlan plan_sweep(const dspark_ctx* c, int B, int V) {
+// Batches of three or more 32-row groups share each W2 tile across the four
+// waves of a workgroup (bf16, r >= 128); smaller batches give every wave its
+// own vocabulary chunk.
+SweepPlan plan_sweep(const dspark_ctx* c, int B, int V, int r, int wdtype) {
   SweepPlan p;
   p.n_rg = (B + kRowsPerWave - 1) / kRowsPerWave;
   p.n_tiles = V / kTileV;
+  p.shared = (wdtype == DSPARK_BF16 && (r == 128 || r == 256) && p.n_rg >= 3) ? 1 : 0;
   const int target_waves = 8 * c->cu_count;
-  int n_vc = target_waves / p.n_rg;
   const int max_vc = p.n_tiles / 4 > 0 ? p.n_tiles / 4 : 1;
-  if (n_vc > max_vc) n_vc = max_vc;
-  if (n_vc < 1) n_vc = 1;
-  p.n_vc = n_vc;
-  const long waves = (long)p.n_rg * p.n_vc;
-  long grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  long grid;
+  if (p.shared) {
+    const int n_rq = (p.n_rg + kWavesPerBlock - 1) / kWavesPerBlock;
+    int n_vc = target_waves / (kWavesPerBlock * n_rq);
+    if (n_vc > max_vc) n_vc = max_vc;
+    if (n_vc < 1) n_vc = 1;
+    p.n_vc = n_vc;
+    grid = (long)n_rq * n_vc;
+  } else {
+    int n_vc = target_waves / p.n_rg;
+    if (n_vc > max_vc) n_vc = max_vc;
+    if (n_vc < 1) n_vc = 1;
+    p.n_vc = n_vc;
+    const long waves = (long)p.n_rg * p.n_vc;
+    grid = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  }
   grid = (grid + 7) / 8 * 8;
   p.grid = (int)grid;
   return p;
@@ -150,7 +173,7 @@ int check_markov_shape(dspark_ctx* c, int B, int gamma, int V, int r, int wdtype
   if (gamma < 1 || gamma > kMaxGamma) return fail(c, DSPARK_EINVAL, "gamma must be in 1..%d", kMaxGamma);
   if (V < kTileV || V % kTileV) return fail(c, DSPARK_EINVAL, "V must be a positive multiple of 16");
   if (wdtype != DSPARK_F32 && wdtype != DSPARK_BF16) return fail(c, DSPARK_EINVAL, "unknown weight dtype");
-  if (!sweep_kernel(wdtype, r, kModeDraftGreedy))
+  if (!sweep_kernel(wdtype, r, kModeDraftGreedy, 0))
     return fail(c, DSPARK_EINVAL, "r must be one of 32, 64, 128, 256 (got %d)", r);
   if (!(T >= 0.0f) || !std::isfinite(T)) return fail(c, DSPARK_EINVAL, "temperature must be finite and >= 0");
   return DSPARK_OK;
@@ -161,9 +184,35 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t 
   return hipLaunchKernel(fn, grid, block, params, 0, s);
 }
 
+hipError_t take_event(dspark_ctx* c, hipEvent_t* e) {
+  if (!c->ev_free.empty()) {
+    *e = c->ev_free.back();
+    c->ev_free.pop_back();
+    return hipSuccess;
+  }
+  return hipEventCreate(e);
+}
+
+// Launch one kernel; while timing is enabled, bracket it with events.
+int klaunch(dspark_ctx* c, int cls, const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t s) {
+  if (!c->timing) {
+    DSPARK_HIP(c, launch(fn, grid, block, arg, s));
+    return DSPARK_OK;
+  }
+  hipEvent_t a, b;
+  DSPARK_HIP(c, take_event(c, &a));
+  DSPARK_HIP(c, take_event(c, &b));
+  DSPARK_HIP(c, hipEventRecord(a, s));
+  DSPARK_HIP(c, launch(fn, grid, block, arg, s));
+  DSPARK_HIP(c, hipEventRecord(b, s));
+  c->pending.push_back({cls, a, b});
+  return DSPARK_OK;
+}
+
 template <typename A>
-void set_node(KernelNode& n, const void* fn, dim3 grid, dim3 block, const A& a) {
+void set_node(KernelNode& n, int cls, const void* fn, dim3 grid, dim3 block, const A& a) {
   static_assert(sizeof(A) <= sizeof(n.args), "argument block too large");
+  n.cls = cls;
   n.fn = fn;
   n.grid = grid;
   n.block = block;
@@ -187,8 +236,11 @@ hipKernelNodeParams node_params(KernelNode& n, void** holder) {
 // enabled.
 int run_chain(dspark_ctx* c, hipStream_t stream, std::vector<KernelNode>& nodes, int B, int gamma, int V,
               int r, int wdtype, int mode, int grid, int n_vc) {
-  if (!c->use_graph) {
-    for (auto& n : nodes) DSPARK_HIP(c, launch(n.fn, n.grid, n.block, n.args, stream));
+  if (!c->use_graph || c->timing) {
+    for (auto& n : nodes) {
+      const int rc = klaunch(c, n.cls, n.fn, n.grid, n.block, n.args, stream);
+      if (rc) return rc;
+    }
     return DSPARK_OK;
   }
   DraftGraph* g = nullptr;
@@ -279,6 +331,11 @@ void dspark_destroy(dspark_ctx* c) {
       if (g.exec) (void)hipGraphExecDestroy(g.exec);
       if (g.graph) (void)hipGraphDestroy(g.graph);
     }
+    for (auto& p : c->pending) {
+      (void)hipEventDestroy(p.a);
+      (void)hipEventDestroy(p.b);
+    }
+    for (auto e : c->ev_free) (void)hipEventDestroy(e);
     if (c->ws) (void)hipFree(c->ws);
     if (c->dev_err) (void)hipFree(c->dev_err);
   }
@@ -304,6 +361,39 @@ int dspark_check(dspark_ctx* c, hipStream_t stream) {
   return DSPARK_OK;
 }
 
+int dspark_timing_enable(dspark_ctx* c, int enable) {
+  if (!c) return DSPARK_EINVAL;
+  c->timing = enable != 0;
+  return DSPARK_OK;
+}
+
+int dspark_timing_read(dspark_ctx* c, double* ms, int* launches) {
+  if (!c || !ms || !launches) return DSPARK_EINVAL;
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  for (int i = 0; i < DSPARK_K_COUNT; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  int rc = DSPARK_OK;
+  for (auto& p : c->pending) {
+    float t = 0.f;
+    if (rc == DSPARK_OK) {
+      hipError_t e = hipEventSynchronize(p.b);
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, p.a, p.b);
+      if (e != hipSuccess) rc = fail(c, DSPARK_EHIP, "event timing failed: %s", hipGetErrorString(e));
+    }
+    if (p.cls >= 0 && p.cls < DSPARK_K_COUNT) {
+      ms[p.cls] += t;
+      launches[p.cls] += 1;
+    }
+    c->ev_free.push_back(p.a);
+    c->ev_free.push_back(p.b);
+  }
+  c->pending.clear();
+  return rc;
+}
+
 int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r,
                         dspark_dtype wdtype, const float* U, int64_t u_stride_b, int64_t u_stride_k,
                         const void* W1, const void* W2, const int32_t* anchor, const uint32_t* req_ids,
@@ -320,7 +410,7 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
 
   const bool greedy = temperature == 0.0f;
   const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
-  const SweepPlan pl = plan_sweep(c, B, V);
+  const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
   const size_t npart = (size_t)B * pl.n_vc;
   const size_t off_pi = align256(npart * sizeof(float4));
   if ((rc = ensure_ws(c, off_pi + align256(npart * sizeof(int2))))) return rc;
@@ -365,13 +455,13 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
   ca.ytok = ytok;
   ca.err = c->dev_err;
 
-  const void* kfn = sweep_kernel((int)wdtype, r, mode);
+  const void* kfn = sweep_kernel((int)wdtype, r, mode, pl.shared);
   std::vector<KernelNode> nodes(2 * gamma);
   for (int k = 1; k <= gamma; ++k) {
     sa.k = k;
     ca.k = k;
-    set_node(nodes[2 * (k - 1)], kfn, dim3(pl.grid), dim3(256), sa);
-    set_node(nodes[2 * (k - 1) + 1], combine_draft_kernel(), dim3(B), dim3(64), ca);
+    set_node(nodes[2 * (k - 1)], DSPARK_K_DRAFT_SWEEP, kfn, dim3(pl.grid), dim3(256), sa);
+    set_node(nodes[2 * (k - 1) + 1], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B), dim3(256), ca);
   }
   return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode, pl.grid, pl.n_vc);
 }
@@ -408,8 +498,9 @@ int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V
   a.conf = conf;
   a.surv = surv;
   a.err = c->dev_err;
-  DSPARK_HIP(c, launch(confidence_kernel(), dim3(B * gamma), dim3(256), &a, stream));
-  DSPARK_HIP(c, launch(survival_kernel(), dim3((B + 255) / 256), dim3(256), &a, stream));
+  int rc;
+  if ((rc = klaunch(c, DSPARK_K_CONFIDENCE, confidence_kernel(), dim3(B * gamma), dim3(256), &a, stream))) return rc;
+  if ((rc = klaunch(c, DSPARK_K_SURVIVAL, survival_kernel(), dim3((B + 255) / 256), dim3(256), &a, stream))) return rc;
   return DSPARK_OK;
 }
 
@@ -431,7 +522,8 @@ int dspark_schedule(dspark_ctx* c, hipStream_t stream, int B, int gamma, const f
   a.K = K;
   a.n_selected = n_selected;
   a.theta = theta;
-  DSPARK_HIP(c, launch(schedule_kernel(), dim3(1), dim3(kSchedThreads), &a, stream));
+  int rc;
+  if ((rc = klaunch(c, DSPARK_K_SCHEDULE, schedule_kernel(), dim3(1), dim3(kSchedThreads), &a, stream))) return rc;
   return DSPARK_OK;
 }
 
@@ -456,8 +548,18 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
 
   const int rows = B * (gamma + 1);
-  const int n_chunks = plan_rows_chunks(rows, V);
-  const SweepPlan pl = plan_sweep(c, B, V);
+  // windows of target rows: rows 1-2 for every request, then the rest only
+  // for requests that kept every draft so far
+  const int n_win = gamma + 1 <= 2 ? 1 : 2;
+  const int win_lo[2] = {1, 3};
+  const int win_hi[2] = {gamma + 1 <= 2 ? gamma + 1 : 2, gamma + 1};
+  int win_chunks[2];
+  int n_chunks = 1;
+  for (int w = 0; w < n_win; ++w) {
+    win_chunks[w] = plan_rows_chunks(B * (win_hi[w] - win_lo[w] + 1), V);
+    if (win_chunks[w] > n_chunks) n_chunks = win_chunks[w];
+  }
+  const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
   const size_t n_rowpart = (size_t)rows * n_chunks;
   const size_t n_respart = (size_t)B * pl.n_vc;
   size_t off = 0;
@@ -473,6 +575,8 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   off += align256((size_t)B * sizeof(int32_t));
   const size_t off_rlt = off;
   off += align256((size_t)B * sizeof(float));
+  const size_t off_vs = off;
+  off += align256((size_t)B * sizeof(int2));
   if ((rc = ensure_ws(c, off))) return rc;
   char* ws = static_cast<char*>(c->ws);
   float4* rpf = reinterpret_cast<float4*>(ws + off_rpf);
@@ -481,52 +585,68 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   int2* spi = reinterpret_cast<int2*>(ws + off_spi);
   int32_t* resid_k = reinterpret_cast<int32_t*>(ws + off_rk);
   float* resid_lt = reinterpret_cast<float*>(ws + off_rlt);
+  int2* vstate = reinterpret_cast<int2*>(ws + off_vs);
 
   const float invT = greedy ? 1.0f : 1.0f / temperature;
-  RowsArgs ra;
-  memset(&ra, 0, sizeof(ra));
-  ra.B = B;
-  ra.gamma = gamma;
-  ra.V = V;
-  ra.n_chunks = n_chunks;
-  ra.greedy = greedy;
-  ra.T = target;
-  ra.tsb = t_stride_b;
-  ra.tsk = t_stride_k;
-  ra.K = K;
-  ra.req = req_ids;
-  ra.s2 = greedy ? kLog2e : kLog2e / temperature;
-  ra.seed = seed;
-  ra.pf = rpf;
-  ra.pi = rpi;
-  ra.err = c->dev_err;
-  DSPARK_HIP(c, launch(verify_rows_kernel(), dim3(n_chunks, rows), dim3(256), &ra, stream));
+  for (int w = 0; w < n_win; ++w) {
+    const int nrows = win_hi[w] - win_lo[w] + 1;
+    RowsArgs ra;
+    memset(&ra, 0, sizeof(ra));
+    ra.B = B;
+    ra.gamma = gamma;
+    ra.V = V;
+    ra.n_chunks = win_chunks[w];
+    ra.pstride = n_chunks;
+    ra.greedy = greedy;
+    ra.lo = win_lo[w];
+    ra.hi = win_hi[w];
+    ra.vstate = w == 0 ? nullptr : vstate;
+    ra.T = target;
+    ra.tsb = t_stride_b;
+    ra.tsk = t_stride_k;
+    ra.K = K;
+    ra.req = req_ids;
+    ra.s2 = greedy ? kLog2e : kLog2e / temperature;
+    ra.seed = seed;
+    ra.pf = rpf;
+    ra.pi = rpi;
+    ra.err = c->dev_err;
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), dim3(win_chunks[w], B * nrows), dim3(256), &ra,
+                      stream)))
+      return rc;
 
-  DecideArgs da;
-  memset(&da, 0, sizeof(da));
-  da.B = B;
-  da.gamma = gamma;
-  da.V = V;
-  da.n_chunks = n_chunks;
-  da.greedy = greedy;
-  da.T = target;
-  da.tsb = t_stride_b;
-  da.tsk = t_stride_k;
-  da.K = K;
-  da.req = req_ids;
-  da.tokens = tokens;
-  da.lse = lse;
-  da.ytok = ytok;
-  da.invT = invT;
-  da.seed = seed;
-  da.pf = rpf;
-  da.pi = rpi;
-  da.accept_len = accept_len;
-  da.out_tokens = out_tokens;
-  da.resid_k = resid_k;
-  da.resid_lt = resid_lt;
-  da.err = c->dev_err;
-  DSPARK_HIP(c, launch(verify_decide_kernel(), dim3(B), dim3(64), &da, stream));
+    DecideArgs da;
+    memset(&da, 0, sizeof(da));
+    da.B = B;
+    da.gamma = gamma;
+    da.V = V;
+    da.n_chunks = win_chunks[w];
+    da.pstride = n_chunks;
+    da.greedy = greedy;
+    da.lo = win_lo[w];
+    da.hi = win_hi[w];
+    da.first = w == 0;
+    da.vstate = vstate;
+    da.T = target;
+    da.tsb = t_stride_b;
+    da.tsk = t_stride_k;
+    da.K = K;
+    da.req = req_ids;
+    da.tokens = tokens;
+    da.lse = lse;
+    da.ytok = ytok;
+    da.invT = invT;
+    da.seed = seed;
+    da.pf = rpf;
+    da.pi = rpi;
+    da.accept_len = accept_len;
+    da.out_tokens = out_tokens;
+    da.resid_k = resid_k;
+    da.resid_lt = resid_lt;
+    da.err = c->dev_err;
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &da, stream)))
+      return rc;
+  }
   if (greedy) return DSPARK_OK;
 
   SweepArgs sa;
@@ -559,7 +679,7 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   sa.pf = spf;
   sa.pi = spi;
   sa.err = c->dev_err;
-  DSPARK_HIP(c, launch(sweep_kernel((int)wdtype, r, kModeResidual), dim3(pl.grid), dim3(256), &sa, stream));
+  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, sweep_kernel((int)wdtype, r, kModeResidual, pl.shared), dim3(pl.grid), dim3(256), &sa, stream))) return rc;
 
   CombineArgs ca;
   memset(&ca, 0, sizeof(ca));
@@ -573,7 +693,7 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   ca.accept_len = accept_len;
   ca.out_tokens = out_tokens;
   ca.err = c->dev_err;
-  DSPARK_HIP(c, launch(combine_resid_kernel(), dim3(B), dim3(64), &ca, stream));
+  if ((rc = klaunch(c, DSPARK_K_RESID_COMBINE, combine_resid_kernel(), dim3(B), dim3(256), &ca, stream))) return rc;
   return DSPARK_OK;
 }
 

@@ -57,6 +57,9 @@ struct CombineArgs {
 
 struct RowsArgs {
   int B, gamma, V, n_chunks, greedy;
+  int lo, hi;                    // 1-based rows of this window
+  int pstride;                   // partials per row in pf / pi
+  const int2* vstate;            // per request {accepted so far, next row (0 = done)}; null = all from row 1
   const float* T;
   int64_t tsb, tsk;
   const int32_t* K;
@@ -70,6 +73,10 @@ struct RowsArgs {
 
 struct DecideArgs {
   int B, gamma, V, n_chunks, greedy;
+  int lo, hi;                    // 1-based rows of this window
+  int pstride;                   // partials per row in pf / pi
+  int first;                     // first window: every request starts at row 1
+  int2* vstate;
   const float* T;
   int64_t tsb, tsk;
   const int32_t* K;
@@ -112,8 +119,10 @@ struct SchedArgs {
 };
 
 // Kernel lookup (host stubs usable with hipLaunchKernel and graph nodes).
-// `wdtype`: 0 = fp32, 1 = bf16.  Returns nullptr for unsupported r.
-const void* sweep_kernel(int wdtype, int r, int mode);
+// `wdtype`: 0 = fp32, 1 = bf16.  `shared`: the workgroup-shared W2-tile
+// variant (bf16, r in {128, 256}; grid = row-group quads x chunks) instead of
+// the private-tile one (grid = waves / 4).  Returns nullptr if unsupported.
+const void* sweep_kernel(int wdtype, int r, int mode, int shared);
 const void* combine_draft_kernel();
 const void* combine_resid_kernel();
 const void* verify_rows_kernel();

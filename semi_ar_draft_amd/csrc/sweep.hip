@@ -75,56 +75,86 @@ __device__ __forceinline__ void lane_init(LaneState& st) {
   st.fidx = 0x7fffffff;
 }
 
-// Fold four z values (vocabulary v0..v0+3 of one request) into the state.
+// Fold four z values (vocabulary v0..v0+3 of one request; z = U + bias came
+// out of the MFMA, whose accumulator was initialised with U) into the state.
+//
+// Sampling uses the exponential-race form of Gumbel-max: with E = -log2(u),
+// the base-2 key y2 - log2(E) beats the running best K iff
+// E < exp2(y2 - K) = exp2(y2 - m) * exp2(m - K).  exp2(y2 - m) is the
+// softmax term already at hand, so most elements cost one log and a compare;
+// the exact key (second log) is formed only for the rare candidates, which
+// are then compared exactly.
 template <int MODE>
-__device__ __forceinline__ void epilogue(LaneState& st, const float4 u, const f32x4_t acc,
-                                         const float4 t, int v0, uint32_t klo, uint32_t khi,
-                                         float invT, float s2, float ld, float lt) {
-  const float z[4] = {u.x + acc[0], u.y + acc[1], u.z + acc[2], u.w + acc[3]};
+__device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const float4 t, int v0,
+                                         uint32_t klo, uint32_t khi, float invT, float s2, float ld,
+                                         float lt) {
   if constexpr (MODE == kModeDraftGreedy || MODE == kModeDraftSample) {
-    float y2[4];
+    const float zt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    const float mn = fmaxf(st.m, zt * s2);
+    float e[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y2[i] = z[i] * s2;
-    const float mt = fmaxf(fmaxf(y2[0], y2[1]), fmaxf(y2[2], y2[3]));
-    const float mn = fmaxf(st.m, mt);
-    float acc_s = st.s * fast_exp2(st.m - mn);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc_s += fast_exp2(y2[i] - mn);
-    st.s = acc_s;
+    for (int i = 0; i < 4; ++i) e[i] = fast_exp2(__builtin_fmaf(z[i], s2, -mn));
+    st.s = st.s * fast_exp2(st.m - mn) + ((e[0] + e[1]) + (e[2] + e[3]));
     st.m = mn;
+    if constexpr (MODE == kModeDraftGreedy) {
+      if (zt > st.key) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float key;
-      if constexpr (MODE == kModeDraftGreedy) {
-        key = z[i];
-      } else {
-        const float uu = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + i)));
-        key = y2[i] - gumbel_log2_term(uu);
+        for (int i = 3; i >= 0; --i) {
+          if (z[i] == zt) st.idx = v0 + i;   // lowest index of the group maximum
+        }
+        st.key = zt;
       }
-      if (key > st.key) {
-        st.key = key;
-        st.idx = v0 + i;
-        st.zb = z[i];
+    } else {
+      float E[4];
+      const float F = fast_exp2(mn - st.key);
+      bool cand = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        E[i] = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + i))));
+        cand |= E[i] < e[i] * F;
+      }
+      if (cand) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float key = __builtin_fmaf(z[i], s2, -fast_log2(E[i]));
+          if (key > st.key) {
+            st.key = key;
+            st.idx = v0 + i;
+            st.zb = z[i];
+          }
+        }
       }
     }
   } else {
+    // residual: r_v = p_t(v) - p_d(v); key log2(r) - log2(E) beats K iff
+    // r > E * 2^K; the target fallback key log2(p_t) - log2(E) likewise.
     const float tv[4] = {t.x, t.y, t.z, t.w};
+    const float FK = fast_exp2(st.key);
+    const float FF = fast_exp2(st.fkey);
+    float E[4], pt[4], r[4];
+    bool cand = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float lpd = __builtin_fmaf(z[i], invT, -ld);    // ln p_d(v)
-      const float lpt = __builtin_fmaf(tv[i], invT, -lt);   // ln p_t(v)
-      const float r = fast_exp2(lpt * kLog2e) - fast_exp2(lpd * kLog2e);
-      const float uu = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + i)));
-      const float gl = gumbel_log2_term(uu);
-      const float key = (r > 0.0f) ? fast_log2(r) - gl : -INFINITY;
-      if (key > st.key) {
-        st.key = key;
-        st.idx = v0 + i;
-      }
-      const float fkey = __builtin_fmaf(lpt, kLog2e, -gl);
-      if (fkey > st.fkey) {
-        st.fkey = fkey;
-        st.fidx = v0 + i;
+      pt[i] = fast_exp2(__builtin_fmaf(tv[i], invT, -lt) * kLog2e);
+      const float pd = fast_exp2(__builtin_fmaf(z[i], invT, -ld) * kLog2e);
+      r[i] = pt[i] - pd;
+      E[i] = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + i))));
+      cand |= (r[i] > 0.0f && r[i] > E[i] * FK) || (pt[i] > E[i] * FF);
+    }
+    if (cand) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lE = fast_log2(E[i]);
+        const float key = (r[i] > 0.0f) ? fast_log2(r[i]) - lE : -INFINITY;
+        if (key > st.key) {
+          st.key = key;
+          st.idx = v0 + i;
+        }
+        const float fkey = fast_log2(pt[i]) - lE;
+        if (fkey > st.fkey) {
+          st.fkey = fkey;
+          st.fidx = v0 + i;
+        }
       }
     }
   }
@@ -163,10 +193,124 @@ __device__ __forceinline__ int xcd_logical_block(int p, int n) {
   return (p & 7) * (n >> 3) + (p >> 3);
 }
 
+// Per-lane row state of one wave: the two 16-row MFMA blocks of row group rg.
+// A row that is not active (past B, or no residual pending) reads request
+// 0's first row so that every load is unconditional; its statistics are
+// never written.
 template <typename WT, int R, int MODE>
-__global__ __launch_bounds__(256) void sweep_kernel_impl(const SweepArgs a) {
+struct WaveRows {
   using F = Frag<WT, R>;
-  constexpr int NS = F::NS;
+  using FragT = typename F::T;
+  static constexpr int NS = F::NS;
+  bool ok[2];
+  int rows[2];
+  int64_t uoff[2], toff[2];
+  uint32_t klo[2], khi[2];
+  float ld[2], lt[2];
+  FragT H[2][NS];
+
+  __device__ __forceinline__ void setup(const SweepArgs& a, int rg, int j, int q) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int b = rg * kRowsPerWave + nb * 16 + j;
+      bool v = rg < a.n_rg && b < a.B;
+      int kk = a.k;
+      if constexpr (MODE == kModeResidual) {
+        kk = v ? a.resid_k[b] : 0;
+        v = v && kk > 0 && kk <= a.gamma;
+      }
+      int prev = 0;
+      uoff[nb] = 0;
+      toff[nb] = 0;
+      klo[nb] = khi[nb] = 0;
+      ld[nb] = lt[nb] = 0.0f;
+      if (v) {
+        prev = (kk == 1) ? a.anchor[b] : a.tokens[(int64_t)b * a.gamma + kk - 2];
+        if ((unsigned)prev >= (unsigned)a.V) {
+          atomicOr(a.err, kErrToken);
+          prev = 0;
+        }
+        uoff[nb] = (int64_t)b * a.usb + (int64_t)(kk - 1) * a.usk;
+        if constexpr (MODE != kModeDraftGreedy) {
+          const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
+          const uint64_t key =
+              stream_key(a.seed, req, (uint32_t)kk, MODE == kModeResidual ? kResid : kDraft);
+          klo[nb] = (uint32_t)key;
+          khi[nb] = (uint32_t)(key >> 32);
+        }
+        if constexpr (MODE == kModeResidual) {
+          toff[nb] = (int64_t)b * a.tsb + (int64_t)(kk - 1) * a.tsk;
+          ld[nb] = a.lse[(int64_t)b * a.gamma + kk - 1];
+          lt[nb] = a.resid_lt[b];
+        }
+      }
+      ok[nb] = v;
+      rows[nb] = b;
+      const WT* w1row = static_cast<const WT*>(a.W1) + (int64_t)prev * R;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) H[nb][s] = F::load(w1row, s, q);
+    }
+  }
+
+  __device__ __forceinline__ void load_ut(const SweepArgs& a, int t, int q, float4 (&uu)[2],
+                                          float4 (&tt)[2]) const {
+    const int v0 = t * kTileV;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      uu[nb] = *reinterpret_cast<const float4*>(a.U + uoff[nb] + v0 + 4 * q);
+      if constexpr (MODE == kModeResidual)
+        tt[nb] = *reinterpret_cast<const float4*>(a.T + toff[nb] + v0 + 4 * q);
+      else
+        tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+
+  // z = U + bias for both blocks (U initialises the accumulators), then fold.
+  __device__ __forceinline__ void compute(const SweepArgs& a, LaneState (&st)[2], int t, int q,
+                                          const FragT (&A)[NS], const float4 (&uu)[2],
+                                          const float4 (&tt)[2]) const {
+    f32x4_t acc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[nb] = f32x4_t{uu[nb].x, uu[nb].y, uu[nb].z, uu[nb].w};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[nb] = F::mma(A[s], H[nb][s], acc[nb]);
+    }
+    const int vb = t * kTileV + 4 * q;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+      epilogue<MODE>(st[nb], acc[nb], tt[nb], vb, klo[nb], khi[nb], a.invT, a.s2, ld[nb], lt[nb]);
+  }
+
+  __device__ __forceinline__ void finish(const SweepArgs& a, LaneState (&st)[2], int q, int vc) const {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      lane_merge<MODE>(st[nb], 16);
+      lane_merge<MODE>(st[nb], 32);
+      if (q == 0 && ok[nb]) {
+        const int64_t o = (int64_t)rows[nb] * a.n_vc + vc;
+        if constexpr (MODE == kModeResidual) {
+          a.pf[o] = make_float4(st[nb].key, st[nb].fkey, 0.f, 0.f);
+          a.pi[o] = make_int2(st[nb].idx, st[nb].fidx);
+        } else {
+          a.pf[o] = make_float4(st[nb].m, st[nb].s, st[nb].key, st[nb].zb);
+          a.pi[o] = make_int2(st[nb].idx, 0);
+        }
+      }
+    }
+  }
+};
+
+// Private-tile variant: every wave owns its vocabulary chunk and loads its W2
+// tiles itself (used when no two waves share a chunk, e.g. B <= 64, and for
+// fp32 or narrow weights).  Double-buffered in registers.
+template <typename WT, int R, int MODE>
+__global__ __launch_bounds__(256) void sweep_private_impl(const SweepArgs a) {
+  using WR = WaveRows<WT, R, MODE>;
+  using F = typename WR::F;
+  using FragT = typename WR::FragT;
+  constexpr int NS = WR::NS;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int q = lane >> 4;
@@ -176,194 +320,225 @@ __global__ __launch_bounds__(256) void sweep_kernel_impl(const SweepArgs a) {
   const int rg = gw % a.n_rg;
   const int vc = gw / a.n_rg;
   if (vc >= a.n_vc) return;
-
-  bool ok[2];
-  int rows[2];
-  const float* urow[2];
-  const float* trow[2];
-  uint32_t klo[2], khi[2];
-  float ld[2], lt[2];
-  typename F::T H[2][NS];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int b = rg * kRowsPerWave + nb * 16 + j;
-    bool v = b < a.B;
-    int kk = a.k;
-    if constexpr (MODE == kModeResidual) {
-      kk = v ? a.resid_k[b] : 0;
-      v = v && kk > 0 && kk <= a.gamma;
-    }
-    int prev = 0;
-    urow[nb] = a.U;
-    trow[nb] = a.T;
-    klo[nb] = khi[nb] = 0;
-    ld[nb] = lt[nb] = 0.0f;
-    if (v) {
-      prev = (kk == 1) ? a.anchor[b] : a.tokens[(int64_t)b * a.gamma + kk - 2];
-      if ((unsigned)prev >= (unsigned)a.V) {
-        atomicOr(a.err, kErrToken);
-        prev = 0;
-      }
-      urow[nb] = a.U + (int64_t)b * a.usb + (int64_t)(kk - 1) * a.usk;
-      if constexpr (MODE != kModeDraftGreedy) {
-        const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
-        const uint64_t key =
-            stream_key(a.seed, req, (uint32_t)kk, MODE == kModeResidual ? kResid : kDraft);
-        klo[nb] = (uint32_t)key;
-        khi[nb] = (uint32_t)(key >> 32);
-      }
-      if constexpr (MODE == kModeResidual) {
-        trow[nb] = a.T + (int64_t)b * a.tsb + (int64_t)(kk - 1) * a.tsk;
-        ld[nb] = a.lse[(int64_t)b * a.gamma + kk - 1];
-        lt[nb] = a.resid_lt[b];
-      }
-    }
-    ok[nb] = v;
-    rows[nb] = b;
-    const WT* w1row = static_cast<const WT*>(a.W1) + (int64_t)prev * R;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) H[nb][s] = v ? F::load(w1row, s, q) : F::zero();
-  }
+  WR w;
+  w.setup(a, rg, j, q);
   if constexpr (MODE == kModeResidual) {
-    if (!__any(ok[0] || ok[1])) return;
+    if (!__any(w.ok[0] || w.ok[1])) return;
   }
-
   LaneState st[2];
   lane_init(st[0]);
   lane_init(st[1]);
-
   const int t0 = (int)((int64_t)a.n_tiles * vc / a.n_vc);
   const int t1 = (int)((int64_t)a.n_tiles * (vc + 1) / a.n_vc);
-  const WT* W2 = static_cast<const WT*>(a.W2);
-  for (int t = t0; t < t1; ++t) {
-    const int v0 = t * kTileV;
-    const WT* w2row = W2 + (int64_t)(v0 + j) * R;
-    typename F::T A[NS];
+  const WT* __restrict__ W2 = static_cast<const WT*>(a.W2);
+  auto load_a = [&](int t, FragT (&A)[NS]) {
+    const WT* w2row = W2 + (int64_t)(t * kTileV + j) * R;
 #pragma unroll
     for (int s = 0; s < NS; ++s) A[s] = F::load(w2row, s, q);
-    float4 uu[2], tt[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      uu[nb] = ok[nb] ? *reinterpret_cast<const float4*>(urow[nb] + v0 + 4 * q)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (MODE == kModeResidual) {
-        tt[nb] = ok[nb] ? *reinterpret_cast<const float4*>(trow[nb] + v0 + 4 * q)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-      } else {
-        tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-    f32x4_t acc[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[nb] = F::mma(A[s], H[nb][s], acc[nb]);
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if (ok[nb])
-        epilogue<MODE>(st[nb], uu[nb], acc[nb], tt[nb], v0 + 4 * q, klo[nb], khi[nb], a.invT,
-                       a.s2, ld[nb], lt[nb]);
+  };
+  if (t0 < t1) {
+    FragT A0[NS], A1[NS];
+    float4 u0[2], u1[2], x0[2], x1[2];
+    load_a(t0, A0);
+    w.load_ut(a, t0, q, u0, x0);
+    for (int t = t0; t < t1; t += 2) {
+      const int tn = min(t + 1, t1 - 1);
+      load_a(tn, A1);
+      w.load_ut(a, tn, q, u1, x1);
+      w.compute(a, st, t, q, A0, u0, x0);
+      if (t + 1 >= t1) break;
+      const int tn2 = min(t + 2, t1 - 1);
+      load_a(tn2, A0);
+      w.load_ut(a, tn2, q, u0, x0);
+      w.compute(a, st, t + 1, q, A1, u1, x1);
     }
   }
+  w.finish(a, st, q, vc);
+}
 
+// Shared-tile variant (bf16): the four waves of a workgroup own four row
+// groups (128 requests) of one vocabulary chunk.  Each W2 tile -- 16
+// vocabulary rows of r bf16, one contiguous block -- is read from HBM once
+// per workgroup with fully coalesced 16-byte loads, staged in LDS (double
+// buffered, one barrier per tile) and read back by every wave as its MFMA A
+// fragments.  Rows are padded by 16 bytes so that the 16 lanes of a
+// ds_read_b128 phase hit disjoint banks.
+template <int R, int MODE>
+__global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
+  using WR = WaveRows<uint16_t, R, MODE>;
+  using FragT = typename WR::FragT;
+  constexpr int NS = WR::NS;
+  constexpr int kRowBytes = R * 2;
+  constexpr int kStride = kRowBytes + 16;           // padded LDS row
+  constexpr int kTileBytes = kTileV * kRowBytes;    // contiguous in HBM
+  constexpr int kParts = kTileBytes / (256 * 16);   // 16-byte loads per thread
+  static_assert(kParts >= 1 && kTileBytes % (256 * 16) == 0, "tile must split into 16-byte loads");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileV * kStride];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int q = lane >> 4;
+  const int j = lane & 15;
+  const int blk = a.xcd_remap ? xcd_logical_block(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int n_rq = (a.n_rg + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int g = blk % n_rq;
+  const int vc = blk / n_rq;
+  if (vc >= a.n_vc) return;                          // uniform over the block
+  WR w;
+  w.setup(a, g * kWavesPerBlock + wid, j, q);
+  const bool wave_active = __any(w.ok[0] || w.ok[1]);
+  if constexpr (MODE == kModeResidual) {
+    if (!__syncthreads_or(wave_active)) return;      // uniform over the block
+  }
+  LaneState st[2];
+  lane_init(st[0]);
+  lane_init(st[1]);
+  const int t0 = (int)((int64_t)a.n_tiles * vc / a.n_vc);
+  const int t1 = (int)((int64_t)a.n_tiles * (vc + 1) / a.n_vc);
+  const unsigned char* W2 = static_cast<const unsigned char*>(a.W2);
+
+  auto gload = [&](int t, uint4 (&part)[kParts]) {
+    const unsigned char* src = W2 + (int64_t)t * kTileBytes;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    lane_merge<MODE>(st[nb], 16);
-    lane_merge<MODE>(st[nb], 32);
-    if (q == 0 && ok[nb]) {
-      const int64_t o = (int64_t)rows[nb] * a.n_vc + vc;
-      if constexpr (MODE == kModeResidual) {
-        a.pf[o] = make_float4(st[nb].key, st[nb].fkey, 0.f, 0.f);
-        a.pi[o] = make_int2(st[nb].idx, st[nb].fidx);
-      } else {
-        a.pf[o] = make_float4(st[nb].m, st[nb].s, st[nb].key, st[nb].zb);
-        a.pi[o] = make_int2(st[nb].idx, 0);
+    for (int p = 0; p < kParts; ++p)
+      part[p] = *reinterpret_cast<const uint4*>(src + (p * 256 + threadIdx.x) * 16);
+  };
+  auto lstore = [&](int buf, const uint4 (&part)[kParts]) {
+#pragma unroll
+    for (int p = 0; p < kParts; ++p) {
+      const int o = (p * 256 + threadIdx.x) * 16;
+      *reinterpret_cast<uint4*>(&lds[buf][(o / kRowBytes) * kStride + (o % kRowBytes)]) = part[p];
+    }
+  };
+  auto lread = [&](int buf, FragT (&A)[NS]) {
+    const unsigned char* row = &lds[buf][j * kStride + 16 * q];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) A[s] = *reinterpret_cast<const FragT*>(row + 64 * s);
+  };
+
+  if (t0 < t1) {
+    // The prefetch of tile t+1 is clamped to the last tile; the final
+    // iteration stores it into the idle buffer, which nothing reads.
+    uint4 part[kParts];
+    float4 u0[2], u1[2], x0[2], x1[2];
+    gload(t0, part);
+    w.load_ut(a, t0, q, u0, x0);
+    lstore(0, part);
+    __syncthreads();
+    int buf = 0;
+    for (int t = t0; t < t1; ++t) {
+      const int tn = min(t + 1, t1 - 1);
+      gload(tn, part);
+      w.load_ut(a, tn, q, u1, x1);
+      if (wave_active) {
+        FragT A[NS];
+        lread(buf, A);
+        w.compute(a, st, t, q, A, u0, x0);
+      }
+      lstore(buf ^ 1, part);
+      __syncthreads();
+      buf ^= 1;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        u0[nb] = u1[nb];
+        x0[nb] = x1[nb];
       }
     }
+  }
+  w.finish(a, st, q, vc);
+}
+
+constexpr int kCombineThreads = 256;
+
+struct DraftPart {
+  float m, s, key, zb;
+  int idx;
+};
+
+__device__ __forceinline__ void part_merge(DraftPart& a, const DraftPart& b) {
+  softmax_merge(a.m, a.s, b.m, b.s);
+  if (key_beats(b.key, b.idx, a.key, a.idx)) {
+    a.key = b.key;
+    a.idx = b.idx;
+    a.zb = b.zb;
   }
 }
 
-// One wave per request row: merge the per-chunk partials of a draft
-// position, write x_k, ln-normaliser and y at x_k.
-__global__ __launch_bounds__(64) void combine_draft_impl(const CombineArgs a) {
+__device__ __forceinline__ DraftPart part_shfl(const DraftPart& p, int mask) {
+  return DraftPart{shfl_xor(p.m, mask), shfl_xor(p.s, mask), shfl_xor(p.key, mask), shfl_xor(p.zb, mask),
+                   shfl_xor(p.idx, mask)};
+}
+
+// One 256-thread workgroup per request row: merge the per-chunk partials of
+// a draft position in a fixed order, write x_k, the log-normaliser and y at
+// x_k.
+__global__ __launch_bounds__(kCombineThreads) void combine_draft_impl(const CombineArgs a) {
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  float m = -INFINITY, s = 0.f, key = -INFINITY, zb = 0.f;
-  int idx = 0x7fffffff;
+  DraftPart p{-INFINITY, 0.f, -INFINITY, 0.f, 0x7fffffff};
   const int64_t base = (int64_t)b * a.n_vc;
-  for (int i = lane; i < a.n_vc; i += 64) {
-    const float4 p = a.pf[base + i];
-    const int pi = a.pi[base + i].x;
-    softmax_merge(m, s, p.x, p.y);
-    if (key_beats(p.z, pi, key, idx)) {
-      key = p.z;
-      idx = pi;
-      zb = p.w;
-    }
+  for (int i = threadIdx.x; i < a.n_vc; i += kCombineThreads) {
+    const float4 f = a.pf[base + i];
+    part_merge(p, DraftPart{f.x, f.y, f.z, f.w, a.pi[base + i].x});
   }
 #pragma unroll
-  for (int mask = 1; mask < 64; mask <<= 1) {
-    const float m2 = shfl_xor(m, mask), s2 = shfl_xor(s, mask);
-    const float k2 = shfl_xor(key, mask), z2 = shfl_xor(zb, mask);
-    const int i2 = shfl_xor(idx, mask);
-    softmax_merge(m, s, m2, s2);
-    if (key_beats(k2, i2, key, idx)) {
-      key = k2;
-      idx = i2;
-      zb = z2;
-    }
-  }
-  if (lane == 0) {
+  for (int mask = 1; mask < 64; mask <<= 1) part_merge(p, part_shfl(p, mask));
+  __shared__ DraftPart red[kCombineThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = p;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) part_merge(p, red[w]);
+    int idx = p.idx;
     if ((unsigned)idx >= (unsigned)a.V) {
       atomicOr(a.err, kErrToken);
       idx = 0;
     }
     const int64_t o = (int64_t)b * a.gamma + a.k - 1;
     a.tokens[o] = idx;
-    a.lse[o] = (m + fast_log2(s)) * kLn2;
-    a.ytok[o] = a.greedy ? key : zb * a.invT;
+    a.lse[o] = (p.m + fast_log2(p.s)) * kLn2;
+    a.ytok[o] = a.greedy ? p.key : p.zb * a.invT;
   }
 }
 
-// One wave per request with a pending residual draw: merge its partials and
-// write the emitted token after the accepted prefix.
-__global__ __launch_bounds__(64) void combine_resid_impl(const CombineArgs a) {
+struct ResidPart {
+  float key, fkey;
+  int idx, fidx;
+};
+
+__device__ __forceinline__ void resid_merge(ResidPart& a, const ResidPart& b) {
+  if (key_beats(b.key, b.idx, a.key, a.idx)) {
+    a.key = b.key;
+    a.idx = b.idx;
+  }
+  if (key_beats(b.fkey, b.fidx, a.fkey, a.fidx)) {
+    a.fkey = b.fkey;
+    a.fidx = b.fidx;
+  }
+}
+
+// One workgroup per request with a pending residual draw: merge its partials
+// and write the emitted token after the accepted prefix.
+__global__ __launch_bounds__(kCombineThreads) void combine_resid_impl(const CombineArgs a) {
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
   if (a.resid_k[b] <= 0) return;
-  float key = -INFINITY, fkey = -INFINITY;
-  int idx = 0x7fffffff, fidx = 0x7fffffff;
+  ResidPart p{-INFINITY, -INFINITY, 0x7fffffff, 0x7fffffff};
   const int64_t base = (int64_t)b * a.n_vc;
-  for (int i = lane; i < a.n_vc; i += 64) {
-    const float4 p = a.pf[base + i];
+  for (int i = threadIdx.x; i < a.n_vc; i += kCombineThreads) {
+    const float4 f = a.pf[base + i];
     const int2 pi = a.pi[base + i];
-    if (key_beats(p.x, pi.x, key, idx)) {
-      key = p.x;
-      idx = pi.x;
-    }
-    if (key_beats(p.y, pi.y, fkey, fidx)) {
-      fkey = p.y;
-      fidx = pi.y;
-    }
+    resid_merge(p, ResidPart{f.x, f.y, pi.x, pi.y});
   }
 #pragma unroll
-  for (int mask = 1; mask < 64; mask <<= 1) {
-    const float k2 = shfl_xor(key, mask), f2 = shfl_xor(fkey, mask);
-    const int i2 = shfl_xor(idx, mask), j2 = shfl_xor(fidx, mask);
-    if (key_beats(k2, i2, key, idx)) {
-      key = k2;
-      idx = i2;
-    }
-    if (key_beats(f2, j2, fkey, fidx)) {
-      fkey = f2;
-      fidx = j2;
-    }
-  }
-  if (lane == 0) {
-    int tok = (key > -INFINITY) ? idx : fidx;
+  for (int mask = 1; mask < 64; mask <<= 1)
+    resid_merge(p, ResidPart{shfl_xor(p.key, mask), shfl_xor(p.fkey, mask), shfl_xor(p.idx, mask),
+                             shfl_xor(p.fidx, mask)});
+  __shared__ ResidPart red[kCombineThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = p;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) resid_merge(p, red[w]);
+    int tok = (p.key > -INFINITY) ? p.idx : p.fidx;
     if ((unsigned)tok >= (unsigned)a.V) {
       atomicOr(a.err, kErrToken);
       tok = 0;
@@ -375,26 +550,46 @@ __global__ __launch_bounds__(64) void combine_resid_impl(const CombineArgs a) {
 
 }  // namespace
 
-const void* sweep_kernel(int wdtype, int r, int mode) {
-#define DSPARK_SWEEP_CASE(WT, R)                                                        \
-  if (r == R) {                                                                         \
-    if (mode == kModeDraftGreedy) return (const void*)&sweep_kernel_impl<WT, R, kModeDraftGreedy>; \
-    if (mode == kModeDraftSample) return (const void*)&sweep_kernel_impl<WT, R, kModeDraftSample>; \
-    if (mode == kModeResidual) return (const void*)&sweep_kernel_impl<WT, R, kModeResidual>;       \
-    return nullptr;                                                                     \
+namespace {
+
+template <int R>
+const void* shared_for(int mode) {
+  if (mode == kModeDraftGreedy) return (const void*)&sweep_shared_impl<R, kModeDraftGreedy>;
+  if (mode == kModeDraftSample) return (const void*)&sweep_shared_impl<R, kModeDraftSample>;
+  if (mode == kModeResidual) return (const void*)&sweep_shared_impl<R, kModeResidual>;
+  return nullptr;
+}
+
+template <typename WT, int R>
+const void* private_for(int mode) {
+  if (mode == kModeDraftGreedy) return (const void*)&sweep_private_impl<WT, R, kModeDraftGreedy>;
+  if (mode == kModeDraftSample) return (const void*)&sweep_private_impl<WT, R, kModeDraftSample>;
+  if (mode == kModeResidual) return (const void*)&sweep_private_impl<WT, R, kModeResidual>;
+  return nullptr;
+}
+
+template <typename WT>
+const void* private_for_r(int r, int mode) {
+  switch (r) {
+    case 32: return private_for<WT, 32>(mode);
+    case 64: return private_for<WT, 64>(mode);
+    case 128: return private_for<WT, 128>(mode);
+    case 256: return private_for<WT, 256>(mode);
+    default: return nullptr;
   }
-  if (wdtype == 1) {
-    DSPARK_SWEEP_CASE(uint16_t, 32)
-    DSPARK_SWEEP_CASE(uint16_t, 64)
-    DSPARK_SWEEP_CASE(uint16_t, 128)
-    DSPARK_SWEEP_CASE(uint16_t, 256)
-  } else if (wdtype == 0) {
-    DSPARK_SWEEP_CASE(float, 32)
-    DSPARK_SWEEP_CASE(float, 64)
-    DSPARK_SWEEP_CASE(float, 128)
-    DSPARK_SWEEP_CASE(float, 256)
+}
+
+}  // namespace
+
+const void* sweep_kernel(int wdtype, int r, int mode, int shared) {
+  if (shared) {
+    if (wdtype != 1) return nullptr;
+    if (r == 128) return shared_for<128>(mode);
+    if (r == 256) return shared_for<256>(mode);
+    return nullptr;
   }
-#undef DSPARK_SWEEP_CASE
+  if (wdtype == 1) return private_for_r<uint16_t>(r, mode);
+  if (wdtype == 0) return private_for_r<float>(r, mode);
   return nullptr;
 }
 

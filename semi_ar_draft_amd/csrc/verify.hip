@@ -1,5 +1,8 @@
-// Verification: one streaming pass over the target rows 1..K_b+1 of every
-// request, then one wave per request that walks its positions in order.
+// Verification: streaming passes over the target rows of every request, then
+// one wave per request that walks its positions in order.  Rows are taken in
+// windows (rows 1-2, then the rest): a row after a request's first rejection
+// is never needed, so the later window only reads rows of requests that have
+// accepted every position so far.
 //
 // [blog] "形式化定义": the target scores every drafted position in one pass,
 // positions are checked in order, the first rejected one is replaced by a
@@ -90,12 +93,14 @@ __device__ __forceinline__ void row_sweep(RowState& st, const float4* p, int c0,
 }
 
 __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const RowsArgs a) {
-  const int row = blockIdx.y;
+  const int nrows = a.hi - a.lo + 1;
   const int chunk = blockIdx.x;
-  const int b = row / (a.gamma + 1);
-  const int k = row % (a.gamma + 1) + 1;
+  const int b = blockIdx.y / nrows;
+  const int k = a.lo + blockIdx.y % nrows;
+  if (a.vstate && a.vstate[b].y == 0) return;   // request already decided
   const int kb = clamp_k(a.K, b, a.gamma, a.err, chunk == 0 && k == 1 && threadIdx.x == 0);
   if (k > kb + 1) return;
+  const int row = b * (a.gamma + 1) + (k - 1);
   const bool bonus = (k == kb + 1);
   const float4* p = reinterpret_cast<const float4*>(a.T + (int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk);
   const int nv4 = a.V >> 2;
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const RowsArgs 
     RowState acc = red[0];
 #pragma unroll
     for (int w = 1; w < kRowsThreads / 64; ++w) row_merge(acc, red[w]);
-    const int64_t o = (int64_t)row * a.n_chunks + chunk;
+    const int64_t o = (int64_t)row * a.pstride + chunk;
     a.pf[o] = make_float4(acc.m, acc.s, acc.key, 0.f);
     a.pi[o] = acc.idx;
   }
@@ -134,17 +139,28 @@ __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const RowsArgs 
 
 constexpr int kMaxGamma = 32;
 
-// One wave per request: finish each examined row's statistics, then take the
-// accept decisions in order.  Writes the kept drafts, the compensation /
-// bonus token when it is known here, and the residual request otherwise.
+// One wave per request: finish the statistics of the rows of this window,
+// then continue the request's accept decisions in order.  Writes the kept
+// drafts, the compensation / bonus token when it is known here, the residual
+// request otherwise; a request that kept every row of the window and has
+// rows left stays pending for the next window.
 __global__ __launch_bounds__(64) void verify_decide_impl(const DecideArgs a) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
+  int A = 0;
+  int start = 1;
+  if (!a.first) {
+    const int2 vs = a.vstate[b];
+    if (vs.y == 0) return;
+    A = vs.x;
+    start = vs.y;
+  }
   const int kb = clamp_k(a.K, b, a.gamma, a.err, false);
+  const int last = min(a.hi, kb + 1);
   __shared__ float s_lt[kMaxGamma + 1];
   __shared__ int s_star[kMaxGamma + 1];
-  for (int k = 1; k <= kb + 1; ++k) {
-    const int64_t base = ((int64_t)b * (a.gamma + 1) + (k - 1)) * a.n_chunks;
+  for (int k = start; k <= last; ++k) {
+    const int64_t base = ((int64_t)b * (a.gamma + 1) + (k - 1)) * a.pstride;
     RowState st{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
     for (int c = lane; c < a.n_chunks; c += 64) {
       const float4 p = a.pf[base + c];
@@ -166,10 +182,11 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const DecideArgs a) {
   if (lane != 0) return;
   const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
   int32_t* out = a.out_tokens + (int64_t)b * (a.gamma + 1);
-  int A = 0;
   int final_tok = -1;
   int resid = 0;
-  for (int k = 1; k <= kb; ++k) {
+  bool rejected = false;
+  int k = start;
+  for (; k <= min(kb, a.hi); ++k) {
     int x = a.tokens[(int64_t)b * a.gamma + k - 1];
     if ((unsigned)x >= (unsigned)a.V) {
       atomicOr(a.err, kErrToken);
@@ -181,6 +198,7 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const DecideArgs a) {
         continue;
       }
       final_tok = s_star[k - 1];
+      rejected = true;
       break;
     }
     const float tx = a.T[(int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk + x];
@@ -195,18 +213,28 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const DecideArgs a) {
       continue;
     }
     resid = k;
+    rejected = true;
     break;
   }
-  if (final_tok < 0 && resid == 0) final_tok = s_star[kb];   // all kept: bonus from row K_b + 1
-  if ((unsigned)final_tok >= (unsigned)a.V && resid == 0) {
-    atomicOr(a.err, kErrToken);
-    final_tok = 0;
+  if (!rejected) {
+    if (kb + 1 > a.hi) {            // rows left: wait for the next window
+      a.vstate[b] = make_int2(A, k);
+      return;
+    }
+    final_tok = s_star[kb];         // all kept: bonus from row K_b + 1
   }
-  if (resid == 0) out[A] = final_tok;
+  if (resid == 0) {
+    if ((unsigned)final_tok >= (unsigned)a.V) {
+      atomicOr(a.err, kErrToken);
+      final_tok = 0;
+    }
+    out[A] = final_tok;
+  }
   for (int i = A + 1; i <= a.gamma; ++i) out[i] = -1;
   a.accept_len[b] = A;
   a.resid_k[b] = resid;
   a.resid_lt[b] = resid ? s_lt[resid - 1] : 0.f;
+  a.vstate[b] = make_int2(A, 0);
 }
 
 }  // namespace
