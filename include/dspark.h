@@ -120,8 +120,11 @@ int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
  * so that ln p_d(x_k) = ytok - lse.
  *
  * B >= 1; 1 <= gamma <= 32; V >= 16, V % 16 == 0; r in {32, 64, 128, 256}.
- * U:      float [B][>= gamma][V] at U + b*u_stride_b + (k-1)*u_stride_k;
- *         strides are multiples of 4 and the pointer 16-byte aligned.
+ * U:      float rows of V logits at U + b*u_stride_b + (k-1)*u_stride_k,
+ *         request-major ([B][>= gamma][V]: u_stride_k >= V, u_stride_b >=
+ *         gamma*u_stride_k) or position-major ([>= gamma][B][V]: u_stride_b
+ *         >= V, u_stride_k >= B*u_stride_b); strides are multiples of 4 and
+ *         the pointer 16-byte aligned.
  * W1:     [V][r] row-major (token -> rank-r vector), dtype wdtype.
  * W2:     the r x V matrix W2 stored column-major, i.e. an array [V][r] whose
  *         row v is column v (an LM-head layout), dtype wdtype.  Both weight

@@ -49,6 +49,8 @@ struct dspark_ctx {
   size_t ws_bytes = 0;
   int32_t* dev_err = nullptr;
   bool use_graph = true;
+  int sweep_waves_per_cu = 8;     // occupancy target of the vocabulary sweeps
+  int sweep_depth = 3;            // shared-tile sweeps: tiles prefetched ahead (1..3)
   std::vector<DraftGraph> graphs;
   // kernel timing (benchmarks): event pairs around every launch while enabled
   bool timing = false;
@@ -125,8 +127,8 @@ SweepPlan plan_sweep(const dspark_ctx* c, int B, int V, int r, int wdtype) {
   SweepPlan p;
   p.n_rg = (B + kRowsPerWave - 1) / kRowsPerWave;
   p.n_tiles = V / kTileV;
-  p.shared = (wdtype == DSPARK_BF16 && (r == 128 || r == 256) && p.n_rg >= 3) ? 1 : 0;
-  const int target_waves = 8 * c->cu_count;
+  p.shared = (wdtype == DSPARK_BF16 && (r == 128 || r == 256) && p.n_rg >= 3) ? c->sweep_depth : 0;
+  const int target_waves = c->sweep_waves_per_cu * c->cu_count;
   const int max_vc = p.n_tiles / 4 > 0 ? p.n_tiles / 4 : 1;
   long grid;
   if (p.shared) {
@@ -158,13 +160,19 @@ int plan_rows_chunks(int rows, int V) {
   return n;
 }
 
-int check_stream_rows(dspark_ctx* c, const char* name, const float* p, int64_t sb, int64_t sk, int rows,
+int check_stream_rows(dspark_ctx* c, const char* name, const float* p, int64_t sb, int64_t sk, int B, int rows,
                       int V) {
   if (!p) return fail(c, DSPARK_EINVAL, "%s is NULL", name);
   if (!aligned16(p)) return fail(c, DSPARK_EINVAL, "%s must be 16-byte aligned", name);
-  if ((sb & 3) || (sk & 3)) return fail(c, DSPARK_EINVAL, "%s strides must be multiples of 4", name);
-  if (sk < V) return fail(c, DSPARK_EINVAL, "%s position stride %lld < V", name, (long long)sk);
-  if (sb < (int64_t)rows * sk) return fail(c, DSPARK_EINVAL, "%s request stride too small", name);
+  if ((sb & 3) || (sk & 3) || sb <= 0 || sk <= 0)
+    return fail(c, DSPARK_EINVAL, "%s strides must be positive multiples of 4", name);
+  // rows (b, k) must not overlap: request-major ([B][rows][V]-like) or
+  // position-major ([rows][B][V]-like) placements
+  const bool req_major = sk >= V && sb >= (int64_t)rows * sk;
+  const bool pos_major = sb >= V && sk >= (int64_t)B * sb;
+  if (!req_major && !pos_major)
+    return fail(c, DSPARK_EINVAL, "%s strides (%lld, %lld) overlap rows of %d values", name, (long long)sb,
+                (long long)sk, V);
   return DSPARK_OK;
 }
 
@@ -318,6 +326,14 @@ int dspark_create(dspark_ctx** out, int device) {
   }
   const char* g = getenv("DSPARK_GRAPH");
   if (g && g[0] == '0') c->use_graph = false;
+  // tuning knob: target resident waves per CU for the vocabulary sweeps
+  const char* w = getenv("DSPARK_SWEEP_WAVES_PER_CU");
+  if (w) {
+    const int v = atoi(w);
+    if (v >= 1 && v <= 32) c->sweep_waves_per_cu = v;
+  }
+  const char* dp = getenv("DSPARK_SWEEP_DEPTH");
+  if (dp && dp[0] >= '1' && dp[0] <= '3' && dp[1] == 0) c->sweep_depth = dp[0] - '0';
   *out = c;
   return DSPARK_OK;
 }
@@ -401,7 +417,7 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
   if (!c) return DSPARK_EINVAL;
   int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
   if (rc) return rc;
-  if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, gamma, V))) return rc;
+  if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
   if (!W1 || !W2 || !anchor || !tokens || !lse || !ytok)
     return fail(c, DSPARK_EINVAL, "null pointer argument");
   if (!aligned16(W1) || !aligned16(W2)) return fail(c, DSPARK_EINVAL, "W1/W2 must be 16-byte aligned");
@@ -536,9 +552,9 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   if (!c) return DSPARK_EINVAL;
   int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
   if (rc) return rc;
-  if ((rc = check_stream_rows(c, "target", target, t_stride_b, t_stride_k, gamma + 1, V))) return rc;
+  if ((rc = check_stream_rows(c, "target", target, t_stride_b, t_stride_k, B, gamma + 1, V))) return rc;
   const bool greedy = temperature == 0.0f;
-  if (!greedy && (rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, gamma, V))) return rc;
+  if (!greedy && (rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
   if (!tokens || !accept_len || !out_tokens) return fail(c, DSPARK_EINVAL, "null pointer argument");
   if (!greedy && (!W1 || !W2 || !anchor || !lse || !ytok))
     return fail(c, DSPARK_EINVAL, "sampling verification needs U, W1, W2, anchor, lse and ytok");
@@ -679,7 +695,7 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   sa.pf = spf;
   sa.pi = spi;
   sa.err = c->dev_err;
-  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, sweep_kernel((int)wdtype, r, kModeResidual, pl.shared), dim3(pl.grid), dim3(256), &sa, stream))) return rc;
+  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, sweep_kernel((int)wdtype, r, kModeResidual, pl.shared > 2 ? 2 : pl.shared), dim3(pl.grid), dim3(256), &sa, stream))) return rc;
 
   CombineArgs ca;
   memset(&ca, 0, sizeof(ca));

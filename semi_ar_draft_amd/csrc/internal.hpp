@@ -119,9 +119,10 @@ struct SchedArgs {
 };
 
 // Kernel lookup (host stubs usable with hipLaunchKernel and graph nodes).
-// `wdtype`: 0 = fp32, 1 = bf16.  `shared`: the workgroup-shared W2-tile
-// variant (bf16, r in {128, 256}; grid = row-group quads x chunks) instead of
-// the private-tile one (grid = waves / 4).  Returns nullptr if unsupported.
+// `wdtype`: 0 = fp32, 1 = bf16.  `shared` = D in 1..3: the workgroup-shared
+// W2-tile variant prefetching D tiles ahead by LDS DMA (bf16, r in {128,
+// 256}; grid = row-group quads x chunks); 0: the private-tile variant (grid =
+// waves / 4).  Returns nullptr if unsupported.
 const void* sweep_kernel(int wdtype, int r, int mode, int shared);
 const void* combine_draft_kernel();
 const void* combine_resid_kernel();

@@ -356,24 +356,61 @@ __global__ __launch_bounds__(256) void sweep_private_impl(const SweepArgs a) {
   w.finish(a, st, q, vc);
 }
 
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+
+// Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's 16 bytes land at LDS byte address lds + 16 i; M0 carries the wave-
+// uniform base.  Written as inline assembly so that the compiler keeps no
+// books on it: its own wait-count tracking of such loads cannot tell the
+// slots of a ring apart and would wait for every load in flight before each
+// LDS read.  The kernels below order these loads explicitly with
+// ring_wait_barrier; the memory clobber keeps the compiler from moving memory
+// accesses across them.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight,
+// then join the workgroup barrier (no implicit drain, no fence).
+template <int N>
+__device__ __forceinline__ void ring_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+
 // Shared-tile variant (bf16): the four waves of a workgroup own four row
-// groups (128 requests) of one vocabulary chunk.  Each W2 tile -- 16
-// vocabulary rows of r bf16, one contiguous block -- is read from HBM once
-// per workgroup with fully coalesced 16-byte loads, staged in LDS (double
-// buffered, one barrier per tile) and read back by every wave as its MFMA A
-// fragments.  Rows are padded by 16 bytes so that the 16 lanes of a
-// ds_read_b128 phase hit disjoint banks.
-template <int R, int MODE>
+// groups (128 requests) of one vocabulary chunk.  Every byte of a tile step
+// -- the 16 x r W2 tile (one contiguous block in HBM) and each wave's U (and,
+// for the residual, target) rows -- is moved by direct global->LDS loads
+// (global_load_lds_dwordx4: no register staging), D tiles ahead, into a ring
+// of D + 1 LDS slots.  Before step t each wave waits until its share of tile
+// t has landed (vmcnt counts the later groups still in flight), then a
+// barrier makes every wave's share visible.
+//
+// LDS layouts are XOR-swizzled instead of padded (a DMA writes 1 KB
+// contiguously per wave): W2 16-byte chunk c of tile row r is stored at chunk
+// c ^ (r & 15) of that row; U float4 c of row j at position c ^ ((j >> 2) & 3).
+// Both make the 16 lanes of a ds_read_b128 phase hit disjoint banks.
+template <int R, int MODE, int D>
 __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   using WR = WaveRows<uint16_t, R, MODE>;
   using FragT = typename WR::FragT;
   constexpr int NS = WR::NS;
+  constexpr int NB = D + 1;                             // ring slots
   constexpr int kRowBytes = R * 2;
-  constexpr int kStride = kRowBytes + 16;           // padded LDS row
-  constexpr int kTileBytes = kTileV * kRowBytes;    // contiguous in HBM
-  constexpr int kParts = kTileBytes / (256 * 16);   // 16-byte loads per thread
-  static_assert(kParts >= 1 && kTileBytes % (256 * 16) == 0, "tile must split into 16-byte loads");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileV * kStride];
+  constexpr int kCPR = kRowBytes / 16;                  // 16-byte chunks per W2 row
+  constexpr int kTileBytes = kTileV * kRowBytes;
+  constexpr int kW2Inst = kTileBytes / (kWavesPerBlock * 1024);   // 1 KB per wave instruction
+  constexpr bool kResid = MODE == kModeResidual;
+  constexpr int kRowsInst = kResid ? 4 : 2;             // U (and T) rows: one per 16-row block
+  constexpr int kG = kW2Inst + kRowsInst;               // loads per wave per step
+  constexpr int kUOff = kTileBytes;                     // per wave: 2 x 1 KB of U
+  constexpr int kTOff = kTileBytes + kWavesPerBlock * 2048;
+  constexpr int kSlotBytes = kTileBytes + kWavesPerBlock * 2048 * (kResid ? 2 : 1);
+  static_assert(kW2Inst >= 1 && kTileBytes % (kWavesPerBlock * 1024) == 0, "tile must split into 1 KB loads");
+  static_assert(D >= 1 && (D - 1) * kG < 64, "ring depth");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NB * kSlotBytes];
 
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -383,68 +420,96 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   const int n_rq = (a.n_rg + kWavesPerBlock - 1) / kWavesPerBlock;
   const int g = blk % n_rq;
   const int vc = blk / n_rq;
-  if (vc >= a.n_vc) return;                          // uniform over the block
+  if (vc >= a.n_vc) return;                              // uniform over the block
   WR w;
   w.setup(a, g * kWavesPerBlock + wid, j, q);
   const bool wave_active = __any(w.ok[0] || w.ok[1]);
-  if constexpr (MODE == kModeResidual) {
-    if (!__syncthreads_or(wave_active)) return;      // uniform over the block
+  if constexpr (kResid) {
+    if (!__syncthreads_or(wave_active)) return;          // uniform over the block
   }
   LaneState st[2];
   lane_init(st[0]);
   lane_init(st[1]);
   const int t0 = (int)((int64_t)a.n_tiles * vc / a.n_vc);
   const int t1 = (int)((int64_t)a.n_tiles * (vc + 1) / a.n_vc);
-  const unsigned char* W2 = static_cast<const unsigned char*>(a.W2);
+  if (t0 >= t1) {
+    w.finish(a, st, q, vc);
+    return;
+  }
 
-  auto gload = [&](int t, uint4 (&part)[kParts]) {
-    const unsigned char* src = W2 + (int64_t)t * kTileBytes;
+  // DMA lane roles.  W2: lane of instruction p fills LDS chunk P = wid*64*kW2Inst
+  // + p*64 + lane of the tile.  Rows: lane i loads float4 (i & 3) ^ swz of row
+  // (i >> 2) of a 16-row block; row offsets come from the MFMA lane holding
+  // that row.
+  const int rj = lane >> 2;
+  const int rc = (lane & 3) ^ ((rj >> 2) & 3);
+  int64_t uoff_d[2], toff_d[2];
 #pragma unroll
-    for (int p = 0; p < kParts; ++p)
-      part[p] = *reinterpret_cast<const uint4*>(src + (p * 256 + threadIdx.x) * 16);
-  };
-  auto lstore = [&](int buf, const uint4 (&part)[kParts]) {
+  for (int nb = 0; nb < 2; ++nb) {
+    uoff_d[nb] = __shfl(w.uoff[nb], rj, 64);
+    toff_d[nb] = kResid ? __shfl(w.toff[nb], rj, 64) : 0;
+  }
+  const unsigned char* W2b = static_cast<const unsigned char*>(a.W2);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8_t*)ring;
+  const uint32_t w2_lds = __builtin_amdgcn_readfirstlane(wid * kW2Inst * 1024);
+  const uint32_t u_lds = __builtin_amdgcn_readfirstlane(kUOff + wid * 2048);
+  const uint32_t t_lds = __builtin_amdgcn_readfirstlane(kTOff + wid * 2048);
+  auto issue = [&](int t, int sidx) {
+    const int tc = min(t, t1 - 1);
+    const unsigned char* tile = W2b + (int64_t)tc * kTileBytes;
+    const uint32_t base = ring_lds + sidx * kSlotBytes;
 #pragma unroll
-    for (int p = 0; p < kParts; ++p) {
-      const int o = (p * 256 + threadIdx.x) * 16;
-      *reinterpret_cast<uint4*>(&lds[buf][(o / kRowBytes) * kStride + (o % kRowBytes)]) = part[p];
+    for (int p = 0; p < kW2Inst; ++p) {
+      const int P = (wid * kW2Inst + p) * 64 + lane;
+      const int r = P / kCPR;
+      const int c = (P % kCPR) ^ (r & 15);
+      dma16(tile + r * kRowBytes + c * 16, base + w2_lds + p * 1024);
+    }
+    const int v0 = tc * kTileV + 4 * rc;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) dma16(a.U + uoff_d[nb] + v0, base + u_lds + nb * 1024);
+    if constexpr (kResid) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) dma16(a.T + toff_d[nb] + v0, base + t_lds + nb * 1024);
     }
   };
-  auto lread = [&](int buf, FragT (&A)[NS]) {
-    const unsigned char* row = &lds[buf][j * kStride + 16 * q];
+  auto compute = [&](int t, const unsigned char* sl) {
+    FragT A[NS];
+    const unsigned char* row = sl + j * kRowBytes;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) A[s] = *reinterpret_cast<const FragT*>(row + 64 * s);
+    for (int s = 0; s < NS; ++s) A[s] = *reinterpret_cast<const FragT*>(row + (((4 * s + q) ^ j) * 16));
+    float4 uu[2], tt[2];
+    const int pos = j * 4 + (q ^ ((j >> 2) & 3));
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      uu[nb] = *reinterpret_cast<const float4*>(sl + kUOff + (wid * 2 + nb) * 1024 + pos * 16);
+      if constexpr (kResid)
+        tt[nb] = *reinterpret_cast<const float4*>(sl + kTOff + (wid * 2 + nb) * 1024 + pos * 16);
+      else
+        tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    w.compute(a, st, t, q, A, uu, tt);
   };
 
-  if (t0 < t1) {
-    // The prefetch of tile t+1 is clamped to the last tile; the final
-    // iteration stores it into the idle buffer, which nothing reads.
-    uint4 part[kParts];
-    float4 u0[2], u1[2], x0[2], x1[2];
-    gload(t0, part);
-    w.load_ut(a, t0, q, u0, x0);
-    lstore(0, part);
-    __syncthreads();
-    int buf = 0;
-    for (int t = t0; t < t1; ++t) {
-      const int tn = min(t + 1, t1 - 1);
-      gload(tn, part);
-      w.load_ut(a, tn, q, u1, x1);
-      if (wave_active) {
-        FragT A[NS];
-        lread(buf, A);
-        w.compute(a, st, t, q, A, u0, x0);
-      }
-      lstore(buf ^ 1, part);
-      __syncthreads();
-      buf ^= 1;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        u0[nb] = u1[nb];
-        x0[nb] = x1[nb];
-      }
+  for (int p = 0; p < D; ++p) issue(t0 + p, p);
+  // Drain once, visibly to the compiler: the row set-up loads (W1 rows,
+  // offsets) are then complete, and it places no waits for them inside the
+  // loop -- such a wait would also drain the ring there.
+  __builtin_amdgcn_s_waitcnt(0xF70);
+  for (int t = t0; t < t1; t += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (t + u >= t1) break;                            // uniform over the block
+      // this wave's loads of tile t+u have landed (the D-1 later tiles may
+      // still be in flight); after the barrier so have every other wave's,
+      // and no wave still reads the slot that the next load overwrites
+      ring_wait_barrier<(D - 1) * kG>();
+      issue(t + u + D, (u + D) % NB);
+      if (wave_active) compute(t + u, ring + u * kSlotBytes);
     }
   }
+  vm_drain();                                            // no load in flight at exit
   w.finish(a, st, q, vc);
 }
 
@@ -552,11 +617,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_resid_impl(const Comb
 
 namespace {
 
-template <int R>
+template <int R, int D>
 const void* shared_for(int mode) {
-  if (mode == kModeDraftGreedy) return (const void*)&sweep_shared_impl<R, kModeDraftGreedy>;
-  if (mode == kModeDraftSample) return (const void*)&sweep_shared_impl<R, kModeDraftSample>;
-  if (mode == kModeResidual) return (const void*)&sweep_shared_impl<R, kModeResidual>;
+  if (mode == kModeDraftGreedy) return (const void*)&sweep_shared_impl<R, kModeDraftGreedy, D>;
+  if (mode == kModeDraftSample) return (const void*)&sweep_shared_impl<R, kModeDraftSample, D>;
+  if (mode == kModeResidual) return (const void*)&sweep_shared_impl<R, kModeResidual, D>;
+  return nullptr;
+}
+
+template <int D>
+const void* shared_for_r(int r, int mode) {
+  if (r == 128) return shared_for<128, D>(mode);
+  if (r == 256) return shared_for<256, D>(mode);
   return nullptr;
 }
 
@@ -584,8 +656,9 @@ const void* private_for_r(int r, int mode) {
 const void* sweep_kernel(int wdtype, int r, int mode, int shared) {
   if (shared) {
     if (wdtype != 1) return nullptr;
-    if (r == 128) return shared_for<128>(mode);
-    if (r == 256) return shared_for<256>(mode);
+    if (shared == 1) return shared_for_r<1>(r, mode);
+    if (shared == 2) return shared_for_r<2>(r, mode);
+    if (shared == 3) return shared_for_r<3>(r, mode);
     return nullptr;
   }
   if (wdtype == 1) return private_for_r<uint16_t>(r, mode);
