@@ -11,8 +11,9 @@ B in R^{V x r}; its one-hot form is used as an independent pin in the tests.
 Readings (listed in DESIGN.md):
   * the draft law is softmax((U_k + B_k) / T); T = 0 means argmax of U_k + B_k;
   * the bias is applied at every position, B_1 from the anchor token x_0;
-  * stochastic sampling is Gumbel-max on y = z / T with the DRAFT stream;
-  * ties go to the lowest vocabulary index;
+  * a stochastic draw takes w_v = exp(y_v), y = z / T, through the two-level
+    exponential race of ``sampling.race_draw`` with the DRAFT stream;
+  * greedy ties go to the lowest vocabulary index;
   * in greedy mode the reported log-normaliser is that of z itself (T = 1).
 """
 from __future__ import annotations
@@ -23,7 +24,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from .rng import DRAFT, row_key, gumbels
+from .rng import DRAFT, row_key
+from .sampling import race_draw
 
 
 def decode_weights(w) -> np.ndarray:
@@ -68,7 +70,7 @@ class DraftResult:
     tokens: np.ndarray    # int64 [B, gamma]
     lse: np.ndarray       # float64 [B, gamma]: L_d = ln sum_v exp(y_v)
     ytok: np.ndarray      # float64 [B, gamma]: y at the drafted token
-    margin: np.ndarray    # float64 [B, gamma]: top-2 gap of the decision key
+    margin: np.ndarray    # float64 [B, gamma]: greedy top-2 gap, or the race draw's margin
     z: Optional[np.ndarray] = None   # float64 [B, gamma, V] when kept
 
 
@@ -100,15 +102,17 @@ def draft_markov(U, W1, W2, anchor, req_ids, temperature: float, seed: int, gamm
         z = Uk + markov_bias(W1d, W2d, prev)
         y = z / T if T > 0 else z
         if T > 0:
-            g = np.stack([gumbels(row_key(seed, int(req[b]), k, DRAFT), V) for b in range(B)])
-            key = y + g
+            for b in range(B):
+                x_b, m_b = race_draw(y[b], row_key(seed, int(req[b]), k, DRAFT))
+                tokens[b, k - 1] = x_b
+                margin[b, k - 1] = m_b
+            x = tokens[:, k - 1].copy()
         else:
-            key = z
-        x = np.argmax(key, axis=-1)            # first maximum = lowest index on ties
-        tokens[:, k - 1] = x
+            x = np.argmax(z, axis=-1)          # first maximum = lowest index on ties
+            tokens[:, k - 1] = x
+            margin[:, k - 1] = top2_margin(z, x)
         lse[:, k - 1] = logsumexp_rows(y)
         ytok[:, k - 1] = y[np.arange(B), x]
-        margin[:, k - 1] = top2_margin(key, x)
         if keep_logits:
             zs[:, k - 1, :] = z
         prev = x

@@ -10,10 +10,11 @@ rejected one is replaced by the target's own choice).
 The accept/residual formulas are stripped from the pages; this follows the
 standard lossless rule they describe (readings listed in the design doc):
   * accept x_k iff u < p_t(x_k) / p_d(x_k) with u the ACCEPT uniform of (req, k);
-  * at the first rejection sample from norm(max(0, p_t - p_d)) by Gumbel-max on
-    ln r_v with the RESID stream (empty residual: sample p_t with that stream);
-  * if all K_b drafts are accepted, sample the bonus from target row K_b + 1
+  * at the first rejection draw from norm(max(0, p_t - p_d)) with the RESID
+    stream (empty residual: draw from p_t with that stream);
+  * if all K_b drafts are accepted, draw the bonus from target row K_b + 1
     with the BONUS stream;
+  * every draw is the two-level exponential race of ``sampling.race_draw``;
   * greedy (T = 0): accept iff x_k equals the lowest-index argmax of the
     target row; the compensation / bonus token is that argmax;
   * p_t = softmax(target / T), p_d = softmax((U + bias) / T), same T.
@@ -26,7 +27,8 @@ import numpy as np
 import torch
 
 from .markov import decode_weights, markov_bias, logsumexp_rows, _ints
-from .rng import ACCEPT, RESID, BONUS, row_key, uniform_at, gumbels
+from .rng import ACCEPT, RESID, BONUS, row_key, uniform_at
+from .sampling import race_draw
 
 
 def _row(x, b, k) -> np.ndarray:
@@ -121,14 +123,12 @@ def verify(target, tokens, lse_d, ytok, U, W1, W2, anchor, K, req_ids,
             prev = int(anc[b]) if k == 1 else int(tok[b, k - 2])
             z = _row(U, b, k - 1) + markov_bias(W1d, W2d, np.array([prev]))[0]
             resid = residual_weights(lpt, z / T - lse_d[b, k - 1])
-            g = gumbels(row_key(seed, r_id, k, RESID), resid.shape[0])
+            rkey = row_key(seed, r_id, k, RESID)
             if np.any(resid > 0):
                 with np.errstate(divide="ignore"):
-                    key = np.where(resid > 0, np.log(resid) + g, -np.inf)
+                    xr, final_margin[b] = race_draw(np.log(resid), rkey)
             else:
-                key = t / T + g
-            xr = int(np.argmax(key))
-            final_margin[b] = _top2(key, xr)
+                xr, final_margin[b] = race_draw(t / T, rkey)
             out[b, A] = xr
             resid_row[b] = k
             done = True
@@ -140,9 +140,7 @@ def verify(target, tokens, lse_d, ytok, U, W1, W2, anchor, K, req_ids,
                 final_margin[b] = _top2(t, star)
                 lse_t[b, Kb] = logsumexp_rows(t[None])[0]
             else:
-                key = t / T + gumbels(row_key(seed, r_id, Kb + 1, BONUS), t.shape[0])
-                star = int(np.argmax(key))
-                final_margin[b] = _top2(key, star)
+                star, final_margin[b] = race_draw(t / T, row_key(seed, r_id, Kb + 1, BONUS))
                 lse_t[b, Kb] = logsumexp_rows((t / T)[None])[0]
             out[b, A] = star
         acc[b] = A

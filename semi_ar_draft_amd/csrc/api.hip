@@ -50,7 +50,9 @@ struct dspark_ctx {
   int32_t* dev_err = nullptr;
   bool use_graph = true;
   int sweep_waves_per_cu = 8;     // occupancy target of the vocabulary sweeps
-  int sweep_depth = 3;            // shared-tile sweeps: tiles prefetched ahead (1..3)
+  // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
+  int draft_nt = 2, draft_depth = 1;
+  int resid_nt = 1, resid_depth = 2;
   std::vector<DraftGraph> graphs;
   // kernel timing (benchmarks): event pairs around every launch while enabled
   bool timing = false;
@@ -117,7 +119,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Vocabulary-sweep plan: aim at eight waves per CU, at least four 16-wide
 // tiles per wave, and a grid that is a multiple of the XCD count.
 struct SweepPlan {
-  int n_rg, n_vc, n_tiles, grid, shared;
+  int n_rg, n_vc, n_tiles, grid;
+  bool shared;
 };
 
 // Batches of three or more 32-row groups share each W2 tile across the four
@@ -127,7 +130,7 @@ SweepPlan plan_sweep(const dspark_ctx* c, int B, int V, int r, int wdtype) {
   SweepPlan p;
   p.n_rg = (B + kRowsPerWave - 1) / kRowsPerWave;
   p.n_tiles = V / kTileV;
-  p.shared = (wdtype == DSPARK_BF16 && (r == 128 || r == 256) && p.n_rg >= 3) ? c->sweep_depth : 0;
+  p.shared = wdtype == DSPARK_BF16 && (r == 128 || r == 256) && p.n_rg >= 3;
   const int target_waves = c->sweep_waves_per_cu * c->cu_count;
   const int max_vc = p.n_tiles / 4 > 0 ? p.n_tiles / 4 : 1;
   long grid;
@@ -181,7 +184,7 @@ int check_markov_shape(dspark_ctx* c, int B, int gamma, int V, int r, int wdtype
   if (gamma < 1 || gamma > kMaxGamma) return fail(c, DSPARK_EINVAL, "gamma must be in 1..%d", kMaxGamma);
   if (V < kTileV || V % kTileV) return fail(c, DSPARK_EINVAL, "V must be a positive multiple of 16");
   if (wdtype != DSPARK_F32 && wdtype != DSPARK_BF16) return fail(c, DSPARK_EINVAL, "unknown weight dtype");
-  if (!sweep_kernel(wdtype, r, kModeDraftGreedy, 0))
+  if (!sweep_kernel(wdtype, r, kModeDraftGreedy, 0, 1))
     return fail(c, DSPARK_EINVAL, "r must be one of 32, 64, 128, 256 (got %d)", r);
   if (!(T >= 0.0f) || !std::isfinite(T)) return fail(c, DSPARK_EINVAL, "temperature must be finite and >= 0");
   return DSPARK_OK;
@@ -332,8 +335,17 @@ int dspark_create(dspark_ctx** out, int device) {
     const int v = atoi(w);
     if (v >= 1 && v <= 32) c->sweep_waves_per_cu = v;
   }
-  const char* dp = getenv("DSPARK_SWEEP_DEPTH");
-  if (dp && dp[0] >= '1' && dp[0] <= '3' && dp[1] == 0) c->sweep_depth = dp[0] - '0';
+  // tuning knobs of the shared-tile sweeps: "<nt>,<depth>" (nt 1 with depth
+  // 1..3, or nt 2 with depth 1..2)
+  auto ring_knob = [](const char* name, int& nt, int& depth) {
+    const char* v = getenv(name);
+    if (!v || v[0] < '1' || v[0] > '2' || v[1] != ',' || v[2] < '1' || v[2] > '3' || v[3] != 0) return;
+    if (v[0] == '2' && v[2] == '3') return;
+    nt = v[0] - '0';
+    depth = v[2] - '0';
+  };
+  ring_knob("DSPARK_DRAFT_RING", c->draft_nt, c->draft_depth);
+  ring_knob("DSPARK_RESID_RING", c->resid_nt, c->resid_depth);
   *out = c;
   return DSPARK_OK;
 }
@@ -471,7 +483,8 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
   ca.ytok = ytok;
   ca.err = c->dev_err;
 
-  const void* kfn = sweep_kernel((int)wdtype, r, mode, pl.shared);
+  const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, c->draft_depth, c->draft_nt)
+                              : sweep_kernel((int)wdtype, r, mode, 0, 1);
   std::vector<KernelNode> nodes(2 * gamma);
   for (int k = 1; k <= gamma; ++k) {
     sa.k = k;
@@ -695,7 +708,7 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   sa.pf = spf;
   sa.pi = spi;
   sa.err = c->dev_err;
-  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, sweep_kernel((int)wdtype, r, kModeResidual, pl.shared > 2 ? 2 : pl.shared), dim3(pl.grid), dim3(256), &sa, stream))) return rc;
+  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, sweep_kernel((int)wdtype, r, kModeResidual, pl.shared ? c->resid_depth : 0, pl.shared ? c->resid_nt : 1), dim3(pl.grid), dim3(256), &sa, stream))) return rc;
 
   CombineArgs ca;
   memset(&ca, 0, sizeof(ca));

@@ -59,11 +59,28 @@ __device__ __forceinline__ float hash_uniform(uint32_t h) {
   return __builtin_fmaf((float)(h >> 9), 0x1.0p-23f, 0x1.0p-24f);
 }
 
-// log2(-log2(u)).  Gumbel-max on natural logits y uses key y - ln(-ln u); in
-// base-2 units (y2 = y * log2 e) the key y2 - log2(-log2 u) is an increasing
-// affine function of it, so every arg-max is unchanged.
-__device__ __forceinline__ float gumbel_log2_term(float u) {
-  return __builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));
+// ---------------------------------------------------------------------------
+// Categorical draws by a two-level exponential race over aligned groups of
+// four vocabulary entries.  Group g = {4g .. 4g+3} with mass S_g draws
+// E_g = -log2(a), a the uniform of element 4g of the row; the largest
+// log2 S_g - log2 E_g wins (an increasing affine map of ln S_g - ln E_g, so
+// the winner is the exponential race's: P(g) = S_g / sum S).  Inside the
+// winner the uniform c of element 4g+1 picks the member by inverse CDF,
+// P(v | g) = w_v / S_g.  A group beats the running key K iff
+// E_g < S_g * 2^(m - K) when its mass is held as S_g * 2^-m, so most groups
+// cost one hash, one log and a compare.
+// ---------------------------------------------------------------------------
+// First member i with c < w0 + .. + wi (c = uniform * group mass); if
+// rounding leaves none, the last member of positive weight.
+__device__ __forceinline__ int group_pick(float c, float w0, float w1, float w2, float w3) {
+  float C = w0;
+  if (c < C) return 0;
+  C += w1;
+  if (c < C) return 1;
+  C += w2;
+  if (c < C) return 2;
+  if (w3 > 0.0f) return 3;
+  return w2 > 0.0f ? 2 : (w1 > 0.0f ? 1 : 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -119,11 +119,12 @@ struct SchedArgs {
 };
 
 // Kernel lookup (host stubs usable with hipLaunchKernel and graph nodes).
-// `wdtype`: 0 = fp32, 1 = bf16.  `shared` = D in 1..3: the workgroup-shared
-// W2-tile variant prefetching D tiles ahead by LDS DMA (bf16, r in {128,
-// 256}; grid = row-group quads x chunks); 0: the private-tile variant (grid =
-// waves / 4).  Returns nullptr if unsupported.
-const void* sweep_kernel(int wdtype, int r, int mode, int shared);
+// `wdtype`: 0 = fp32, 1 = bf16.  `depth` = D > 0: the workgroup-shared
+// W2-tile variant walking `nt` 16-wide tiles per step and loading D steps
+// ahead into LDS (bf16, r in {128, 256}; nt = 1 with D <= 3 or nt = 2 with
+// D <= 2; grid = row-group quads x chunks); 0: the private-tile variant
+// (grid = waves / 4).  Returns nullptr if unsupported.
+const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt);
 const void* combine_draft_kernel();
 const void* combine_resid_kernel();
 const void* verify_rows_kernel();

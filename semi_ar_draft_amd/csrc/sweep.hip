@@ -13,9 +13,9 @@
 // r/32 bf16 MFMAs per 16-row block, and folds z = U + bias into per-lane
 // running statistics:
 //   draft:    online log-sum-exp of y = z / T (base 2), arg-max of z
-//             (greedy) or of the Gumbel key (sampling);
-//   residual: arg-max of ln max(0, p_t - p_d) + Gumbel (and of the target's
-//             own Gumbel key as the empty-residual fallback).
+//             (greedy) or the group-race draw from exp(y) (sampling);
+//   residual: the group-race draw from max(0, p_t - p_d) (and from p_t as
+//             the empty-residual fallback).
 // With the 16x16x32 MFMA lane l holds rows D[4*(l/16) + i][l % 16]: four
 // consecutive vocabulary entries of one request, so U is read with one
 // 16-byte load per lane and the per-lane statistics need no cross-lane work
@@ -61,7 +61,7 @@ struct LaneState {
   float key;        // best key
   int idx;          // its vocabulary index
   float zb;         // z at the best key (sampling draft)
-  float fkey;       // residual: fallback key (target Gumbel)
+  float fkey;       // residual: fallback key (draw from p_t)
   int fidx;
 };
 
@@ -75,15 +75,14 @@ __device__ __forceinline__ void lane_init(LaneState& st) {
   st.fidx = 0x7fffffff;
 }
 
-// Fold four z values (vocabulary v0..v0+3 of one request; z = U + bias came
-// out of the MFMA, whose accumulator was initialised with U) into the state.
+// Fold four z values (vocabulary v0..v0+3 of one request, one race group;
+// z = U + bias came out of the MFMA, whose accumulator was initialised with
+// U) into the state.
 //
-// Sampling uses the exponential-race form of Gumbel-max: with E = -log2(u),
-// the base-2 key y2 - log2(E) beats the running best K iff
-// E < exp2(y2 - K) = exp2(y2 - m) * exp2(m - K).  exp2(y2 - m) is the
-// softmax term already at hand, so most elements cost one log and a compare;
-// the exact key (second log) is formed only for the rare candidates, which
-// are then compared exactly.
+// Sampling draws by the group race (common.hpp): the group's mass relative
+// to the running max is the softmax term already at hand, so a group costs
+// one hash, one log and a compare; the exact key and the member choice are
+// formed only for the rare groups that beat the running best.
 template <int MODE>
 __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const float4 t, int v0,
                                          uint32_t klo, uint32_t khi, float invT, float s2, float ld,
@@ -94,7 +93,8 @@ __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const f
     float e[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) e[i] = fast_exp2(__builtin_fmaf(z[i], s2, -mn));
-    st.s = st.s * fast_exp2(st.m - mn) + ((e[0] + e[1]) + (e[2] + e[3]));
+    const float S = (e[0] + e[1]) + (e[2] + e[3]);
+    st.s = st.s * fast_exp2(st.m - mn) + S;
     st.m = mn;
     if constexpr (MODE == kModeDraftGreedy) {
       if (zt > st.key) {
@@ -105,55 +105,50 @@ __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const f
         st.key = zt;
       }
     } else {
-      float E[4];
-      const float F = fast_exp2(mn - st.key);
-      bool cand = false;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        E[i] = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + i))));
-        cand |= E[i] < e[i] * F;
-      }
-      if (cand) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float key = __builtin_fmaf(z[i], s2, -fast_log2(E[i]));
-          if (key > st.key) {
-            st.key = key;
-            st.idx = v0 + i;
-            st.zb = z[i];
-          }
+      const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)v0)));
+      if (E < S * fast_exp2(mn - st.key)) {
+        const float key = fast_log2(S) + mn - fast_log2(E);
+        if (key > st.key) {
+          const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + 1))) * S;
+          const int i = group_pick(c, e[0], e[1], e[2], e[3]);
+          st.key = key;
+          st.idx = v0 + i;
+          st.zb = z[i];
         }
       }
     }
   } else {
-    // residual: r_v = p_t(v) - p_d(v); key log2(r) - log2(E) beats K iff
-    // r > E * 2^K; the target fallback key log2(p_t) - log2(E) likewise.
+    // residual: weights r_v = max(0, p_t - p_d) with mass R; the fallback
+    // (empty residual) draws from p_t with mass P, sharing the group's
+    // uniforms.  Keys log2 R - log2 E and log2 P - log2 E.
     const float tv[4] = {t.x, t.y, t.z, t.w};
-    const float FK = fast_exp2(st.key);
-    const float FF = fast_exp2(st.fkey);
-    float E[4], pt[4], r[4];
-    bool cand = false;
+    float pt[4], r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pt[i] = fast_exp2(__builtin_fmaf(tv[i], invT, -lt) * kLog2e);
       const float pd = fast_exp2(__builtin_fmaf(z[i], invT, -ld) * kLog2e);
-      r[i] = pt[i] - pd;
-      E[i] = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + i))));
-      cand |= (r[i] > 0.0f && r[i] > E[i] * FK) || (pt[i] > E[i] * FF);
+      r[i] = fmaxf(pt[i] - pd, 0.0f);
     }
-    if (cand) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float lE = fast_log2(E[i]);
-        const float key = (r[i] > 0.0f) ? fast_log2(r[i]) - lE : -INFINITY;
+    const float R = (r[0] + r[1]) + (r[2] + r[3]);
+    const float P = (pt[0] + pt[1]) + (pt[2] + pt[3]);
+    const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)v0)));
+    const bool cr = R > 0.0f && R > E * fast_exp2(st.key);
+    const bool cf = P > E * fast_exp2(st.fkey);
+    if (cr || cf) {
+      const float lE = fast_log2(E);
+      const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + 1)));
+      if (cr) {
+        const float key = fast_log2(R) - lE;
         if (key > st.key) {
           st.key = key;
-          st.idx = v0 + i;
+          st.idx = v0 + group_pick(c * R, r[0], r[1], r[2], r[3]);
         }
-        const float fkey = fast_log2(pt[i]) - lE;
+      }
+      if (cf) {
+        const float fkey = fast_log2(P) - lE;
         if (fkey > st.fkey) {
           st.fkey = fkey;
-          st.fidx = v0 + i;
+          st.fidx = v0 + group_pick(c * P, pt[0], pt[1], pt[2], pt[3]);
         }
       }
     }
@@ -209,47 +204,64 @@ struct WaveRows {
   float ld[2], lt[2];
   FragT H[2][NS];
 
-  __device__ __forceinline__ void setup(const SweepArgs& a, int rg, int j, int q) {
+  int kk[2];
+
+  // Row identities and stream offsets (the residual reads its position).
+  __device__ __forceinline__ void setup_rows(const SweepArgs& a, int rg, int j) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int b = rg * kRowsPerWave + nb * 16 + j;
       bool v = rg < a.n_rg && b < a.B;
-      int kk = a.k;
+      int k = a.k;
       if constexpr (MODE == kModeResidual) {
-        kk = v ? a.resid_k[b] : 0;
-        v = v && kk > 0 && kk <= a.gamma;
+        k = v ? a.resid_k[b] : 0;
+        v = v && k > 0 && k <= a.gamma;
       }
+      uoff[nb] = v ? (int64_t)b * a.usb + (int64_t)(k - 1) * a.usk : 0;
+      toff[nb] = (v && MODE == kModeResidual) ? (int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk : 0;
+      ok[nb] = v;
+      rows[nb] = b;
+      kk[nb] = k;
+    }
+  }
+
+  // Previous token, its gathered W1 row (MFMA B operand), stream keys and
+  // the residual's normalisers.
+  __device__ __forceinline__ void setup_rest(const SweepArgs& a, int q) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int b = rows[nb];
+      const int k = kk[nb];
       int prev = 0;
-      uoff[nb] = 0;
-      toff[nb] = 0;
       klo[nb] = khi[nb] = 0;
       ld[nb] = lt[nb] = 0.0f;
-      if (v) {
-        prev = (kk == 1) ? a.anchor[b] : a.tokens[(int64_t)b * a.gamma + kk - 2];
+      if (ok[nb]) {
+        prev = (k == 1) ? a.anchor[b] : a.tokens[(int64_t)b * a.gamma + k - 2];
         if ((unsigned)prev >= (unsigned)a.V) {
           atomicOr(a.err, kErrToken);
           prev = 0;
         }
-        uoff[nb] = (int64_t)b * a.usb + (int64_t)(kk - 1) * a.usk;
         if constexpr (MODE != kModeDraftGreedy) {
           const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
           const uint64_t key =
-              stream_key(a.seed, req, (uint32_t)kk, MODE == kModeResidual ? kResid : kDraft);
+              stream_key(a.seed, req, (uint32_t)k, MODE == kModeResidual ? kResid : kDraft);
           klo[nb] = (uint32_t)key;
           khi[nb] = (uint32_t)(key >> 32);
         }
         if constexpr (MODE == kModeResidual) {
-          toff[nb] = (int64_t)b * a.tsb + (int64_t)(kk - 1) * a.tsk;
-          ld[nb] = a.lse[(int64_t)b * a.gamma + kk - 1];
+          ld[nb] = a.lse[(int64_t)b * a.gamma + k - 1];
           lt[nb] = a.resid_lt[b];
         }
       }
-      ok[nb] = v;
-      rows[nb] = b;
       const WT* w1row = static_cast<const WT*>(a.W1) + (int64_t)prev * R;
 #pragma unroll
       for (int s = 0; s < NS; ++s) H[nb][s] = F::load(w1row, s, q);
     }
+  }
+
+  __device__ __forceinline__ void setup(const SweepArgs& a, int rg, int j, int q) {
+    setup_rows(a, rg, j);
+    setup_rest(a, q);
   }
 
   __device__ __forceinline__ void load_ut(const SweepArgs& a, int t, int q, float4 (&uu)[2],
@@ -360,14 +372,22 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
 // Direct global->LDS load of 16 bytes per lane (global_load_lds_dwordx4):
 // lane i's 16 bytes land at LDS byte address lds + 16 i; M0 carries the wave-
-// uniform base.  Written as inline assembly so that the compiler keeps no
-// books on it: its own wait-count tracking of such loads cannot tell the
-// slots of a ring apart and would wait for every load in flight before each
-// LDS read.  The kernels below order these loads explicitly with
-// ring_wait_barrier; the memory clobber keeps the compiler from moving memory
-// accesses across them.
+// uniform base and is restored afterwards.  Written as inline assembly so
+// that the compiler keeps no books on it: its own wait-count tracking of such
+// loads cannot tell the slots of a ring apart and would wait for every load
+// in flight before each LDS read.  The kernels below order these loads
+// explicitly with ring_wait_barrier; the memory clobber keeps the compiler
+// from moving memory accesses across them.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds)
+      : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight,
@@ -380,19 +400,21 @@ __device__ __forceinline__ void ring_wait_barrier() {
 __device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
 // Shared-tile variant (bf16): the four waves of a workgroup own four row
-// groups (128 requests) of one vocabulary chunk.  Every byte of a tile step
-// -- the 16 x r W2 tile (one contiguous block in HBM) and each wave's U (and,
-// for the residual, target) rows -- is moved by direct global->LDS loads
-// (global_load_lds_dwordx4: no register staging), D tiles ahead, into a ring
-// of D + 1 LDS slots.  Before step t each wave waits until its share of tile
-// t has landed (vmcnt counts the later groups still in flight), then a
-// barrier makes every wave's share visible.
+// groups (128 requests) of one vocabulary chunk, walked in steps of NT
+// 16-wide tiles.  Every byte of a step -- NT W2 tiles (one contiguous block
+// in HBM) and each wave's U (and, for the residual, target) rows -- is moved
+// by direct global->LDS loads (global_load_lds_dwordx4: no register
+// staging), D steps ahead, into a ring of D + 1 LDS slots.  Before a step
+// each wave waits until its own loads of that step have landed (vmcnt counts
+// the later steps still in flight), then a barrier makes every wave's share
+// visible.  With NT = 2 a row load moves 128 contiguous bytes of each of 8
+// rows: loads that touch 16 rows of 64 bytes each stream markedly slower.
 //
-// LDS layouts are XOR-swizzled instead of padded (a DMA writes 1 KB
-// contiguously per wave): W2 16-byte chunk c of tile row r is stored at chunk
-// c ^ (r & 15) of that row; U float4 c of row j at position c ^ ((j >> 2) & 3).
+// LDS layouts are XOR-swizzled instead of padded (a load writes 1 KB
+// contiguously per wave): 16-byte chunk c of W2 tile row r is stored at
+// chunk c ^ (r & 15); float4 c of U row j at c ^ ((j >> (2 / NT)) & (4 NT - 1)).
 // Both make the 16 lanes of a ds_read_b128 phase hit disjoint banks.
-template <int R, int MODE, int D>
+template <int R, int MODE, int D, int NT>
 __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   using WR = WaveRows<uint16_t, R, MODE>;
   using FragT = typename WR::FragT;
@@ -401,14 +423,20 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   constexpr int kRowBytes = R * 2;
   constexpr int kCPR = kRowBytes / 16;                  // 16-byte chunks per W2 row
   constexpr int kTileBytes = kTileV * kRowBytes;
-  constexpr int kW2Inst = kTileBytes / (kWavesPerBlock * 1024);   // 1 KB per wave instruction
+  constexpr int kW2Bytes = NT * kTileBytes;             // W2 per step
+  constexpr int kW2Inst = kW2Bytes / (kWavesPerBlock * 1024);   // 1 KB per wave instruction
   constexpr bool kResid = MODE == kModeResidual;
-  constexpr int kRowsInst = kResid ? 4 : 2;             // U (and T) rows: one per 16-row block
-  constexpr int kG = kW2Inst + kRowsInst;               // loads per wave per step
-  constexpr int kUOff = kTileBytes;                     // per wave: 2 x 1 KB of U
-  constexpr int kTOff = kTileBytes + kWavesPerBlock * 2048;
-  constexpr int kSlotBytes = kTileBytes + kWavesPerBlock * 2048 * (kResid ? 2 : 1);
-  static_assert(kW2Inst >= 1 && kTileBytes % (kWavesPerBlock * 1024) == 0, "tile must split into 1 KB loads");
+  constexpr int kFPR = 4 * NT;                          // float4 per U row per step
+  constexpr int kRPI = 16 / NT;                         // U rows per load instruction
+  constexpr int kSwzShift = 2 / NT;
+  constexpr int kUInst = kRowsPerWave / kRPI;           // per wave per step (= 2 NT)
+  constexpr int kWaveRowBytes = kRowsPerWave * kFPR * 16;
+  constexpr int kG = kW2Inst + kUInst * (kResid ? 2 : 1);   // loads per wave per step
+  constexpr int kUOff = kW2Bytes;
+  constexpr int kTOff = kW2Bytes + kWavesPerBlock * kWaveRowBytes;
+  constexpr int kSlotBytes = kW2Bytes + kWavesPerBlock * kWaveRowBytes * (kResid ? 2 : 1);
+  static_assert(NT == 1 || NT == 2, "steps of one or two tiles");
+  static_assert(kW2Inst >= 1 && kW2Bytes % (kWavesPerBlock * 1024) == 0, "W2 step must split into 1 KB loads");
   static_assert(D >= 1 && (D - 1) * kG < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) unsigned char ring[NB * kSlotBytes];
 
@@ -422,7 +450,7 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   const int vc = blk / n_rq;
   if (vc >= a.n_vc) return;                              // uniform over the block
   WR w;
-  w.setup(a, g * kWavesPerBlock + wid, j, q);
+  w.setup_rows(a, g * kWavesPerBlock + wid, j);
   const bool wave_active = __any(w.ok[0] || w.ok[1]);
   if constexpr (kResid) {
     if (!__syncthreads_or(wave_active)) return;          // uniform over the block
@@ -430,83 +458,99 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   LaneState st[2];
   lane_init(st[0]);
   lane_init(st[1]);
-  const int t0 = (int)((int64_t)a.n_tiles * vc / a.n_vc);
-  const int t1 = (int)((int64_t)a.n_tiles * (vc + 1) / a.n_vc);
+  // chunk boundaries on whole steps; only the last chunk may end mid-step
+  const int n_steps = (a.n_tiles + NT - 1) / NT;
+  const int t0 = min(NT * (int)((int64_t)n_steps * vc / a.n_vc), a.n_tiles);
+  const int t1 = min(NT * (int)((int64_t)n_steps * (vc + 1) / a.n_vc), a.n_tiles);
   if (t0 >= t1) {
+    w.setup_rest(a, q);
     w.finish(a, st, q, vc);
     return;
   }
 
-  // DMA lane roles.  W2: lane of instruction p fills LDS chunk P = wid*64*kW2Inst
-  // + p*64 + lane of the tile.  Rows: lane i loads float4 (i & 3) ^ swz of row
-  // (i >> 2) of a 16-row block; row offsets come from the MFMA lane holding
-  // that row.
-  const int rj = lane >> 2;
-  const int rc = (lane & 3) ^ ((rj >> 2) & 3);
-  int64_t uoff_d[2], toff_d[2];
+  // Load lane roles.  W2: lane of instruction p fills LDS chunk
+  // P = (wid kW2Inst + p) 64 + lane of the step.  Rows: lane i of row load m
+  // fills row m kRPI + i / kFPR, float4 slot i % kFPR, which holds logical
+  // float4 (i % kFPR) ^ swizzle(row); row offsets come from the MFMA lane
+  // holding that row.
+  int64_t uoff_d[kUInst], toff_d[kUInst];
+  int ucol_d[kUInst];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    uoff_d[nb] = __shfl(w.uoff[nb], rj, 64);
-    toff_d[nb] = kResid ? __shfl(w.toff[nb], rj, 64) : 0;
+  for (int m = 0; m < kUInst; ++m) {
+    const int row = m * kRPI + lane / kFPR;
+    ucol_d[m] = 4 * ((lane % kFPR) ^ ((row >> kSwzShift) & (kFPR - 1)));
+    uoff_d[m] = __shfl(w.uoff[row >> 4], row & 15, 64);
+    toff_d[m] = kResid ? __shfl(w.toff[row >> 4], row & 15, 64) : 0;
   }
   const unsigned char* W2b = static_cast<const unsigned char*>(a.W2);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8_t*)ring;
   const uint32_t w2_lds = __builtin_amdgcn_readfirstlane(wid * kW2Inst * 1024);
-  const uint32_t u_lds = __builtin_amdgcn_readfirstlane(kUOff + wid * 2048);
-  const uint32_t t_lds = __builtin_amdgcn_readfirstlane(kTOff + wid * 2048);
+  const uint32_t u_lds = __builtin_amdgcn_readfirstlane(kUOff + wid * kWaveRowBytes);
+  const uint32_t t_lds = __builtin_amdgcn_readfirstlane(kTOff + wid * kWaveRowBytes);
+  // step at tile t (t0 + a multiple of NT): tiles t .. t+NT-1; addresses
+  // past the chunk are clamped into it (in bounds; those values are unused)
   auto issue = [&](int t, int sidx) {
-    const int tc = min(t, t1 - 1);
-    const unsigned char* tile = W2b + (int64_t)tc * kTileBytes;
     const uint32_t base = ring_lds + sidx * kSlotBytes;
 #pragma unroll
     for (int p = 0; p < kW2Inst; ++p) {
       const int P = (wid * kW2Inst + p) * 64 + lane;
-      const int r = P / kCPR;
+      const int r = P / kCPR;                            // row of the step, 0 .. 16 NT - 1
       const int c = (P % kCPR) ^ (r & 15);
-      dma16(tile + r * kRowBytes + c * 16, base + w2_lds + p * 1024);
+      const int tc = min(t + r / kTileV, t1 - 1);
+      dma16(W2b + (int64_t)tc * kTileBytes + (r % kTileV) * kRowBytes + c * 16, base + w2_lds + p * 1024);
     }
-    const int v0 = tc * kTileV + 4 * rc;
+    int vcol[kUInst];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) dma16(a.U + uoff_d[nb] + v0, base + u_lds + nb * 1024);
+    for (int m = 0; m < kUInst; ++m) vcol[m] = min(t * kTileV + ucol_d[m], t1 * kTileV - 4);
+#pragma unroll
+    for (int m = 0; m < kUInst; ++m) dma16(a.U + uoff_d[m] + vcol[m], base + u_lds + m * 1024);
     if constexpr (kResid) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) dma16(a.T + toff_d[nb] + v0, base + t_lds + nb * 1024);
+      for (int m = 0; m < kUInst; ++m) dma16(a.T + toff_d[m] + vcol[m], base + t_lds + m * 1024);
     }
   };
   auto compute = [&](int t, const unsigned char* sl) {
-    FragT A[NS];
-    const unsigned char* row = sl + j * kRowBytes;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) A[s] = *reinterpret_cast<const FragT*>(row + (((4 * s + q) ^ j) * 16));
-    float4 uu[2], tt[2];
-    const int pos = j * 4 + (q ^ ((j >> 2) & 3));
+    for (int h = 0; h < NT; ++h) {
+      if (t + h >= t1) break;                            // uniform over the block
+      FragT A[NS];
+      const unsigned char* row = sl + (h * kTileV + j) * kRowBytes;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      uu[nb] = *reinterpret_cast<const float4*>(sl + kUOff + (wid * 2 + nb) * 1024 + pos * 16);
-      if constexpr (kResid)
-        tt[nb] = *reinterpret_cast<const float4*>(sl + kTOff + (wid * 2 + nb) * 1024 + pos * 16);
-      else
-        tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < NS; ++s) A[s] = *reinterpret_cast<const FragT*>(row + (((4 * s + q) ^ j) * 16));
+      float4 uu[2], tt[2];
+      const int col = (4 * h + q) ^ ((j >> kSwzShift) & (kFPR - 1));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int off = wid * kWaveRowBytes + ((nb * 16 + j) * kFPR + col) * 16;
+        uu[nb] = *reinterpret_cast<const float4*>(sl + kUOff + off);
+        if constexpr (kResid)
+          tt[nb] = *reinterpret_cast<const float4*>(sl + kTOff + off);
+        else
+          tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      w.compute(a, st, t + h, q, A, uu, tt);
     }
-    w.compute(a, st, t, q, A, uu, tt);
   };
 
+  // First loads go out before the W1 gathers so both latencies overlap.
 #pragma unroll
-  for (int p = 0; p < D; ++p) issue(t0 + p, p);
-  // Drain once, visibly to the compiler: the row set-up loads (W1 rows,
-  // offsets) are then complete, and it places no waits for them inside the
-  // loop -- such a wait would also drain the ring there.
+  for (int p = 0; p < D; ++p) issue(t0 + p * NT, p);
+  w.setup_rest(a, q);
+  // Drain once, visibly to the compiler: the set-up loads (W1 rows, tokens)
+  // are then complete, and it places no waits for them inside the loop --
+  // such a wait would also drain the ring there.
   __builtin_amdgcn_s_waitcnt(0xF70);
-  for (int t = t0; t < t1; t += NB) {
+  for (int t = t0; t < t1; t += NB * NT) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      if (t + u >= t1) break;                            // uniform over the block
-      // this wave's loads of tile t+u have landed (the D-1 later tiles may
+      const int ts = t + u * NT;
+      if (ts >= t1) break;                               // uniform over the block
+      // this wave's loads of step ts have landed (the D-1 later steps may
       // still be in flight); after the barrier so have every other wave's,
       // and no wave still reads the slot that the next load overwrites
       ring_wait_barrier<(D - 1) * kG>();
-      issue(t + u + D, (u + D) % NB);
-      if (wave_active) compute(t + u, ring + u * kSlotBytes);
+      issue(ts + D * NT, (u + D) % NB);
+      if (wave_active) compute(ts, ring + u * kSlotBytes);
     }
   }
   vm_drain();                                            // no load in flight at exit
@@ -613,22 +657,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_resid_impl(const Comb
   }
 }
 
-}  // namespace
-
-namespace {
-
-template <int R, int D>
+template <int R, int D, int NT>
 const void* shared_for(int mode) {
-  if (mode == kModeDraftGreedy) return (const void*)&sweep_shared_impl<R, kModeDraftGreedy, D>;
-  if (mode == kModeDraftSample) return (const void*)&sweep_shared_impl<R, kModeDraftSample, D>;
-  if (mode == kModeResidual) return (const void*)&sweep_shared_impl<R, kModeResidual, D>;
+  if (mode == kModeDraftGreedy) return (const void*)&sweep_shared_impl<R, kModeDraftGreedy, D, NT>;
+  if (mode == kModeDraftSample) return (const void*)&sweep_shared_impl<R, kModeDraftSample, D, NT>;
+  if (mode == kModeResidual) return (const void*)&sweep_shared_impl<R, kModeResidual, D, NT>;
   return nullptr;
 }
 
-template <int D>
+template <int D, int NT>
 const void* shared_for_r(int r, int mode) {
-  if (r == 128) return shared_for<128, D>(mode);
-  if (r == 256) return shared_for<256, D>(mode);
+  if (r == 128) return shared_for<128, D, NT>(mode);
+  if (r == 256) return shared_for<256, D, NT>(mode);
   return nullptr;
 }
 
@@ -653,12 +693,17 @@ const void* private_for_r(int r, int mode) {
 
 }  // namespace
 
-const void* sweep_kernel(int wdtype, int r, int mode, int shared) {
-  if (shared) {
+const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt) {
+  if (depth) {
     if (wdtype != 1) return nullptr;
-    if (shared == 1) return shared_for_r<1>(r, mode);
-    if (shared == 2) return shared_for_r<2>(r, mode);
-    if (shared == 3) return shared_for_r<3>(r, mode);
+    if (nt == 1) {
+      if (depth == 1) return shared_for_r<1, 1>(r, mode);
+      if (depth == 2) return shared_for_r<2, 1>(r, mode);
+      if (depth == 3) return shared_for_r<3, 1>(r, mode);
+    } else if (nt == 2) {
+      if (depth == 1) return shared_for_r<1, 2>(r, mode);
+      if (depth == 2) return shared_for_r<2, 2>(r, mode);
+    }
     return nullptr;
   }
   if (wdtype == 1) return private_for_r<uint16_t>(r, mode);

@@ -7,8 +7,8 @@
 // [blog] "形式化定义": the target scores every drafted position in one pass,
 // positions are checked in order, the first rejected one is replaced by a
 // target token and the rest dropped, so the output law is the target's.
-// Row statistics (log-sum-exp of t/T; greedy arg-max; the bonus row's Gumbel
-// key) need the whole vocabulary and are formed here; the accept tests need
+// Row statistics (log-sum-exp of t/T; greedy arg-max; the bonus row's
+// group-race draw from exp(t/T)) need the whole vocabulary and are formed here; the accept tests need
 // only t at the drafted token, read directly by the decision kernel.  The
 // residual draw at the first rejection reuses the MFMA sweep (sweep.hip).
 #include "common.hpp"
@@ -42,7 +42,9 @@ __device__ __forceinline__ void row_merge(RowState& a, const RowState& b) {
   }
 }
 
-template <int KEYMODE>  // 0: no key, 1: arg-max of t, 2: Gumbel key of t/T
+// KEYMODE 0: no key, 1: arg-max of t, 2: group-race draw from exp(t/T) (the
+// four values of a float4 form one aligned race group).
+template <int KEYMODE>
 __device__ __forceinline__ void row_fold(RowState& st, const float4 x, int v0, float s2, uint32_t klo,
                                          uint32_t khi) {
   const float xv[4] = {x.x, x.y, x.z, x.w};
@@ -51,24 +53,28 @@ __device__ __forceinline__ void row_fold(RowState& st, const float4 x, int v0, f
   for (int i = 0; i < 4; ++i) y2[i] = xv[i] * s2;
   const float mt = fmaxf(fmaxf(y2[0], y2[1]), fmaxf(y2[2], y2[3]));
   const float mn = fmaxf(st.m, mt);
-  float acc = st.s * fast_exp2(st.m - mn);
+  float e[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc += fast_exp2(y2[i] - mn);
-  st.s = acc;
+  for (int i = 0; i < 4; ++i) e[i] = fast_exp2(y2[i] - mn);
+  const float S = (e[0] + e[1]) + (e[2] + e[3]);
+  st.s = st.s * fast_exp2(st.m - mn) + S;
   st.m = mn;
-  if constexpr (KEYMODE != 0) {
+  if constexpr (KEYMODE == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float key;
-      if constexpr (KEYMODE == 1) {
-        key = xv[i];
-      } else {
-        const float u = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + i)));
-        key = y2[i] - gumbel_log2_term(u);
-      }
-      if (key > st.key) {
-        st.key = key;
+      if (xv[i] > st.key) {
+        st.key = xv[i];
         st.idx = v0 + i;
+      }
+    }
+  } else if constexpr (KEYMODE == 2) {
+    const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)v0)));
+    if (E < S * fast_exp2(mn - st.key)) {
+      const float key = fast_log2(S) + mn - fast_log2(E);
+      if (key > st.key) {
+        const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + 1))) * S;
+        st.key = key;
+        st.idx = v0 + group_pick(c, e[0], e[1], e[2], e[3]);
       }
     }
   }

@@ -92,8 +92,8 @@ def test_zero_weights_stochastic_ignores_previous_token():
     assert not np.array_equal(d1.lse, d2.lse)
 
 
-def test_gumbel_max_draws_follow_softmax():
-    """Textbook: argmax(y + Gumbel) ~ softmax(y).  One position, V = 8, chi-square."""
+def test_draws_follow_softmax():
+    """The draft token at one position ~ softmax(y).  V = 8, chi-square."""
     V = 8
     y = np.array([0.3, -1.0, 2.0, 0.0, 1.1, -0.4, 0.8, 1.5])
     U = torch.tensor(y, dtype=torch.float32)[None, None, :].repeat(1, 2, 1)
