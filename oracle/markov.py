@@ -8,7 +8,7 @@ column of the r x |V| matrix W2).  [teardown] "DSpark 的解法" writes the same
 as Logits_adjusted = Logits_parallel + B (A e_{t-1}) with A in R^{r x V},
 B in R^{V x r}; its one-hot form is used as an independent pin in the tests.
 
-Readings (listed in DESIGN.md):
+Readings:
   * the draft law is softmax((U_k + B_k) / T); T = 0 means argmax of U_k + B_k;
   * the bias is applied at every position, B_1 from the anchor token x_0;
   * a stochastic draw takes w_v = exp(y_v), y = z / T, through the two-level

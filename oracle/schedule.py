@@ -10,7 +10,7 @@ table profiled at start-up; the early stop is what keeps the rule lossless.
 [summary] section 5: the table is step-shaped with efficiency cliffs, so the
 early stop can end in a local optimum (expected behaviour, kept as is).
 
-Readings (listed in DESIGN.md):
+Readings:
   * tau = sum_b (1 + sum of admitted a_{b,j}) -- each request always yields one
     target token besides its accepted drafts; N = B + n tokens after admitting n
     candidates; Theta_n = (B + S_n) * SPS[N - 1], Theta_0 = B * SPS[B - 1];

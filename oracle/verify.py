@@ -8,7 +8,7 @@ lossless guarantee (accepted tokens are those the target would produce; a
 rejected one is replaced by the target's own choice).
 
 The accept/residual formulas are stripped from the pages; this follows the
-standard lossless rule they describe (readings listed in the design doc):
+standard lossless rule they describe (readings):
   * accept x_k iff u < p_t(x_k) / p_d(x_k) with u the ACCEPT uniform of (req, k);
   * at the first rejection draw from norm(max(0, p_t - p_d)) with the RESID
     stream (empty residual: draw from p_t with that stream);

@@ -8,8 +8,8 @@ produces.
 
 Workloads (the paper's pages, "DSpark" technical blog, sections on the Markov
 head and the prefix scheduler, plus the long-form summary's deployment
-section, describe the shapes; distributions are the builder's synthetic
-choices and are listed in the design doc):
+section, describe the shapes; the value distributions are synthetic choices
+of this package):
 
   tiny    B=4,   gamma=7, V=1024,   r=32,  fp32 weights ~N(0,0.1), U ~N(0,2),
           target = U + N(0,0.5), greedy.
