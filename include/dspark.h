@@ -95,7 +95,7 @@ enum {
   DSPARK_K_SURVIVAL = 3,
   DSPARK_K_SCHEDULE = 4,
   DSPARK_K_VERIFY_ROWS = 5,    /* streaming pass over target rows */
-  DSPARK_K_VERIFY_DECIDE = 6,
+  DSPARK_K_VERIFY_DECIDE = 6,  /* per-request merge of its rows + accept tests */
   DSPARK_K_RESID_SWEEP = 7,    /* MFMA residual sweep */
   DSPARK_K_RESID_COMBINE = 8,
   DSPARK_K_COUNT = 9
@@ -111,9 +111,13 @@ int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
  *     z_v    = U[b][k-1][v] + sum_i h_i * W2col_v[i]
  *     y_v    = z_v / T                     (T = temperature; y = z if T == 0)
  *     x_k    = argmin-index argmax_v z_v                     if T == 0
- *            = argmin-index argmax_v (y_v + G(seed, req_b, k, DRAFT, v))  else
- * where G is a standard Gumbel variate, so x_k ~ softmax(y) (Gumbel-max).
- * x_k feeds position k+1.  Outputs per (b, k):
+ *            = draw(exp(y), stream (seed, req_b, k, DRAFT))  else
+ * where draw(w, s) picks v with probability w_v / sum w by a two-level
+ * exponential race over the groups {4g .. 4g+3}: S_g = sum of w over the
+ * group, E_g = -ln u_s(4g), the group with the largest ln S_g - ln E_g wins
+ * (lowest g on ties), and inside it the first member i with
+ * u_s(4g+1) * S_g < w_4g + ... + w_{4g+i} is drawn (u_s(v): the uniform of
+ * element v of stream s).  x_k feeds position k+1.  Outputs per (b, k):
  *     tokens[b][k-1] = x_k
  *     lse[b][k-1]    = ln sum_v exp(y_v)      (of z when T == 0)
  *     ytok[b][k-1]   = y_{x_k}
@@ -188,12 +192,12 @@ int dspark_schedule(dspark_ctx* ctx, hipStream_t stream,
  *     T  > 0: p_t = softmax(target[b][k-1] / T), p_d from the draft
  *             (ln p_d(x_k) = ytok - lse); keep x_k iff
  *             u(seed, req_b, k, ACCEPT, 0) < p_t(x_k) / p_d(x_k);
- *             at the first rejection emit
- *             argmax_{v: r_v > 0} (ln r_v + G(seed, req_b, k, RESID, v)),
- *             r_v = max(0, p_t(v) - p_d(v)), recomputing the draft row from
- *             U, W1, W2 (if no r_v > 0, sample p_t with the same stream).
+ *             at the first rejection emit draw(r, stream (seed, req_b, k,
+ *             RESID)), r_v = max(0, p_t(v) - p_d(v)), recomputing the draft
+ *             row from U, W1, W2 (if every r_v is 0, draw(p_t) with the same
+ *             stream); draw() as for dspark_draft_markov.
  * If all K_b drafts are kept, emit the bonus token from target row K_b + 1
- * (its argmax, or a Gumbel-max sample with purpose BONUS at position K_b+1).
+ * (its argmax, or draw(exp(t / T)) with purpose BONUS at position K_b+1).
  * Outputs: accept_len[b] = number kept; out_tokens[b][0..accept_len] = the
  * kept drafts followed by the emitted token, then -1 up to gamma.
  * target: float [B][>= gamma+1][V] (same stride rules as U).  The other

@@ -52,7 +52,10 @@ struct dspark_ctx {
   int sweep_waves_per_cu = 8;     // occupancy target of the vocabulary sweeps
   // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
   int draft_nt = 2, draft_depth = 1;
-  int resid_nt = 1, resid_depth = 2;
+  int resid_nt = 1, resid_depth = 1;
+  // verify: last target row of each window but the final one (window k covers
+  // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list
+  int verify_win[8] = {3, 0, 0, 0, 0, 0, 0, 0};
   std::vector<DraftGraph> graphs;
   // kernel timing (benchmarks): event pairs around every launch while enabled
   bool timing = false;
@@ -152,15 +155,6 @@ SweepPlan plan_sweep(const dspark_ctx* c, int B, int V, int r, int wdtype) {
   grid = (grid + 7) / 8 * 8;
   p.grid = (int)grid;
   return p;
-}
-
-int plan_rows_chunks(int rows, int V) {
-  int n = (2048 + rows - 1) / rows;
-  const int by_len = (V / 4) / 1024;      // at least ~1024 float4 per chunk
-  if (n > by_len) n = by_len;
-  if (n > 64) n = 64;
-  if (n < 1) n = 1;
-  return n;
 }
 
 int check_stream_rows(dspark_ctx* c, const char* name, const float* p, int64_t sb, int64_t sk, int B, int rows,
@@ -346,6 +340,25 @@ int dspark_create(dspark_ctx** out, int device) {
   };
   ring_knob("DSPARK_DRAFT_RING", c->draft_nt, c->draft_depth);
   ring_knob("DSPARK_RESID_RING", c->resid_nt, c->resid_depth);
+  // verify windows: "e1,e2,..." increasing last rows of all windows but the final one
+  const char* vw = getenv("DSPARK_VERIFY_WINDOWS");
+  if (vw) {
+    int tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int n = 0, prev = 0;
+    bool ok = true;
+    for (const char* q = vw; *q && ok;) {
+      char* end = nullptr;
+      const long v = strtol(q, &end, 10);
+      if (end == q || v <= prev || v > 64 || n >= 7) ok = false;
+      else {
+        tmp[n++] = (int)v;
+        prev = (int)v;
+        q = (*end == ',') ? end + 1 : end;
+        if (*end && *end != ',') ok = false;
+      }
+    }
+    if (ok) memcpy(c->verify_win, tmp, sizeof(tmp));
+  }
   *out = c;
   return DSPARK_OK;
 }
@@ -577,17 +590,23 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
 
   const int rows = B * (gamma + 1);
-  // windows of target rows: rows 1-2 for every request, then the rest only
+  // windows of target rows: the first for every request, each later one only
   // for requests that kept every draft so far
-  const int n_win = gamma + 1 <= 2 ? 1 : 2;
-  const int win_lo[2] = {1, 3};
-  const int win_hi[2] = {gamma + 1 <= 2 ? gamma + 1 : 2, gamma + 1};
-  int win_chunks[2];
-  int n_chunks = 1;
-  for (int w = 0; w < n_win; ++w) {
-    win_chunks[w] = plan_rows_chunks(B * (win_hi[w] - win_lo[w] + 1), V);
-    if (win_chunks[w] > n_chunks) n_chunks = win_chunks[w];
+  int win_lo[9], win_hi[9];
+  int n_win = 0;
+  {
+    int lo = 1;
+    for (int i = 0; i < 8 && c->verify_win[i] > 0 && c->verify_win[i] < gamma + 1; ++i) {
+      win_lo[n_win] = lo;
+      win_hi[n_win] = c->verify_win[i];
+      lo = c->verify_win[i] + 1;
+      ++n_win;
+    }
+    win_lo[n_win] = lo;
+    win_hi[n_win] = gamma + 1;
+    ++n_win;
   }
+  const int n_chunks = ((V >> 2) + kRowsThreads * kRowsPer - 1) / (kRowsThreads * kRowsPer);
   const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
   const size_t n_rowpart = (size_t)rows * n_chunks;
   const size_t n_respart = (size_t)B * pl.n_vc;
@@ -619,62 +638,39 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   const float invT = greedy ? 1.0f : 1.0f / temperature;
   for (int w = 0; w < n_win; ++w) {
     const int nrows = win_hi[w] - win_lo[w] + 1;
-    RowsArgs ra;
-    memset(&ra, 0, sizeof(ra));
-    ra.B = B;
-    ra.gamma = gamma;
-    ra.V = V;
-    ra.n_chunks = win_chunks[w];
-    ra.pstride = n_chunks;
-    ra.greedy = greedy;
-    ra.lo = win_lo[w];
-    ra.hi = win_hi[w];
-    ra.vstate = w == 0 ? nullptr : vstate;
-    ra.T = target;
-    ra.tsb = t_stride_b;
-    ra.tsk = t_stride_k;
-    ra.K = K;
-    ra.req = req_ids;
-    ra.s2 = greedy ? kLog2e : kLog2e / temperature;
-    ra.seed = seed;
-    ra.pf = rpf;
-    ra.pi = rpi;
-    ra.err = c->dev_err;
-    if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), dim3(win_chunks[w], B * nrows), dim3(256), &ra,
+    VerifyArgs va;
+    memset(&va, 0, sizeof(va));
+    va.B = B;
+    va.gamma = gamma;
+    va.V = V;
+    va.n_chunks = n_chunks;
+    va.greedy = greedy;
+    va.lo = win_lo[w];
+    va.hi = win_hi[w];
+    va.first = w == 0;
+    va.vstate = vstate;
+    va.T = target;
+    va.tsb = t_stride_b;
+    va.tsk = t_stride_k;
+    va.K = K;
+    va.req = req_ids;
+    va.tokens = tokens;
+    va.lse = lse;
+    va.ytok = ytok;
+    va.invT = invT;
+    va.s2 = greedy ? kLog2e : kLog2e / temperature;
+    va.seed = seed;
+    va.pf = rpf;
+    va.pi = rpi;
+    va.accept_len = accept_len;
+    va.out_tokens = out_tokens;
+    va.resid_k = resid_k;
+    va.resid_lt = resid_lt;
+    va.err = c->dev_err;
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), dim3(n_chunks, B * nrows), dim3(kRowsThreads), &va,
                       stream)))
       return rc;
-
-    DecideArgs da;
-    memset(&da, 0, sizeof(da));
-    da.B = B;
-    da.gamma = gamma;
-    da.V = V;
-    da.n_chunks = win_chunks[w];
-    da.pstride = n_chunks;
-    da.greedy = greedy;
-    da.lo = win_lo[w];
-    da.hi = win_hi[w];
-    da.first = w == 0;
-    da.vstate = vstate;
-    da.T = target;
-    da.tsb = t_stride_b;
-    da.tsk = t_stride_k;
-    da.K = K;
-    da.req = req_ids;
-    da.tokens = tokens;
-    da.lse = lse;
-    da.ytok = ytok;
-    da.invT = invT;
-    da.seed = seed;
-    da.pf = rpf;
-    da.pi = rpi;
-    da.accept_len = accept_len;
-    da.out_tokens = out_tokens;
-    da.resid_k = resid_k;
-    da.resid_lt = resid_lt;
-    da.err = c->dev_err;
-    if ((rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &da, stream)))
-      return rc;
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &va, stream))) return rc;
   }
   if (greedy) return DSPARK_OK;
 

@@ -55,28 +55,15 @@ struct CombineArgs {
   int32_t* err;
 };
 
-struct RowsArgs {
-  int B, gamma, V, n_chunks, greedy;
-  int lo, hi;                    // 1-based rows of this window
-  int pstride;                   // partials per row in pf / pi
-  const int2* vstate;            // per request {accepted so far, next row (0 = done)}; null = all from row 1
-  const float* T;
-  int64_t tsb, tsk;
-  const int32_t* K;
-  const uint32_t* req;
-  float s2;
-  uint64_t seed;
-  float4* pf;                    // [B*(gamma+1)][n_chunks]: m2, s, key, -
-  int* pi;
-  int32_t* err;
-};
+// Verify row pass of one window (rows lo .. hi, 1-based).
+constexpr int kRowsThreads = 256;
+constexpr int kRowsPer = 8;      // float4 per thread per chunk: chunks of 2048 float4 (32 KB)
 
-struct DecideArgs {
+struct VerifyArgs {
   int B, gamma, V, n_chunks, greedy;
   int lo, hi;                    // 1-based rows of this window
-  int pstride;                   // partials per row in pf / pi
   int first;                     // first window: every request starts at row 1
-  int2* vstate;
+  int2* vstate;                  // per request {accepted so far, next row (0 = done)}
   const float* T;
   int64_t tsb, tsk;
   const int32_t* K;
@@ -84,10 +71,10 @@ struct DecideArgs {
   const int32_t* tokens;
   const float* lse;
   const float* ytok;
-  float invT;
+  float invT, s2;                // 1/T and log2(e)/T (greedy: 1 and log2 e)
   uint64_t seed;
-  const float4* pf;
-  const int* pi;
+  float4* pf;                    // [B*(gamma+1)][n_chunks]: m2, s, key, -
+  int* pi;
   int32_t* accept_len;
   int32_t* out_tokens;
   int32_t* resid_k;

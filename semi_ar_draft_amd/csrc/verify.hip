@@ -1,8 +1,8 @@
-// Verification: streaming passes over the target rows of every request, then
-// one wave per request that walks its positions in order.  Rows are taken in
-// windows (rows 1-2, then the rest): a row after a request's first rejection
-// is never needed, so the later window only reads rows of requests that have
-// accepted every position so far.
+// Verification: per window of rows, a streaming pass over the target rows
+// (one partial per 32 KB chunk), then one wave per request that merges its
+// rows and takes its accept decisions.  Rows are taken in windows: a row
+// after a request's first rejection is never needed, so a later window only
+// reads rows of requests that have accepted every position so far.
 //
 // [blog] "形式化定义": the target scores every drafted position in one pass,
 // positions are checked in order, the first rejected one is replaced by a
@@ -16,8 +16,6 @@
 
 namespace dspark {
 namespace {
-
-constexpr int kRowsThreads = 256;
 
 __device__ __forceinline__ int clamp_k(const int32_t* K, int b, int gamma, int32_t* err, bool report) {
   if (!K) return gamma;
@@ -39,6 +37,14 @@ __device__ __forceinline__ void row_merge(RowState& a, const RowState& b) {
   if (key_beats(b.key, b.idx, a.key, a.idx)) {
     a.key = b.key;
     a.idx = b.idx;
+  }
+}
+
+__device__ __forceinline__ void wave_row_reduce(RowState& st) {
+#pragma unroll
+  for (int mask = 1; mask < 64; mask <<= 1) {
+    RowState o{shfl_xor(st.m, mask), shfl_xor(st.s, mask), shfl_xor(st.key, mask), shfl_xor(st.idx, mask)};
+    row_merge(st, o);
   }
 }
 
@@ -80,55 +86,48 @@ __device__ __forceinline__ void row_fold(RowState& st, const float4 x, int v0, f
   }
 }
 
+// One chunk of kRowsPer float4 per thread: every load is issued before the
+// first is used; float4 indices at or past c1 are skipped.
 template <int KEYMODE>
-__device__ __forceinline__ void row_sweep(RowState& st, const float4* p, int c0, int c1, float s2,
-                                          uint32_t klo, uint32_t khi) {
-  int i = c0 + (int)threadIdx.x;
-  // four independent 16-byte loads in flight per thread
-  for (; i + 3 * kRowsThreads < c1; i += 4 * kRowsThreads) {
-    const float4 x0 = p[i];
-    const float4 x1 = p[i + kRowsThreads];
-    const float4 x2 = p[i + 2 * kRowsThreads];
-    const float4 x3 = p[i + 3 * kRowsThreads];
-    row_fold<KEYMODE>(st, x0, 4 * i, s2, klo, khi);
-    row_fold<KEYMODE>(st, x1, 4 * (i + kRowsThreads), s2, klo, khi);
-    row_fold<KEYMODE>(st, x2, 4 * (i + 2 * kRowsThreads), s2, klo, khi);
-    row_fold<KEYMODE>(st, x3, 4 * (i + 3 * kRowsThreads), s2, klo, khi);
+__device__ __forceinline__ void row_chunk(RowState& st, const float4* p, int c0, int c1, float s2, uint32_t klo,
+                                          uint32_t khi) {
+  float4 x[kRowsPer];
+#pragma unroll
+  for (int i = 0; i < kRowsPer; ++i) x[i] = p[min(c0 + (int)threadIdx.x + i * kRowsThreads, c1 - 1)];
+#pragma unroll
+  for (int i = 0; i < kRowsPer; ++i) {
+    const int c = c0 + (int)threadIdx.x + i * kRowsThreads;
+    if (c < c1) row_fold<KEYMODE>(st, x[i], 4 * c, s2, klo, khi);
   }
-  for (; i < c1; i += kRowsThreads) row_fold<KEYMODE>(st, p[i], 4 * i, s2, klo, khi);
 }
 
-__global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const RowsArgs a) {
+// One workgroup per (row chunk): the chunk's partial (max, sum, key, index).
+__global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArgs a) {
   const int nrows = a.hi - a.lo + 1;
   const int chunk = blockIdx.x;
   const int b = blockIdx.y / nrows;
   const int k = a.lo + blockIdx.y % nrows;
-  if (a.vstate && a.vstate[b].y == 0) return;   // request already decided
-  const int kb = clamp_k(a.K, b, a.gamma, a.err, chunk == 0 && k == 1 && threadIdx.x == 0);
+  if (!a.first && a.vstate[b].y == 0) return;   // request already decided
+  const int kb = clamp_k(a.K, b, a.gamma, a.err, a.first && chunk == 0 && k == 1 && threadIdx.x == 0);
   if (k > kb + 1) return;
-  const int row = b * (a.gamma + 1) + (k - 1);
+  const int64_t row = (int64_t)b * (a.gamma + 1) + (k - 1);
   const bool bonus = (k == kb + 1);
   const float4* p = reinterpret_cast<const float4*>(a.T + (int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk);
   const int nv4 = a.V >> 2;
-  const int c0 = (int)((int64_t)nv4 * chunk / a.n_chunks);
-  const int c1 = (int)((int64_t)nv4 * (chunk + 1) / a.n_chunks);
+  const int c0 = chunk * kRowsThreads * kRowsPer;
+  const int c1 = min(nv4, c0 + kRowsThreads * kRowsPer);
   RowState st{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
   if (a.greedy) {
-    row_sweep<1>(st, p, c0, c1, a.s2, 0, 0);
+    row_chunk<1>(st, p, c0, c1, a.s2, 0, 0);
   } else if (bonus) {
     const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
     const uint64_t key = stream_key(a.seed, req, (uint32_t)k, kBonus);
-    row_sweep<2>(st, p, c0, c1, a.s2, (uint32_t)key, (uint32_t)(key >> 32));
+    row_chunk<2>(st, p, c0, c1, a.s2, (uint32_t)key, (uint32_t)(key >> 32));
   } else {
-    row_sweep<0>(st, p, c0, c1, a.s2, 0, 0);
+    row_chunk<0>(st, p, c0, c1, a.s2, 0, 0);
   }
   // wave reduction, then across the four waves in a fixed order
-#pragma unroll
-  for (int mask = 1; mask < 64; mask <<= 1) {
-    RowState o{shfl_xor(st.m, mask), shfl_xor(st.s, mask), shfl_xor(st.key, mask),
-               shfl_xor(st.idx, mask)};
-    row_merge(st, o);
-  }
+  wave_row_reduce(st);
   __shared__ RowState red[kRowsThreads / 64];
   const int wid = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wid] = st;
@@ -137,110 +136,123 @@ __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const RowsArgs 
     RowState acc = red[0];
 #pragma unroll
     for (int w = 1; w < kRowsThreads / 64; ++w) row_merge(acc, red[w]);
-    const int64_t o = (int64_t)row * a.pstride + chunk;
+    const int64_t o = row * a.n_chunks + chunk;
     a.pf[o] = make_float4(acc.m, acc.s, acc.key, 0.f);
     a.pi[o] = acc.idx;
   }
 }
 
-constexpr int kMaxGamma = 32;
-
-// One wave per request: finish the statistics of the rows of this window,
-// then continue the request's accept decisions in order.  Writes the kept
+// One wave per request: merge the chunk partials of its rows lo .. last of
+// this window (8 lanes per row, 8 rows at a time), then test the rows in
+// parallel (lane i tests row lo + i: the tests of different rows are
+// independent, and the first rejection ends the request).  Writes the kept
 // drafts, the compensation / bonus token when it is known here, the residual
 // request otherwise; a request that kept every row of the window and has
 // rows left stays pending for the next window.
-__global__ __launch_bounds__(64) void verify_decide_impl(const DecideArgs a) {
+__global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  int A = 0;
-  int start = 1;
-  if (!a.first) {
-    const int2 vs = a.vstate[b];
-    if (vs.y == 0) return;
-    A = vs.x;
-    start = vs.y;
-  }
+  if (!a.first && a.vstate[b].y == 0) return;
   const int kb = clamp_k(a.K, b, a.gamma, a.err, false);
+  const int A0 = a.first ? 0 : a.vstate[b].x;
   const int last = min(a.hi, kb + 1);
-  __shared__ float s_lt[kMaxGamma + 1];
-  __shared__ int s_star[kMaxGamma + 1];
-  for (int k = start; k <= last; ++k) {
-    const int64_t base = ((int64_t)b * (a.gamma + 1) + (k - 1)) * a.pstride;
-    RowState st{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
-    for (int c = lane; c < a.n_chunks; c += 64) {
-      const float4 p = a.pf[base + c];
-      RowState o{p.x, p.y, p.z, a.pi[base + c]};
-      row_merge(st, o);
-    }
-#pragma unroll
-    for (int mask = 1; mask < 64; mask <<= 1) {
-      RowState o{shfl_xor(st.m, mask), shfl_xor(st.s, mask), shfl_xor(st.key, mask),
-                 shfl_xor(st.idx, mask)};
-      row_merge(st, o);
-    }
-    if (lane == 0) {
-      s_lt[k - 1] = (st.m + fast_log2(st.s)) * kLn2;   // ln sum exp(t / T)
-      s_star[k - 1] = st.idx;
-    }
-  }
-  __syncthreads();
-  if (lane != 0) return;
+  const int n_rows = last - a.lo + 1;                      // >= 1 for a pending request
+  const int n_test = max(0, min(last, kb) - a.lo + 1);     // rows with an accept test
+  const int64_t row0 = (int64_t)b * (a.gamma + 1) + (a.lo - 1);
   const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
-  int32_t* out = a.out_tokens + (int64_t)b * (a.gamma + 1);
-  int final_tok = -1;
-  int resid = 0;
-  bool rejected = false;
-  int k = start;
-  for (; k <= min(kb, a.hi); ++k) {
-    int x = a.tokens[(int64_t)b * a.gamma + k - 1];
+
+  // draft-side values of the tested row of this lane (independent of the merge)
+  const int k = a.lo + lane;
+  int x = 0;
+  float tx = 0.f, lpd = 0.f;
+  if (lane < n_test) {
+    x = a.tokens[(int64_t)b * a.gamma + k - 1];
     if ((unsigned)x >= (unsigned)a.V) {
       atomicOr(a.err, kErrToken);
       x = 0;
     }
-    if (a.greedy) {
-      if (x == s_star[k - 1]) {
-        out[A++] = x;
-        continue;
+    if (!a.greedy) {
+      tx = a.T[(int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk + x];
+      const int64_t o = (int64_t)b * a.gamma + k - 1;
+      lpd = a.ytok[o] - a.lse[o];
+    }
+  }
+  // row statistics: lanes 8r .. 8r+7 merge row r of each group of 8 rows
+  float my_lse = 0.f;   // of row lo + lane, for lane < n_rows
+  int my_star = 0;
+  for (int g0 = 0; g0 < n_rows; g0 += 8) {
+    const int r = g0 + (lane >> 3);
+    RowState st{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+    if (r < n_rows) {
+      const int64_t base = (row0 + r) * a.n_chunks;
+      for (int c = lane & 7; c < a.n_chunks; c += 8) {
+        const float4 q = a.pf[base + c];
+        row_merge(st, RowState{q.x, q.y, q.z, a.pi[base + c]});
       }
-      final_tok = s_star[k - 1];
-      rejected = true;
-      break;
     }
-    const float tx = a.T[(int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk + x];
-    const float lpt = tx * a.invT - s_lt[k - 1];
-    const int64_t o = (int64_t)b * a.gamma + k - 1;
-    const float lpd = a.ytok[o] - a.lse[o];
-    const float rho = fast_exp2((lpt - lpd) * kLog2e);
-    const uint64_t key = stream_key(a.seed, req, (uint32_t)k, kAccept);
-    const float u = hash_uniform(elem_hash((uint32_t)key, (uint32_t)(key >> 32), 0u));
-    if (u < rho) {
-      out[A++] = x;
-      continue;
+#pragma unroll
+    for (int mask = 1; mask < 8; mask <<= 1) {
+      RowState o{shfl_xor(st.m, mask), shfl_xor(st.s, mask), shfl_xor(st.key, mask), shfl_xor(st.idx, mask)};
+      row_merge(st, o);
     }
-    resid = k;
-    rejected = true;
-    break;
+    const float lse_r = (st.m + fast_log2(st.s)) * kLn2;   // ln sum exp(t / T)
+    // lane g0 + i takes the statistics of row g0 + i (held by lane 8 i)
+    const int src = ((lane - g0) & 7) * 8;
+    const float l2 = __shfl(lse_r, src, 64);
+    const int s2 = __shfl(st.idx, src, 64);
+    if (lane >= g0 && lane < g0 + 8) {
+      my_lse = l2;
+      my_star = s2;
+    }
   }
-  if (!rejected) {
-    if (kb + 1 > a.hi) {            // rows left: wait for the next window
-      a.vstate[b] = make_int2(A, k);
-      return;
+  bool rej = false;
+  if (lane < n_test) {
+    if (a.greedy) {
+      rej = x != my_star;
+    } else {
+      const float lpt = tx * a.invT - my_lse;
+      const float rho = fast_exp2((lpt - lpd) * kLog2e);
+      const uint64_t key = stream_key(a.seed, req, (uint32_t)k, kAccept);
+      const float u = hash_uniform(elem_hash((uint32_t)key, (uint32_t)(key >> 32), 0u));
+      rej = !(u < rho);
     }
-    final_tok = s_star[kb];         // all kept: bonus from row K_b + 1
   }
-  if (resid == 0) {
-    if ((unsigned)final_tok >= (unsigned)a.V) {
-      atomicOr(a.err, kErrToken);
-      final_tok = 0;
+  const uint64_t rmask = __ballot(rej);
+  const int f = rmask ? __builtin_ctzll(rmask) : -1;       // first rejecting lane
+  const int n_acc = f >= 0 ? f : n_test;
+  int32_t* out = a.out_tokens + (int64_t)b * (a.gamma + 1);
+  if (lane < n_acc) out[A0 + lane] = x;
+  const int A = A0 + n_acc;
+  int final_tok = -1;
+  int resid = 0;
+  float resid_lt = 0.f;
+  if (f >= 0) {
+    if (a.greedy)
+      final_tok = __shfl(my_star, f, 64);
+    else {
+      resid = a.lo + f;
+      resid_lt = __shfl(my_lse, f, 64);
     }
-    out[A] = final_tok;
+  } else if (kb + 1 <= a.hi) {
+    final_tok = __shfl(my_star, kb + 1 - a.lo, 64);        // every draft kept: bonus from row K_b + 1
+  } else {
+    if (lane == 0) a.vstate[b] = make_int2(A, a.hi + 1);    // rows left: wait for the next window
+    return;
   }
-  for (int i = A + 1; i <= a.gamma; ++i) out[i] = -1;
-  a.accept_len[b] = A;
-  a.resid_k[b] = resid;
-  a.resid_lt[b] = resid ? s_lt[resid - 1] : 0.f;
-  a.vstate[b] = make_int2(A, 0);
+  for (int i = A + 1 + lane; i <= a.gamma; i += 64) out[i] = -1;
+  if (lane == 0) {
+    if (resid == 0) {
+      if ((unsigned)final_tok >= (unsigned)a.V) {
+        atomicOr(a.err, kErrToken);
+        final_tok = 0;
+      }
+      out[A] = final_tok;
+    }
+    a.accept_len[b] = A;
+    a.resid_k[b] = resid;
+    a.resid_lt[b] = resid_lt;
+    a.vstate[b] = make_int2(A, 0);
+  }
 }
 
 }  // namespace
