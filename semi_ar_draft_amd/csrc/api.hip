@@ -56,6 +56,9 @@ struct dspark_ctx {
   // verify: last target row of each window but the final one (window k covers
   // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list
   int verify_win[8] = {3, 0, 0, 0, 0, 0, 0, 0};
+  // draft: running best (key, index) per (position, request), zero between calls
+  unsigned long long* best = nullptr;
+  size_t best_n = 0;
   std::vector<DraftGraph> graphs;
   // kernel timing (benchmarks): event pairs around every launch while enabled
   bool timing = false;
@@ -114,6 +117,23 @@ int ensure_ws(dspark_ctx* c, size_t bytes) {
     return fail(c, DSPARK_ENOMEM, "workspace allocation of %zu bytes failed", want);
   }
   c->ws_bytes = want;
+  return DSPARK_OK;
+}
+
+// The draft's running bests must be zero when a call starts; every call
+// clears the ones it used, so they are zeroed only when (re)allocated.
+int ensure_best(dspark_ctx* c, size_t n) {
+  if (n <= c->best_n) return DSPARK_OK;
+  DSPARK_HIP(c, hipDeviceSynchronize());
+  if (c->best) (void)hipFree(c->best);
+  c->best = nullptr;
+  c->best_n = 0;
+  if (hipMalloc(&c->best, n * sizeof(unsigned long long)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, DSPARK_ENOMEM, "allocation of %zu bytes failed", n * sizeof(unsigned long long));
+  }
+  DSPARK_HIP(c, hipMemset(c->best, 0, n * sizeof(unsigned long long)));
+  c->best_n = n;
   return DSPARK_OK;
 }
 
@@ -378,6 +398,7 @@ void dspark_destroy(dspark_ctx* c) {
     }
     for (auto e : c->ev_free) (void)hipEventDestroy(e);
     if (c->ws) (void)hipFree(c->ws);
+    if (c->best) (void)hipFree(c->best);
     if (c->dev_err) (void)hipFree(c->dev_err);
   }
   delete c;
@@ -452,9 +473,11 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
   const bool greedy = temperature == 0.0f;
   const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
   const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
-  const size_t npart = (size_t)B * pl.n_vc;
+  const size_t npos = (size_t)B * pl.n_vc;             // partials of one position
+  const size_t npart = npos * gamma;
   const size_t off_pi = align256(npart * sizeof(float4));
   if ((rc = ensure_ws(c, off_pi + align256(npart * sizeof(int2))))) return rc;
+  if ((rc = ensure_best(c, (size_t)B * gamma * kBestGroups))) return rc;
   float4* pf = reinterpret_cast<float4*>(c->ws);
   int2* pi = reinterpret_cast<int2*>(static_cast<char*>(c->ws) + off_pi);
 
@@ -491,6 +514,7 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
   ca.invT = sa.invT;
   ca.pf = pf;
   ca.pi = pi;
+  ca.best = c->best;
   ca.tokens = tokens;
   ca.lse = lse;
   ca.ytok = ytok;
@@ -498,13 +522,18 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
 
   const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, c->draft_depth, c->draft_nt)
                               : sweep_kernel((int)wdtype, r, mode, 0, 1);
-  std::vector<KernelNode> nodes(2 * gamma);
+  // gamma sweeps (each takes x_{k-1} from the previous position's running
+  // bests), then one merge of every position's partials
+  std::vector<KernelNode> nodes(gamma + 1);
   for (int k = 1; k <= gamma; ++k) {
     sa.k = k;
-    ca.k = k;
-    set_node(nodes[2 * (k - 1)], DSPARK_K_DRAFT_SWEEP, kfn, dim3(pl.grid), dim3(256), sa);
-    set_node(nodes[2 * (k - 1) + 1], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B), dim3(256), ca);
+    sa.pf = pf + (size_t)(k - 1) * npos;
+    sa.pi = pi + (size_t)(k - 1) * npos;
+    sa.best = c->best + (size_t)(k - 1) * kBestGroups * B;
+    sa.best_prev = k > 1 ? c->best + (size_t)(k - 2) * kBestGroups * B : nullptr;
+    set_node(nodes[k - 1], DSPARK_K_DRAFT_SWEEP, kfn, dim3(pl.grid), dim3(256), sa);
   }
+  set_node(nodes[gamma], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
   return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode, pl.grid, pl.n_vc);
 }
 

@@ -102,6 +102,19 @@ __device__ __forceinline__ void softmax_merge(float& m, float& s, float m2, floa
   s = a + b;
 }
 
+// (key, index) packed into 64 bits so that unsigned order is the winner
+// order: larger key first (the float's bits mapped to an order-preserving
+// integer; -0 folded into +0), then lower index.  0 is below every pair.
+__device__ __forceinline__ unsigned long long pack_best(float key, int idx) {
+  uint32_t u = __float_as_uint(key + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ int best_index(unsigned long long packed) {
+  return (int)(0xFFFFFFFFu - (uint32_t)packed);
+}
+
 // true if (k2, i2) beats (k1, i1): larger key, or equal key and lower index.
 __device__ __forceinline__ bool key_beats(float k2, int i2, float k1, int i1) {
   return (k2 > k1) || (k2 == k1 && i2 < i1);

@@ -14,6 +14,7 @@ namespace dspark {
 constexpr int kRowsPerWave = 32;
 constexpr int kTileV = 16;
 constexpr int kWavesPerBlock = 4;
+constexpr int kBestGroups = 16;
 
 enum SweepMode : int { kModeDraftGreedy = 0, kModeDraftSample = 1, kModeResidual = 2 };
 
@@ -37,14 +38,22 @@ struct SweepArgs {
   uint64_t seed;
   float4* pf;                    // partials [B][n_vc]
   int2* pi;
+  // draft modes: running best (key, index) of each request at this position,
+  // packed so that a larger integer is the winner (see pack_best), kept in
+  // kBestGroups slot groups [kBestGroups][B] (chunk vc updates group
+  // vc % kBestGroups, which spreads the atomics); and the same for the
+  // previous position (its token feeds this one), null at k = 1
+  unsigned long long* best;
+  const unsigned long long* best_prev;
   int32_t* err;
 };
 
 struct CombineArgs {
   int B, gamma, V, k, n_vc, greedy;
   float invT;
-  const float4* pf;
+  const float4* pf;              // draft: [gamma][B][n_vc] (every position at once)
   const int2* pi;
+  unsigned long long* best;      // draft: [gamma][kBestGroups][B] running bests, cleared here
   int32_t* tokens;               // draft: [B][gamma]
   float* lse;
   float* ytok;

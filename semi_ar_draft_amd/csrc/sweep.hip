@@ -226,8 +226,28 @@ struct WaveRows {
   }
 
   // Previous token, its gathered W1 row (MFMA B operand), stream keys and
-  // the residual's normalisers.
+  // the residual's normalisers.  In the draft the previous token is the
+  // maximum over the previous position's slot groups: the four lanes of a
+  // row (q = 0..3) read a quarter of the groups each and share the maximum.
   __device__ __forceinline__ void setup_rest(const SweepArgs& a, int q) {
+    unsigned long long pb[2] = {0ull, 0ull};
+    if (MODE != kModeResidual && a.best_prev) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if (ok[nb]) {
+#pragma unroll
+          for (int i = 0; i < kBestGroups / 4; ++i) {
+            const unsigned long long v = a.best_prev[(int64_t)(q * (kBestGroups / 4) + i) * a.B + rows[nb]];
+            pb[nb] = v > pb[nb] ? v : pb[nb];
+          }
+        }
+#pragma unroll
+        for (int m = 16; m <= 32; m <<= 1) {
+          const unsigned long long o = __shfl_xor(pb[nb], m, 64);
+          pb[nb] = o > pb[nb] ? o : pb[nb];
+        }
+      }
+    }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int b = rows[nb];
@@ -236,7 +256,12 @@ struct WaveRows {
       klo[nb] = khi[nb] = 0;
       ld[nb] = lt[nb] = 0.0f;
       if (ok[nb]) {
-        prev = (k == 1) ? a.anchor[b] : a.tokens[(int64_t)b * a.gamma + k - 2];
+        if (k == 1)
+          prev = a.anchor[b];
+        else if (MODE != kModeResidual && a.best_prev)
+          prev = best_index(pb[nb]);
+        else
+          prev = a.tokens[(int64_t)b * a.gamma + k - 2];
         if ((unsigned)prev >= (unsigned)a.V) {
           atomicOr(a.err, kErrToken);
           prev = 0;
@@ -308,6 +333,13 @@ struct WaveRows {
         } else {
           a.pf[o] = make_float4(st[nb].m, st[nb].s, st[nb].key, st[nb].zb);
           a.pi[o] = make_int2(st[nb].idx, 0);
+          // publish the chunk's winner into its slot group (no return value:
+          // the next position reads the groups after this kernel ends)
+          if (a.best) {
+            unsigned long long* slot = a.best + (int64_t)(vc % kBestGroups) * a.B + rows[nb];
+            __hip_atomic_fetch_max(slot, pack_best(st[nb].key, st[nb].idx), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
     }
@@ -578,13 +610,15 @@ __device__ __forceinline__ DraftPart part_shfl(const DraftPart& p, int mask) {
                    shfl_xor(p.idx, mask)};
 }
 
-// One 256-thread workgroup per request row: merge the per-chunk partials of
-// a draft position in a fixed order, write x_k, the log-normaliser and y at
-// x_k.
+// One 256-thread workgroup per (request, position), after the whole draft
+// loop: merge the per-chunk partials in a fixed order, write x_k, the
+// log-normaliser and y at x_k, and clear the position's running best (the
+// sweeps already took x_k from it; it must be zero for the next call).
 __global__ __launch_bounds__(kCombineThreads) void combine_draft_impl(const CombineArgs a) {
   const int b = blockIdx.x;
+  const int k = blockIdx.y + 1;
   DraftPart p{-INFINITY, 0.f, -INFINITY, 0.f, 0x7fffffff};
-  const int64_t base = (int64_t)b * a.n_vc;
+  const int64_t base = ((int64_t)(k - 1) * a.B + b) * a.n_vc;
   for (int i = threadIdx.x; i < a.n_vc; i += kCombineThreads) {
     const float4 f = a.pf[base + i];
     part_merge(p, DraftPart{f.x, f.y, f.z, f.w, a.pi[base + i].x});
@@ -602,10 +636,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_draft_impl(const Comb
       atomicOr(a.err, kErrToken);
       idx = 0;
     }
-    const int64_t o = (int64_t)b * a.gamma + a.k - 1;
+    const int64_t o = (int64_t)b * a.gamma + k - 1;
     a.tokens[o] = idx;
     a.lse[o] = (p.m + fast_log2(p.s)) * kLn2;
     a.ytok[o] = a.greedy ? p.key : p.zb * a.invT;
+  }
+  if (a.best && threadIdx.x < kBestGroups) {
+    unsigned long long* slot = a.best + ((int64_t)(k - 1) * kBestGroups + threadIdx.x) * a.B + b;
+    __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
