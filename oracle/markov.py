@@ -72,6 +72,7 @@ class DraftResult:
     ytok: np.ndarray      # float64 [B, gamma]: y at the drafted token
     margin: np.ndarray    # float64 [B, gamma]: greedy top-2 gap, or the race draw's margin
     z: Optional[np.ndarray] = None   # float64 [B, gamma, V] when kept
+    states: Optional[np.ndarray] = None   # GRU head: float64 [B, gamma, r], the state position k projected
 
 
 def draft_markov(U, W1, W2, anchor, req_ids, temperature: float, seed: int, gamma: int,

@@ -18,6 +18,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 from .markov import draft_markov, DraftResult
+from .rnn import draft_rnn
 from .confidence import confidence, ConfidenceResult
 from .schedule import schedule, ScheduleResult
 from .verify import verify, VerifyResult
@@ -44,8 +45,12 @@ def run_step(inp: dict, seed: int, rows: Optional[Sequence[int]] = None) -> Step
         return x if len(rows) == B else x[rows]
 
     T = inp["temperature"]
-    d = draft_markov(sel(inp["U"]), inp["W1"], inp["W2"], sel(inp["anchor"]),
-                     sel(inp["req_ids"]), T, seed, wl.gamma)
+    gru = inp.get("gru")
+    if gru is None:
+        d = draft_markov(sel(inp["U"]), inp["W1"], inp["W2"], sel(inp["anchor"]),
+                         sel(inp["req_ids"]), T, seed, wl.gamma)
+    else:
+        d = draft_rnn(sel(inp["U"]), inp["W1"], inp["W2"], gru, sel(inp["req_ids"]), T, seed, wl.gamma)
     c = None
     if inp.get("h") is not None:
         c = confidence(sel(inp["h"]), inp["E"], sel(inp["anchor"]), d.tokens, inp["wc"],
@@ -57,5 +62,5 @@ def run_step(inp: dict, seed: int, rows: Optional[Sequence[int]] = None) -> Step
         s = schedule(c.surv.astype(np.float32), inp["sps"])
         K = s.K
     v = verify(sel(inp["target"]), d.tokens, d.lse, d.ytok, sel(inp["U"]), inp["W1"], inp["W2"],
-               sel(inp["anchor"]), K, sel(inp["req_ids"]), T, seed, wl.gamma)
+               sel(inp["anchor"]), K, sel(inp["req_ids"]), T, seed, wl.gamma, states=d.states)
     return StepResult(rows, d, c, s, v)

@@ -71,9 +71,11 @@ class VerifyResult:
 
 
 def verify(target, tokens, lse_d, ytok, U, W1, W2, anchor, K, req_ids,
-           temperature: float, seed: int, gamma: int) -> VerifyResult:
+           temperature: float, seed: int, gamma: int, states=None) -> VerifyResult:
+    """``states`` (GRU head, [B][gamma][r]): the residual's draft row uses the
+    bias states[b, k-1] . W2 instead of the Markov bias W1[x_{k-1}] . W2."""
     tok = _ints(tokens)
-    anc = _ints(anchor)
+    anc = _ints(anchor) if anchor is not None else None
     req = _ints(req_ids) & 0xFFFFFFFF
     lse_d = np.asarray(lse_d, dtype=np.float64)
     ytok = np.asarray(ytok, dtype=np.float64)
@@ -118,10 +120,15 @@ def verify(target, tokens, lse_d, ytok, U, W1, W2, anchor, K, req_ids,
                 A += 1
                 continue
             # first rejection: residual draw from norm(max(0, p_t - p_d))
-            if W1d is None:
-                W1d, W2d = decode_weights(W1), decode_weights(W2)
-            prev = int(anc[b]) if k == 1 else int(tok[b, k - 2])
-            z = _row(U, b, k - 1) + markov_bias(W1d, W2d, np.array([prev]))[0]
+            if W2d is None:
+                W1d = decode_weights(W1) if states is None else None
+                W2d = decode_weights(W2)
+            if states is None:
+                prev = int(anc[b]) if k == 1 else int(tok[b, k - 2])
+                bias = markov_bias(W1d, W2d, np.array([prev]))[0]
+            else:
+                bias = W2d @ np.asarray(states[b, k - 1], dtype=np.float64)
+            z = _row(U, b, k - 1) + bias
             resid = residual_weights(lpt, z / T - lse_d[b, k - 1])
             rkey = row_key(seed, r_id, k, RESID)
             if np.any(resid > 0):

@@ -20,6 +20,11 @@ of this package):
           b_c = 1.
   sched   B=512, gamma=7, V=129280, r=256, temperature 1, STS temperatures
           ~U[1,2], SPS table of 4096 entries, scheduled K_b.
+  rnn     B=256, gamma=16, V=151936, r=256, the GRU head (state of width r,
+          GRU weights, biases and learned s_0 bf16 ~N(0,0.05)), temperature 1,
+          confidence with STS, scheduled K_b as for sched.
+  rnn_tiny B=8, gamma=6, V=2048, r=32, fp32 W1/W2 ~N(0,0.1), the GRU head,
+          temperature 1 (CPU-scale).
 
 Layouts (row-major, contiguous):
   U, target : float32 [B][gamma+1][V]   (row k-1 holds draft position k)
@@ -33,6 +38,8 @@ Layouts (row-major, contiguous):
   wc        : bf16 [d_h + d_e]
   sts_T     : float32 [gamma]
   sps       : float32 [n_sps]   (SPS[N-1] for a verify batch of N tokens)
+  GRU head  : W_ih, W_hh bf16 [3r][r] (gate rows in the order reset, update,
+              new), b_ih, b_hh bf16 [3r], s0 bf16 [r]
 """
 from __future__ import annotations
 
@@ -64,6 +71,8 @@ class Workload:
     sts: bool = False
     sched: bool = False
     n_sps: int = 4096
+    head: str = "markov"   # "markov" or "gru"
+    gru_std: float = 0.05
     seed: int = 1000
 
     def with_(self, **kw) -> "Workload":
@@ -81,6 +90,12 @@ WORKLOADS = {
     "sched": Workload("sched", B=512, gamma=7, V=129280, r=256, wdtype="bf16", u_std=3.0,
                       w_std=0.02, noise_std=1.0, peak=None, temperature=1.0, conf=True,
                       sts=True, sched=True, seed=1004),
+    "rnn": Workload("rnn", B=256, gamma=16, V=151936, r=256, wdtype="bf16", u_std=3.0,
+                    w_std=0.02, noise_std=1.0, peak=None, temperature=1.0, conf=True,
+                    sts=True, sched=True, head="gru", seed=1005),
+    "rnn_tiny": Workload("rnn_tiny", B=8, gamma=6, V=2048, r=32, wdtype="f32", u_std=2.0,
+                         w_std=0.1, noise_std=0.5, peak=None, temperature=1.0, head="gru",
+                         seed=1006),
 }
 
 # SPS table shape: a step every 64 tokens, slowly decreasing, with three cliffs.
@@ -111,7 +126,8 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, *, random_req_ids: boo
     """Draw every input of one step for workload ``wl`` (CPU tensors).
 
     Draw order is fixed: U, target noise, W1, W2, anchors, peaks, req_ids, h, E,
-    wc, STS temperatures.  The SPS table is deterministic.
+    wc, STS temperatures, then the GRU head's W_ih, W_hh, b_ih, b_hh, s0.  The
+    SPS table is deterministic.
     """
     g = torch.Generator().manual_seed(wl.seed if seed is None else seed)
     B, G, V, r = wl.B, wl.gamma, wl.V, wl.r
@@ -152,6 +168,15 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, *, random_req_ids: boo
             out["sts_T"] = None
     if wl.sched:
         out["sps"] = sps_table(wl.n_sps)
+    if wl.head == "gru":
+        out["gru"] = dict(
+            W_ih=_randn(g, (3 * r, r), wl.gru_std).to(torch.bfloat16),
+            W_hh=_randn(g, (3 * r, r), wl.gru_std).to(torch.bfloat16),
+            b_ih=_randn(g, (3 * r,), wl.gru_std).to(torch.bfloat16),
+            b_hh=_randn(g, (3 * r,), wl.gru_std).to(torch.bfloat16),
+            s0=_randn(g, (r,), wl.gru_std).to(torch.bfloat16))
+    elif wl.head != "markov":
+        raise ValueError(wl.head)
     return out
 
 
