@@ -30,7 +30,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="sample", choices=["tiny", "greedy", "sample", "sched"])
+    ap.add_argument("--workload", default="sample", choices=["tiny", "greedy", "sample", "sched", "rnn"])
     ap.add_argument("--seed", type=int, default=0x5EED)
     ap.add_argument("--cpu-sample", type=int, default=128,
                     help="requests of the same batch the CPU oracle runs for cpu_baseline")
@@ -88,10 +88,11 @@ def measured_traffic(wl_name, B, V, r, T):
     return float(prof["traffic_bytes_per_launch"])
 
 
-def sweep_bytes(B, V, r, wbytes):
-    """Algorithmic HBM bytes of one vocabulary sweep with the Markov bias:
-    U rows (4 B per logit), the whole W2, the gathered W1 rows."""
-    return 4 * B * V + wbytes * r * V + wbytes * B * r
+def sweep_bytes(B, V, r, wbytes, hbytes=None):
+    """Algorithmic HBM bytes of one vocabulary sweep with the head's bias:
+    U rows (4 B per logit), the whole W2, the rank-r vectors the bias is
+    projected from (gathered W1 rows, or the GRU head's fp32 states)."""
+    return 4 * B * V + wbytes * r * V + (wbytes if hbytes is None else hbytes) * B * r
 
 
 def main():
@@ -111,6 +112,9 @@ def main():
     t0 = time.time()
     inp = synth.make_inputs(wl)
     d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    gru = inp.get("gru")
+    if gru is not None:
+        d["gru"] = {k: v.cuda() for k, v in gru.items()}
     print(f"[bench] inputs {wl.name} B={wl.B} gamma={wl.gamma} V={wl.V} r={wl.r} "
           f"generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     B, G, V, r = wl.B, wl.gamma, wl.V, wl.r
@@ -127,6 +131,7 @@ def main():
     theta = torch.empty((1,), dtype=torch.float64, device=dev)
     acc = torch.empty((B,), dtype=torch.int32, device=dev)
     out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    states = torch.empty((G, B, r), dtype=torch.float32, device=dev) if gru is not None else None
     n_steps_max = max(args.steps, 1)
     K_log = torch.zeros((n_steps_max, B), dtype=torch.int32, device=dev)
     A_log = torch.zeros((n_steps_max, B), dtype=torch.int32, device=dev)
@@ -136,8 +141,12 @@ def main():
 
     def step(i, log=None):
         seed = args.seed ^ i
-        ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, seed, G,
-                         out=(tok, lse, ytok))
+        if gru is None:
+            ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, seed, G,
+                             out=(tok, lse, ytok))
+        else:
+            ctx.draft_rnn(d["U"], d["W1"], d["W2"], d["gru"], d["req_ids"], T, seed, G,
+                          out=(tok, lse, ytok, states))
         if has_conf:
             ctx.confidence(d["h"], d["E"], d["anchor"], tok, d["wc"], d["bc"], d.get("sts_T"),
                            out=(conf, surv))
@@ -147,7 +156,7 @@ def main():
             ctx.schedule(surv, d["sps"], out=(K, nsel, theta))
         # the timed steps write their accept lengths straight into the log rows
         ctx.verify(d["target"], d["U"], d["W1"], d["W2"], d["anchor"], tok, lse, ytok, K,
-                   d["req_ids"], T, seed, out=(acc if log is None else A_log[log], out))
+                   d["req_ids"], T, seed, out=(acc if log is None else A_log[log], out), states=states)
 
     for i in range(args.warmup):
         step(1000 + i)
@@ -205,7 +214,7 @@ def main():
         wbytes = 2 if d["W1"].dtype == torch.bfloat16 else 4
         # dominant kernel: the draft sweep (gamma launches per step)
         sw = per_kernel["draft_sweep"]
-        b_sweep = sweep_bytes(B, V, r, wbytes)
+        b_sweep = sweep_bytes(B, V, r, wbytes, 4 if gru is not None else None)
         sw["alg_bytes"] = b_sweep
         sw["alg_GBps"] = b_sweep / (sw["avg_us"] * 1e-6) / 1e9
         sw["mfma_TFLOPs"] = 2.0 * B * r * V / (sw["avg_us"] * 1e-6) / 1e12
@@ -231,7 +240,8 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": measured_traffic(wl.name, B, V, r, T),
-                    "kernel": "draft_sweep (MFMA Markov bias + vocabulary sweep, one position)",
+                    "kernel": ("draft_sweep (MFMA Markov bias + vocabulary sweep, one position)" if gru is None
+                               else "draft_sweep (MFMA GRU-state bias + vocabulary sweep, one position)"),
                     "alg_bytes_per_launch": b_sweep, "avg_launch_us": round(sw["avg_us"], 2),
                     "mfma_util": round(sw["mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 5)}
         print(f"[bench] kernels: " + ", ".join(f"{k} {v['avg_us']:.1f}us x{v['launches_per_step']:.0f}"
@@ -240,7 +250,7 @@ def main():
     # step-level algorithmic bytes (what one step must move at least)
     wbytes = 2 if d["W1"].dtype == torch.bfloat16 else 4
     n_rej_all = float((A < Ks).sum().item()) / args.steps
-    step_bytes = (G * sweep_bytes(B, V, r, wbytes)
+    step_bytes = (G * sweep_bytes(B, V, r, wbytes, 4 if gru is not None else None)
                   + (2.0 * B * G * (wl.d_h + wl.d_e) if has_conf else 0.0)
                   + 4.0 * V * needed_rows
                   + (8.0 * V * n_rej_all + wbytes * r * V if (T > 0 and n_rej_all > 0) else 0.0))
@@ -278,6 +288,7 @@ def main():
         "dtype": "f32 (bf16 weights, bf16 MFMA with f32 accumulation)",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={B} gamma={G} V={V} r={r} T={T}"
+                               + (" GRU head" if gru is not None else " Markov head")
                                + (f" confidence d_h={wl.d_h} d_e={wl.d_e}" if has_conf else "")
                                + (" scheduled" if sched else " K_b=gamma"),
                    "B": B, "gamma": G, "V": V, "r": r, "temperature": T,

@@ -98,7 +98,8 @@ enum {
   DSPARK_K_VERIFY_DECIDE = 6,  /* per-request merge of its rows + accept tests */
   DSPARK_K_RESID_SWEEP = 7,    /* MFMA residual sweep */
   DSPARK_K_RESID_COMBINE = 8,
-  DSPARK_K_COUNT = 9
+  DSPARK_K_GRU = 9,            /* GRU head: s_0 fill and state updates */
+  DSPARK_K_COUNT = 10
 };
 int dspark_timing_enable(dspark_ctx* ctx, int enable);
 int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
@@ -144,6 +145,34 @@ int dspark_draft_markov(dspark_ctx* ctx, hipStream_t stream,
                         const int32_t* anchor, const uint32_t* req_ids,
                         float temperature, uint64_t seed,
                         int32_t* tokens, float* lse, float* ytok);
+
+/* Semi-autoregressive draft with the RNN (GRU) head.
+ *
+ * [blog] "RNN Head：长程依赖"; [summary] section 3 (the state-vector head).
+ * As dspark_draft_markov, except that the bias of position k is projected
+ * from a recurrent state instead of the previous token's W1 row:
+ *     s_0    = s0                          (learned, the same for every request)
+ *     z_v    = U[b][k-1][v] + sum_i s_{k-1}[i] * W2col_v[i]
+ *     s_k    = GRU(s_{k-1}, W1[x_k])       (k < gamma)
+ * with the textbook GRU cell, gate rows in the order reset, update, new:
+ *     r  = sigmoid(W_ih[0:r] x + b_ih[0:r] + W_hh[0:r] s + b_hh[0:r])
+ *     z  = sigmoid(W_ih[r:2r] x + b_ih[r:2r] + W_hh[r:2r] s + b_hh[r:2r])
+ *     n  = tanh(W_ih[2r:3r] x + b_ih[2r:3r] + r * (W_hh[2r:3r] s + b_hh[2r:3r]))
+ *     s' = (1 - z) * n + z * s
+ * The state is carried in fp32 (it enters the bf16 MFMA projection as a
+ * hi + lo pair, so the bias is fp32-accurate).  The anchor token does not
+ * enter.  Inputs as for dspark_draft_markov, plus W_ih, W_hh: bf16 [3r][r]
+ * (16-byte aligned); b_ih, b_hh: bf16 [3r]; s0: bf16 [r].
+ * states: float [gamma][B][r], 16-byte aligned: states[k-1][b] is the state
+ * position k projected (s_0 .. s_{gamma-1}); pass it to dspark_verify. */
+int dspark_draft_rnn(dspark_ctx* ctx, hipStream_t stream,
+                     int B, int gamma, int V, int r, dspark_dtype wdtype,
+                     const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                     const void* W1, const void* W2,
+                     const void* W_ih, const void* W_hh, const void* b_ih,
+                     const void* b_hh, const void* s0,
+                     const uint32_t* req_ids, float temperature, uint64_t seed,
+                     int32_t* tokens, float* lse, float* ytok, float* states);
 
 /* Confidence head with sequential temperature scaling and survival products.
  *
@@ -194,15 +223,18 @@ int dspark_schedule(dspark_ctx* ctx, hipStream_t stream,
  *             u(seed, req_b, k, ACCEPT, 0) < p_t(x_k) / p_d(x_k);
  *             at the first rejection emit draw(r, stream (seed, req_b, k,
  *             RESID)), r_v = max(0, p_t(v) - p_d(v)), recomputing the draft
- *             row from U, W1, W2 (if every r_v is 0, draw(p_t) with the same
- *             stream); draw() as for dspark_draft_markov.
+ *             row from U, W2 and either W1 + anchor (Markov head) or states
+ *             (GRU head: the bias at position k is states[k-1][b] . W2); if
+ *             every r_v is 0, draw(p_t) with the same stream; draw() as for
+ *             dspark_draft_markov.
  * If all K_b drafts are kept, emit the bonus token from target row K_b + 1
  * (its argmax, or draw(exp(t / T)) with purpose BONUS at position K_b+1).
  * Outputs: accept_len[b] = number kept; out_tokens[b][0..accept_len] = the
  * kept drafts followed by the emitted token, then -1 up to gamma.
  * target: float [B][>= gamma+1][V] (same stride rules as U).  The other
- * arguments are those given to / returned by dspark_draft_markov; K: int32
- * [B] or NULL (values outside 0..gamma are clamped and flagged).
+ * arguments are those given to / returned by dspark_draft_markov, or by
+ * dspark_draft_rnn (states non-NULL; W1 and anchor may then be NULL); K:
+ * int32 [B] or NULL (values outside 0..gamma are clamped and flagged).
  * accept_len: int32 [B]; out_tokens: int32 [B][gamma+1]. */
 int dspark_verify(dspark_ctx* ctx, hipStream_t stream,
                   int B, int gamma, int V, int r, dspark_dtype wdtype,
@@ -210,7 +242,7 @@ int dspark_verify(dspark_ctx* ctx, hipStream_t stream,
                   const float* U, int64_t u_stride_b, int64_t u_stride_k,
                   const void* W1, const void* W2, const int32_t* anchor,
                   const int32_t* tokens, const float* lse, const float* ytok,
-                  const int32_t* K, const uint32_t* req_ids,
+                  const float* states, const int32_t* K, const uint32_t* req_ids,
                   float temperature, uint64_t seed,
                   int32_t* accept_len, int32_t* out_tokens);
 

@@ -22,11 +22,11 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 
 EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
-    "dspark_draft_markov", "dspark_confidence", "dspark_schedule", "dspark_verify",
+    "dspark_draft_markov", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_verify",
     "dspark_timing_enable", "dspark_timing_read",
 )
 KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
-                  "verify_rows", "verify_decide", "resid_sweep", "resid_combine")
+                  "verify_rows", "verify_decide", "resid_sweep", "resid_combine", "gru")
 
 _lib = None
 _vp, _i32, _i64, _u64, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
@@ -65,6 +65,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_draft_markov.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
         _vp, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp, _vp]
+    lib.dspark_draft_rnn.restype = _i32
+    lib.dspark_draft_rnn.argtypes = [
+        _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+        _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp, _vp, _vp]
     lib.dspark_confidence.restype = _i32
     lib.dspark_confidence.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp]
@@ -74,7 +78,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_verify.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
         _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
-        _vp, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp]
+        _vp, _vp, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp]
     if path is None:
         _lib = lib
     return lib
@@ -202,6 +206,43 @@ class Context:
             tokens.data_ptr(), lse.data_ptr(), ytok.data_ptr()))
         return tokens, lse, ytok
 
+    # -- dspark_draft_rnn ------------------------------------------------------
+    def draft_rnn(self, U, W1, W2, gru: dict, req_ids, temperature: float, seed: int, gamma: int,
+                  out=None, stream=None):
+        """GRU head; ``gru`` holds W_ih, W_hh [3r][r], b_ih, b_hh [3r], s0 [r] (bf16).
+        Returns tokens, lse, ytok and the fp32 states [gamma][B][r]."""
+        dev = self.device
+        sb, sk = _logits3(U, "U", dev)
+        B, rows, V = U.shape
+        if rows < gamma:
+            raise ValueError(f"U has {rows} positions, gamma is {gamma}")
+        _need(W1, "W1", None, dev, 2)
+        _need(W2, "W2", W1.dtype, dev, 2)
+        r = W1.shape[1]
+        if W1.shape != (V, r) or W2.shape != (V, r):
+            raise ValueError("W1 and W2 must both be [V][r]")
+        for nm, shape in (("W_ih", (3 * r, r)), ("W_hh", (3 * r, r)), ("b_ih", (3 * r,)),
+                          ("b_hh", (3 * r,)), ("s0", (r,))):
+            _need(gru[nm], nm, torch.bfloat16, dev, len(shape))
+            if tuple(gru[nm].shape) != shape:
+                raise ValueError(f"{nm} must be {list(shape)}")
+        if req_ids is not None:
+            _need(req_ids, "req_ids", torch.int32, dev, 1)
+            _len(req_ids, B, "req_ids")
+        if out is None:
+            out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+                   torch.empty((B, gamma), dtype=torch.float32, device=dev),
+                   torch.empty((B, gamma), dtype=torch.float32, device=dev),
+                   torch.empty((gamma, B, r), dtype=torch.float32, device=dev))
+        tokens, lse, ytok, states = out
+        self._rc(self.lib.dspark_draft_rnn(
+            self._h, _stream(dev, stream), B, gamma, V, r, _wdtype(W1),
+            U.data_ptr(), sb, sk, W1.data_ptr(), W2.data_ptr(), gru["W_ih"].data_ptr(),
+            gru["W_hh"].data_ptr(), gru["b_ih"].data_ptr(), gru["b_hh"].data_ptr(), gru["s0"].data_ptr(),
+            _ptr(req_ids), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+            tokens.data_ptr(), lse.data_ptr(), ytok.data_ptr(), states.data_ptr()))
+        return tokens, lse, ytok, states
+
     # -- dspark_confidence ----------------------------------------------------
     def confidence(self, h, E, anchor, tokens, wc, bc: float, sts_T=None, out=None, stream=None):
         dev = self.device
@@ -248,7 +289,9 @@ class Context:
 
     # -- dspark_verify ------------------------------------------------------------
     def verify(self, target, U, W1, W2, anchor, tokens, lse, ytok, K, req_ids,
-               temperature: float, seed: int, out=None, stream=None):
+               temperature: float, seed: int, out=None, stream=None, states=None):
+        """Markov head: W1 and anchor; GRU head: ``states`` from draft_rnn (W1 and
+        anchor may then be None)."""
         dev = self.device
         tsb, tsk = _logits3(target, "target", dev)
         usb, usk = _logits3(U, "U", dev)
@@ -257,15 +300,23 @@ class Context:
         gamma = tokens.shape[1]
         if trows < gamma + 1 or U.shape[0] != B or U.shape[1] < gamma or U.shape[2] != V:
             raise ValueError("target must be [B][>=gamma+1][V] and U [B][>=gamma][V]")
-        _need(W1, "W1", None, dev, 2)
-        _need(W2, "W2", W1.dtype, dev, 2)
-        r = W1.shape[1]
-        if W1.shape != (V, r) or W2.shape != (V, r):
-            raise ValueError("W1 and W2 must both be [V][r]")
-        _need(anchor, "anchor", torch.int32, dev, 1)
+        _need(W2, "W2", None, dev, 2)
+        r = W2.shape[1]
+        if W2.shape != (V, r):
+            raise ValueError("W2 must be [V][r]")
+        if states is None or W1 is not None:
+            _need(W1, "W1", W2.dtype, dev, 2)
+            if W1.shape != (V, r):
+                raise ValueError("W1 and W2 must both be [V][r]")
+        if states is None or anchor is not None:
+            _need(anchor, "anchor", torch.int32, dev, 1)
+            _len(anchor, B, "anchor")
+        if states is not None:
+            _need(states, "states", torch.float32, dev, 3)
+            if tuple(states.shape) != (gamma, B, r):
+                raise ValueError("states must be [gamma][B][r]")
         _need(lse, "lse", torch.float32, dev, 2)
         _need(ytok, "ytok", torch.float32, dev, 2)
-        _len(anchor, B, "anchor")
         for t, nm in ((tokens, "tokens"), (lse, "lse"), (ytok, "ytok")):
             if tuple(t.shape) != (B, gamma):
                 raise ValueError(f"{nm} must be [B][gamma]")
@@ -280,9 +331,9 @@ class Context:
                    torch.empty((B, gamma + 1), dtype=torch.int32, device=dev))
         acc, toks = out
         self._rc(self.lib.dspark_verify(
-            self._h, _stream(dev, stream), B, gamma, V, r, _wdtype(W1),
-            target.data_ptr(), tsb, tsk, U.data_ptr(), usb, usk, W1.data_ptr(), W2.data_ptr(),
-            anchor.data_ptr(), tokens.data_ptr(), lse.data_ptr(), ytok.data_ptr(), _ptr(K),
+            self._h, _stream(dev, stream), B, gamma, V, r, _wdtype(W2),
+            target.data_ptr(), tsb, tsk, U.data_ptr(), usb, usk, _ptr(W1), W2.data_ptr(),
+            _ptr(anchor), tokens.data_ptr(), lse.data_ptr(), ytok.data_ptr(), _ptr(states), _ptr(K),
             _ptr(req_ids), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
             acc.data_ptr(), toks.data_ptr()))
         return acc, toks

@@ -198,7 +198,7 @@ int check_markov_shape(dspark_ctx* c, int B, int gamma, int V, int r, int wdtype
   if (gamma < 1 || gamma > kMaxGamma) return fail(c, DSPARK_EINVAL, "gamma must be in 1..%d", kMaxGamma);
   if (V < kTileV || V % kTileV) return fail(c, DSPARK_EINVAL, "V must be a positive multiple of 16");
   if (wdtype != DSPARK_F32 && wdtype != DSPARK_BF16) return fail(c, DSPARK_EINVAL, "unknown weight dtype");
-  if (!sweep_kernel(wdtype, r, kModeDraftGreedy, 0, 1))
+  if (!sweep_kernel(wdtype, r, kModeDraftGreedy, 0, 1, 0))
     return fail(c, DSPARK_EINVAL, "r must be one of 32, 64, 128, 256 (got %d)", r);
   if (!(T >= 0.0f) || !std::isfinite(T)) return fail(c, DSPARK_EINVAL, "temperature must be finite and >= 0");
   return DSPARK_OK;
@@ -316,6 +316,117 @@ int run_chain(dspark_ctx* c, hipStream_t stream, std::vector<KernelNode>& nodes,
 }
 
 }  // namespace
+
+// The draft loop of either head: gamma sweeps (+ gamma - 1 GRU updates and
+// the s_0 fill for the GRU head), then one combine.  `gru` null = Markov.
+int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
+                const float* U, int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
+                const int32_t* anchor, const GruArgs* gru, const uint32_t* req_ids, float temperature,
+                uint64_t seed, int32_t* tokens, float* lse, float* ytok, float* states) {
+  int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
+  if (rc) return rc;
+  if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
+  if (!W1 || !W2 || !tokens || !lse || !ytok) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  if (!aligned16(W1) || !aligned16(W2)) return fail(c, DSPARK_EINVAL, "W1/W2 must be 16-byte aligned");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+
+  const bool greedy = temperature == 0.0f;
+  const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
+  const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
+  const size_t npos = (size_t)B * pl.n_vc;             // partials of one position
+  const size_t npart = npos * gamma;
+  const size_t off_pi = align256(npart * sizeof(float4));
+  if ((rc = ensure_ws(c, off_pi + align256(npart * sizeof(int2))))) return rc;
+  if ((rc = ensure_best(c, (size_t)B * gamma * kBestGroups))) return rc;
+  float4* pf = reinterpret_cast<float4*>(c->ws);
+  int2* pi = reinterpret_cast<int2*>(static_cast<char*>(c->ws) + off_pi);
+
+  SweepArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.B = B;
+  sa.gamma = gamma;
+  sa.V = V;
+  sa.n_rg = pl.n_rg;
+  sa.n_vc = pl.n_vc;
+  sa.n_tiles = pl.n_tiles;
+  sa.xcd_remap = 1;
+  sa.U = U;
+  sa.usb = u_stride_b;
+  sa.usk = u_stride_k;
+  sa.W1 = W1;
+  sa.W2 = W2;
+  sa.anchor = anchor;
+  sa.tokens = tokens;
+  sa.req = req_ids;
+  sa.invT = greedy ? 1.0f : 1.0f / temperature;
+  sa.s2 = greedy ? kLog2e : kLog2e / temperature;
+  sa.seed = seed;
+  sa.pf = pf;
+  sa.pi = pi;
+  sa.err = c->dev_err;
+  CombineArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.B = B;
+  ca.gamma = gamma;
+  ca.V = V;
+  ca.n_vc = pl.n_vc;
+  ca.greedy = greedy;
+  ca.invT = sa.invT;
+  ca.pf = pf;
+  ca.pi = pi;
+  ca.best = c->best;
+  ca.tokens = tokens;
+  ca.lse = lse;
+  ca.ytok = ytok;
+  ca.err = c->dev_err;
+
+  const int hs = gru ? 1 : 0;
+  const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, c->draft_depth, c->draft_nt, hs)
+                              : sweep_kernel((int)wdtype, r, mode, 0, 1, hs);
+  // Markov: gamma sweeps, each taking x_{k-1} from the previous position's
+  // running bests.  GRU: s_0 fill, then per position the sweep (bias from
+  // s_{k-1}) and, before the next one, s_k = GRU(s_{k-1}, W1[x_k]).  Then one
+  // merge of every position's partials.
+  std::vector<KernelNode> nodes;
+  nodes.reserve(2 * gamma + 1);
+  GruArgs ga;
+  if (gru) {
+    ga = *gru;
+    ga.B = B;
+    ga.R = r;
+    ga.V = V;
+    ga.W1 = W1;
+    ga.w1_bf16 = wdtype == DSPARK_BF16;
+    ga.states = states;
+    ga.err = c->dev_err;
+    ga.k = 0;
+    KernelNode n;
+    set_node(n, DSPARK_K_GRU, gru_init_kernel(), dim3((unsigned)(((int64_t)B * r + 255) / 256)), dim3(256), ga);
+    nodes.push_back(n);
+    sa.hstate = states;
+  }
+  for (int k = 1; k <= gamma; ++k) {
+    sa.k = k;
+    sa.pf = pf + (size_t)(k - 1) * npos;
+    sa.pi = pi + (size_t)(k - 1) * npos;
+    sa.best = c->best + (size_t)(k - 1) * kBestGroups * B;
+    sa.best_prev = (!gru && k > 1) ? c->best + (size_t)(k - 2) * kBestGroups * B : nullptr;
+    KernelNode n;
+    set_node(n, DSPARK_K_DRAFT_SWEEP, kfn, dim3(pl.grid), dim3(256), sa);
+    nodes.push_back(n);
+    if (gru && k < gamma) {
+      ga.k = k;
+      ga.best = sa.best;
+      set_node(n, DSPARK_K_GRU, gru_step_kernel(r), dim3(r / 16, (B + 15) / 16), dim3(64), ga);
+      nodes.push_back(n);
+    }
+  }
+  KernelNode n;
+  set_node(n, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
+  nodes.push_back(n);
+  return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 4 * hs, pl.grid, pl.n_vc);
+}
 
 extern "C" {
 
@@ -461,80 +572,30 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
                         const void* W1, const void* W2, const int32_t* anchor, const uint32_t* req_ids,
                         float temperature, uint64_t seed, int32_t* tokens, float* lse, float* ytok) {
   if (!c) return DSPARK_EINVAL;
-  int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
-  if (rc) return rc;
-  if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
-  if (!W1 || !W2 || !anchor || !tokens || !lse || !ytok)
+  if (!anchor) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  return draft_chain(c, stream, B, gamma, V, r, wdtype, U, u_stride_b, u_stride_k, W1, W2, anchor, nullptr,
+                     req_ids, temperature, seed, tokens, lse, ytok, nullptr);
+}
+
+int dspark_draft_rnn(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
+                     const float* U, int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
+                     const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh, const void* s0,
+                     const uint32_t* req_ids, float temperature, uint64_t seed, int32_t* tokens, float* lse,
+                     float* ytok, float* states) {
+  if (!c) return DSPARK_EINVAL;
+  if (!W_ih || !W_hh || !b_ih || !b_hh || !s0 || !states)
     return fail(c, DSPARK_EINVAL, "null pointer argument");
-  if (!aligned16(W1) || !aligned16(W2)) return fail(c, DSPARK_EINVAL, "W1/W2 must be 16-byte aligned");
-  DeviceGuard dg(c->device);
-  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
-
-  const bool greedy = temperature == 0.0f;
-  const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
-  const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
-  const size_t npos = (size_t)B * pl.n_vc;             // partials of one position
-  const size_t npart = npos * gamma;
-  const size_t off_pi = align256(npart * sizeof(float4));
-  if ((rc = ensure_ws(c, off_pi + align256(npart * sizeof(int2))))) return rc;
-  if ((rc = ensure_best(c, (size_t)B * gamma * kBestGroups))) return rc;
-  float4* pf = reinterpret_cast<float4*>(c->ws);
-  int2* pi = reinterpret_cast<int2*>(static_cast<char*>(c->ws) + off_pi);
-
-  SweepArgs sa;
-  memset(&sa, 0, sizeof(sa));
-  sa.B = B;
-  sa.gamma = gamma;
-  sa.V = V;
-  sa.n_rg = pl.n_rg;
-  sa.n_vc = pl.n_vc;
-  sa.n_tiles = pl.n_tiles;
-  sa.xcd_remap = 1;
-  sa.U = U;
-  sa.usb = u_stride_b;
-  sa.usk = u_stride_k;
-  sa.W1 = W1;
-  sa.W2 = W2;
-  sa.anchor = anchor;
-  sa.tokens = tokens;
-  sa.req = req_ids;
-  sa.invT = greedy ? 1.0f : 1.0f / temperature;
-  sa.s2 = greedy ? kLog2e : kLog2e / temperature;
-  sa.seed = seed;
-  sa.pf = pf;
-  sa.pi = pi;
-  sa.err = c->dev_err;
-  CombineArgs ca;
-  memset(&ca, 0, sizeof(ca));
-  ca.B = B;
-  ca.gamma = gamma;
-  ca.V = V;
-  ca.n_vc = pl.n_vc;
-  ca.greedy = greedy;
-  ca.invT = sa.invT;
-  ca.pf = pf;
-  ca.pi = pi;
-  ca.best = c->best;
-  ca.tokens = tokens;
-  ca.lse = lse;
-  ca.ytok = ytok;
-  ca.err = c->dev_err;
-
-  const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, c->draft_depth, c->draft_nt)
-                              : sweep_kernel((int)wdtype, r, mode, 0, 1);
-  // gamma sweeps (each takes x_{k-1} from the previous position's running
-  // bests), then one merge of every position's partials
-  std::vector<KernelNode> nodes(gamma + 1);
-  for (int k = 1; k <= gamma; ++k) {
-    sa.k = k;
-    sa.pf = pf + (size_t)(k - 1) * npos;
-    sa.pi = pi + (size_t)(k - 1) * npos;
-    sa.best = c->best + (size_t)(k - 1) * kBestGroups * B;
-    sa.best_prev = k > 1 ? c->best + (size_t)(k - 2) * kBestGroups * B : nullptr;
-    set_node(nodes[k - 1], DSPARK_K_DRAFT_SWEEP, kfn, dim3(pl.grid), dim3(256), sa);
-  }
-  set_node(nodes[gamma], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
-  return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode, pl.grid, pl.n_vc);
+  if (!aligned16(W_ih) || !aligned16(W_hh) || !aligned16(states))
+    return fail(c, DSPARK_EINVAL, "W_ih, W_hh and states must be 16-byte aligned");
+  GruArgs g;
+  memset(&g, 0, sizeof(g));
+  g.W_ih = static_cast<const uint16_t*>(W_ih);
+  g.W_hh = static_cast<const uint16_t*>(W_hh);
+  g.b_ih = static_cast<const uint16_t*>(b_ih);
+  g.b_hh = static_cast<const uint16_t*>(b_hh);
+  g.s0 = static_cast<const uint16_t*>(s0);
+  return draft_chain(c, stream, B, gamma, V, r, wdtype, U, u_stride_b, u_stride_k, W1, W2, nullptr, &g,
+                     req_ids, temperature, seed, tokens, lse, ytok, states);
 }
 
 int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int d_h, int d_e,
@@ -602,8 +663,8 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
                   const float* target, int64_t t_stride_b, int64_t t_stride_k, const float* U,
                   int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
                   const int32_t* anchor, const int32_t* tokens, const float* lse, const float* ytok,
-                  const int32_t* K, const uint32_t* req_ids, float temperature, uint64_t seed,
-                  int32_t* accept_len, int32_t* out_tokens) {
+                  const float* states, const int32_t* K, const uint32_t* req_ids, float temperature,
+                  uint64_t seed, int32_t* accept_len, int32_t* out_tokens) {
   if (!c) return DSPARK_EINVAL;
   int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
   if (rc) return rc;
@@ -611,10 +672,10 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   const bool greedy = temperature == 0.0f;
   if (!greedy && (rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
   if (!tokens || !accept_len || !out_tokens) return fail(c, DSPARK_EINVAL, "null pointer argument");
-  if (!greedy && (!W1 || !W2 || !anchor || !lse || !ytok))
-    return fail(c, DSPARK_EINVAL, "sampling verification needs U, W1, W2, anchor, lse and ytok");
-  if (!greedy && (!aligned16(W1) || !aligned16(W2)))
-    return fail(c, DSPARK_EINVAL, "W1/W2 must be 16-byte aligned");
+  if (!greedy && (!W2 || !lse || !ytok || (!states && (!W1 || !anchor))))
+    return fail(c, DSPARK_EINVAL, "sampling verification needs U, W2, lse, ytok and W1 + anchor or states");
+  if (!greedy && ((W1 && !aligned16(W1)) || !aligned16(W2) || (states && !aligned16(states))))
+    return fail(c, DSPARK_EINVAL, "W1, W2 and states must be 16-byte aligned");
   DeviceGuard dg(c->device);
   if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
 
@@ -732,8 +793,11 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   sa.seed = seed;
   sa.pf = spf;
   sa.pi = spi;
+  sa.hstate = states;
   sa.err = c->dev_err;
-  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, sweep_kernel((int)wdtype, r, kModeResidual, pl.shared ? c->resid_depth : 0, pl.shared ? c->resid_nt : 1), dim3(pl.grid), dim3(256), &sa, stream))) return rc;
+  const void* rfn = sweep_kernel((int)wdtype, r, kModeResidual, pl.shared ? c->resid_depth : 0,
+                                 pl.shared ? c->resid_nt : 1, states ? 1 : 0);
+  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, rfn, dim3(pl.grid), dim3(256), &sa, stream))) return rc;
 
   CombineArgs ca;
   memset(&ca, 0, sizeof(ca));

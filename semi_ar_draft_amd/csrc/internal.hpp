@@ -45,6 +45,9 @@ struct SweepArgs {
   // previous position (its token feeds this one), null at k = 1
   unsigned long long* best;
   const unsigned long long* best_prev;
+  // GRU head: fp32 states [gamma][B][r]; position k projects hstate[k-1][b]
+  // instead of W1[x_{k-1}] (kernels built with the state bias source)
+  const float* hstate;
   int32_t* err;
 };
 
@@ -114,18 +117,37 @@ struct SchedArgs {
   double* theta;
 };
 
+// GRU head recurrence (position k: states[k] = GRU(states[k-1], W1[x_k])).
+struct GruArgs {
+  int B, R, V, k;
+  const void* W1;                // [V][R], bf16 (w1_bf16) or fp32
+  int w1_bf16;
+  const uint16_t* W_ih;          // bf16 [3R][R], gate rows reset, update, new
+  const uint16_t* W_hh;          // bf16 [3R][R]
+  const uint16_t* b_ih;          // bf16 [3R]
+  const uint16_t* b_hh;          // bf16 [3R]
+  const uint16_t* s0;            // bf16 [R]
+  const unsigned long long* best;   // running bests of position k: [kBestGroups][B]
+  float* states;                 // fp32 [gamma][B][R]
+  int32_t* err;
+};
+
 // Kernel lookup (host stubs usable with hipLaunchKernel and graph nodes).
 // `wdtype`: 0 = fp32, 1 = bf16.  `depth` = D > 0: the workgroup-shared
 // W2-tile variant walking `nt` 16-wide tiles per step and loading D steps
 // ahead into LDS (bf16, r in {128, 256}; nt = 1 with D <= 3 or nt = 2 with
 // D <= 2; grid = row-group quads x chunks); 0: the private-tile variant
-// (grid = waves / 4).  Returns nullptr if unsupported.
-const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt);
+// (grid = waves / 4).  `hs` = 1: the bias is projected from the fp32 GRU
+// states in SweepArgs::hstate instead of W1 rows.  Returns nullptr if
+// unsupported.
+const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs);
 const void* combine_draft_kernel();
 const void* combine_resid_kernel();
 const void* verify_rows_kernel();
 const void* verify_decide_kernel();
 const void* confidence_kernel();
+const void* gru_init_kernel();
+const void* gru_step_kernel(int r);
 const void* survival_kernel();
 const void* schedule_kernel();
 

@@ -43,6 +43,20 @@ struct Frag<uint16_t, R> {
   static __device__ __forceinline__ f32x4_t mma(T a, T b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  // fp32 operand as hi + lo bf16 fragments (hi = RNE(x), lo = RNE(x - hi)):
+  // two MFMAs then carry x to about 2^-16 relative.
+  static constexpr bool kSplit = true;
+  static __device__ __forceinline__ void split(const float* row, int s, int q, T& hi, T& lo) {
+    const float4 a = *reinterpret_cast<const float4*>(row + 32 * s + 8 * q);
+    const float4 b = *reinterpret_cast<const float4*>(row + 32 * s + 8 * q + 4);
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = (__bf16)v[i];
+      hi[i] = h;
+      lo[i] = (__bf16)(v[i] - (float)h);
+    }
+  }
 };
 
 template <int R>
@@ -53,6 +67,11 @@ struct Frag<float, R> {
   static __device__ __forceinline__ T zero() { return 0.0f; }
   static __device__ __forceinline__ f32x4_t mma(T a, T b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  static constexpr bool kSplit = false;   // fp32 operands are taken whole
+  static __device__ __forceinline__ void split(const float* row, int s, int q, T& hi, T& lo) {
+    hi = row[4 * s + q];
+    lo = 0.0f;
   }
 };
 
@@ -192,17 +211,24 @@ __device__ __forceinline__ int xcd_logical_block(int p, int n) {
 // A row that is not active (past B, or no residual pending) reads request
 // 0's first row so that every load is unconditional; its statistics are
 // never written.
-template <typename WT, int R, int MODE>
+//
+// HS selects the MFMA B operand (the rank-r vector the bias is projected
+// from): 0 = the Markov head's W1 row of the previous token; 1 = the GRU
+// head's fp32 state s_{k-1} of the request (hstate [gamma][B][r]), split
+// into hi + lo bf16 fragments for bf16 weights.
+template <typename WT, int R, int MODE, int HS = 0>
 struct WaveRows {
   using F = Frag<WT, R>;
   using FragT = typename F::T;
   static constexpr int NS = F::NS;
+  static constexpr bool kLo = HS == 1 && F::kSplit;
   bool ok[2];
   int rows[2];
   int64_t uoff[2], toff[2];
   uint32_t klo[2], khi[2];
   float ld[2], lt[2];
   FragT H[2][NS];
+  FragT Hlo[2][kLo ? NS : 1];
 
   int kk[2];
 
@@ -231,7 +257,7 @@ struct WaveRows {
   // row (q = 0..3) read a quarter of the groups each and share the maximum.
   __device__ __forceinline__ void setup_rest(const SweepArgs& a, int q) {
     unsigned long long pb[2] = {0ull, 0ull};
-    if (MODE != kModeResidual && a.best_prev) {
+    if (HS == 0 && MODE != kModeResidual && a.best_prev) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if (ok[nb]) {
@@ -255,7 +281,7 @@ struct WaveRows {
       int prev = 0;
       klo[nb] = khi[nb] = 0;
       ld[nb] = lt[nb] = 0.0f;
-      if (ok[nb]) {
+      if (ok[nb] && HS == 0) {
         if (k == 1)
           prev = a.anchor[b];
         else if (MODE != kModeResidual && a.best_prev)
@@ -266,6 +292,8 @@ struct WaveRows {
           atomicOr(a.err, kErrToken);
           prev = 0;
         }
+      }
+      if (ok[nb]) {
         if constexpr (MODE != kModeDraftGreedy) {
           const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
           const uint64_t key =
@@ -278,9 +306,16 @@ struct WaveRows {
           lt[nb] = a.resid_lt[b];
         }
       }
-      const WT* w1row = static_cast<const WT*>(a.W1) + (int64_t)prev * R;
+      if constexpr (HS == 0) {
+        const WT* w1row = static_cast<const WT*>(a.W1) + (int64_t)prev * R;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) H[nb][s] = F::load(w1row, s, q);
+        for (int s = 0; s < NS; ++s) H[nb][s] = F::load(w1row, s, q);
+      } else {
+        // state of position k (inactive rows: request 0, position 1)
+        const float* srow = a.hstate + ((int64_t)(ok[nb] ? k - 1 : 0) * a.B + (ok[nb] ? b : 0)) * R;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) F::split(srow, s, q, H[nb][s], Hlo[nb][kLo ? s : 0]);
+      }
     }
   }
 
@@ -313,6 +348,13 @@ struct WaveRows {
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) acc[nb] = F::mma(A[s], H[nb][s], acc[nb]);
+    }
+    if constexpr (kLo) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[nb] = F::mma(A[s], Hlo[nb][s], acc[nb]);
+      }
     }
     const int vb = t * kTileV + 4 * q;
 #pragma unroll
@@ -349,9 +391,9 @@ struct WaveRows {
 // Private-tile variant: every wave owns its vocabulary chunk and loads its W2
 // tiles itself (used when no two waves share a chunk, e.g. B <= 64, and for
 // fp32 or narrow weights).  Double-buffered in registers.
-template <typename WT, int R, int MODE>
+template <typename WT, int R, int MODE, int HS>
 __global__ __launch_bounds__(256) void sweep_private_impl(const SweepArgs a) {
-  using WR = WaveRows<WT, R, MODE>;
+  using WR = WaveRows<WT, R, MODE, HS>;
   using F = typename WR::F;
   using FragT = typename WR::FragT;
   constexpr int NS = WR::NS;
@@ -446,9 +488,9 @@ __device__ __forceinline__ void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" :
 // contiguously per wave): 16-byte chunk c of W2 tile row r is stored at
 // chunk c ^ (r & 15); float4 c of U row j at c ^ ((j >> (2 / NT)) & (4 NT - 1)).
 // Both make the 16 lanes of a ds_read_b128 phase hit disjoint banks.
-template <int R, int MODE, int D, int NT>
+template <int R, int MODE, int D, int NT, int HS>
 __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
-  using WR = WaveRows<uint16_t, R, MODE>;
+  using WR = WaveRows<uint16_t, R, MODE, HS>;
   using FragT = typename WR::FragT;
   constexpr int NS = WR::NS;
   constexpr int NB = D + 1;                             // ring slots
@@ -695,57 +737,62 @@ __global__ __launch_bounds__(kCombineThreads) void combine_resid_impl(const Comb
   }
 }
 
-template <int R, int D, int NT>
+template <int R, int D, int NT, int HS>
 const void* shared_for(int mode) {
-  if (mode == kModeDraftGreedy) return (const void*)&sweep_shared_impl<R, kModeDraftGreedy, D, NT>;
-  if (mode == kModeDraftSample) return (const void*)&sweep_shared_impl<R, kModeDraftSample, D, NT>;
-  if (mode == kModeResidual) return (const void*)&sweep_shared_impl<R, kModeResidual, D, NT>;
+  if (mode == kModeDraftGreedy) return (const void*)&sweep_shared_impl<R, kModeDraftGreedy, D, NT, HS>;
+  if (mode == kModeDraftSample) return (const void*)&sweep_shared_impl<R, kModeDraftSample, D, NT, HS>;
+  if (mode == kModeResidual) return (const void*)&sweep_shared_impl<R, kModeResidual, D, NT, HS>;
   return nullptr;
 }
 
-template <int D, int NT>
+template <int D, int NT, int HS>
 const void* shared_for_r(int r, int mode) {
-  if (r == 128) return shared_for<128, D, NT>(mode);
-  if (r == 256) return shared_for<256, D, NT>(mode);
+  if (r == 128) return shared_for<128, D, NT, HS>(mode);
+  if (r == 256) return shared_for<256, D, NT, HS>(mode);
   return nullptr;
 }
 
-template <typename WT, int R>
+template <int HS>
+const void* shared_for_ring(int r, int mode, int depth, int nt) {
+  if (nt == 1) {
+    if (depth == 1) return shared_for_r<1, 1, HS>(r, mode);
+    if (depth == 2) return shared_for_r<2, 1, HS>(r, mode);
+    if (depth == 3) return shared_for_r<3, 1, HS>(r, mode);
+  } else if (nt == 2) {
+    if (depth == 1) return shared_for_r<1, 2, HS>(r, mode);
+    if (depth == 2) return shared_for_r<2, 2, HS>(r, mode);
+  }
+  return nullptr;
+}
+
+template <typename WT, int R, int HS>
 const void* private_for(int mode) {
-  if (mode == kModeDraftGreedy) return (const void*)&sweep_private_impl<WT, R, kModeDraftGreedy>;
-  if (mode == kModeDraftSample) return (const void*)&sweep_private_impl<WT, R, kModeDraftSample>;
-  if (mode == kModeResidual) return (const void*)&sweep_private_impl<WT, R, kModeResidual>;
+  if (mode == kModeDraftGreedy) return (const void*)&sweep_private_impl<WT, R, kModeDraftGreedy, HS>;
+  if (mode == kModeDraftSample) return (const void*)&sweep_private_impl<WT, R, kModeDraftSample, HS>;
+  if (mode == kModeResidual) return (const void*)&sweep_private_impl<WT, R, kModeResidual, HS>;
   return nullptr;
 }
 
-template <typename WT>
+template <typename WT, int HS>
 const void* private_for_r(int r, int mode) {
   switch (r) {
-    case 32: return private_for<WT, 32>(mode);
-    case 64: return private_for<WT, 64>(mode);
-    case 128: return private_for<WT, 128>(mode);
-    case 256: return private_for<WT, 256>(mode);
+    case 32: return private_for<WT, 32, HS>(mode);
+    case 64: return private_for<WT, 64, HS>(mode);
+    case 128: return private_for<WT, 128, HS>(mode);
+    case 256: return private_for<WT, 256, HS>(mode);
     default: return nullptr;
   }
 }
 
 }  // namespace
 
-const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt) {
+const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs) {
   if (depth) {
     if (wdtype != 1) return nullptr;
-    if (nt == 1) {
-      if (depth == 1) return shared_for_r<1, 1>(r, mode);
-      if (depth == 2) return shared_for_r<2, 1>(r, mode);
-      if (depth == 3) return shared_for_r<3, 1>(r, mode);
-    } else if (nt == 2) {
-      if (depth == 1) return shared_for_r<1, 2>(r, mode);
-      if (depth == 2) return shared_for_r<2, 2>(r, mode);
-    }
-    return nullptr;
+    return hs ? shared_for_ring<1>(r, mode, depth, nt) : shared_for_ring<0>(r, mode, depth, nt);
   }
-  if (wdtype == 1) return private_for_r<uint16_t>(r, mode);
-  if (wdtype == 0) return private_for_r<float>(r, mode);
+  if (wdtype == 1) return hs ? private_for_r<uint16_t, 1>(r, mode) : private_for_r<uint16_t, 0>(r, mode);
+  if (wdtype == 0) return hs ? private_for_r<float, 1>(r, mode) : private_for_r<float, 0>(r, mode);
   return nullptr;
 }
 

@@ -25,11 +25,14 @@ class Report:
     compared: int = 0
     ties: int = 0
     max_rel: float = 0.0
+    worst: str = ""
     problems: list = dataclasses.field(default_factory=list)
 
     def close(self, what, got, want):
         err = abs(float(got) - float(want)) / max(abs(float(want)), FLOOR)
-        self.max_rel = max(self.max_rel, err)
+        if err > self.max_rel:
+            self.max_rel = err
+            self.worst = f"{what} got {float(got)!r} want {float(want)!r}"
         if not err <= RTOL:
             self.problems.append(f"{what}: got {got!r} want {want!r} (rel {err:.2e})")
 
@@ -42,7 +45,7 @@ class Report:
         return not self.problems
 
     def summary(self):
-        head = f"compared={self.compared} ties={self.ties} max_rel={self.max_rel:.2e}"
+        head = f"compared={self.compared} ties={self.ties} max_rel={self.max_rel:.2e} ({self.worst})"
         return head + ("" if self.ok() else "\n  " + "\n  ".join(self.problems[:20]))
 
 
@@ -68,6 +71,24 @@ def compare_draft(tok, lse, ytok, od, rows=None, rep=None):
                 break
             rep.close(f"ytok[{g},{k}]", ytok[g, k - 1], od.ytok[i, k - 1])
     return rep, taint
+
+
+def compare_states(states, od, taint, rows=None, rep=None):
+    """GRU head: the state position k projected ([gamma][B][r] on the GPU,
+    [B][gamma][r] in the oracle) is comparable while x_1 .. x_{k-1} agree."""
+    rep = rep or Report()
+    B, G, _ = od.states.shape
+    rows = np.arange(B) if rows is None else np.asarray(rows)
+    for i in range(B):
+        g = rows[i]
+        for k in range(1, min(G, int(taint[i])) + 1):
+            got = np.asarray(states[k - 1, g], dtype=np.float64)
+            want = od.states[i, k - 1]
+            err = np.abs(got - want) / np.maximum(np.abs(want), FLOOR)
+            j = int(np.argmax(err))
+            rep.close(f"state[{k},{g},{j}]", got[j], want[j])
+            rep.compared += 1
+    return rep
 
 
 def compare_confidence(conf, surv, oc, taint, rows=None, rep=None):
