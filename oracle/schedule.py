@@ -66,3 +66,59 @@ def schedule(surv, sps) -> ScheduleResult:
         K[b] += 1
         n_sel = n
     return ScheduleResult(K, n_sel, float(theta_prev), float(min_rel), float(cut_gap))
+
+
+def schedule_async(surv, surv_hist, sps) -> ScheduleResult:
+    """Asynchronous variant: capacity from history, order from the current step.
+
+    [blog] "硬件感知前缀调度器" (the asynchronous mechanism: the verify
+    length is estimated from confidences of earlier steps so the decision
+    does not block the pipeline) and [summary] section 5 (the production
+    rule: the truncation count comes from confidences two steps old, the
+    candidates are still ranked by the latest confidences, and with the
+    count fixed from history the early-stop break is dropped in favour of an
+    unconstrained global search over the jagged throughput table).
+
+    Readings:
+      * surv_hist has the shape of surv (the same request slots two steps
+        earlier); Theta_n = (B + S_n^hist) * SPS[B + n - 1] with S_n^hist the
+        sum of the n largest historical survivals; the count n* is the first
+        n attaining the maximum over 0 <= n <= min(B * gamma, n_sps - B);
+      * the admitted set is the top n* candidates of the current survivals,
+        ranked (a descending, request ascending, position ascending) as in
+        the synchronous rule, so each request's set is a prefix;
+      * theta is Theta_{n*} (the historical objective); min_rel_step is the
+        relative gap between the maximum and the best other n (how clear the
+        argmax is); cut_gap is the current survival of the last admitted
+        candidate minus that of the first refused one.
+    """
+    a = decode_weights(surv)
+    h = decode_weights(surv_hist)
+    s = decode_weights(sps).reshape(-1)
+    B, gamma = a.shape
+    n_sps = s.shape[0]
+    if h.shape != a.shape:
+        raise ValueError("surv_hist must have the shape of surv")
+    if B < 1 or B > n_sps:
+        raise ValueError("need 1 <= B <= n_sps")
+    old = sorted((float(h[b, j]) for b in range(B) for j in range(gamma)), reverse=True)
+    n_max = min(B * gamma, n_sps - B)
+    thetas = [B * s[B - 1]]
+    S = 0.0
+    for n in range(1, n_max + 1):
+        S += old[n - 1]
+        thetas.append((B + S) * s[B + n - 1])
+    n_star = int(np.argmax(thetas))          # first maximum
+    best = float(thetas[n_star])
+    others = [t for i, t in enumerate(thetas) if i != n_star]
+    min_rel = (best - max(others)) / best if others else np.inf
+    cands = [(float(a[b, j]), b, j) for b in range(B) for j in range(gamma)]
+    cands.sort(key=lambda e: (-e[0], e[1], e[2]))
+    K = np.zeros(B, dtype=np.int64)
+    for av, b, j in cands[:n_star]:
+        K[b] += 1
+    if 0 < n_star < len(cands):
+        cut_gap = cands[n_star - 1][0] - cands[n_star][0]
+    else:
+        cut_gap = np.inf
+    return ScheduleResult(K, n_star, best, float(min_rel), float(cut_gap))
