@@ -212,6 +212,27 @@ int dspark_schedule(dspark_ctx* ctx, hipStream_t stream,
                     const float* sps, int n_sps,
                     int32_t* K, int32_t* n_selected, double* theta);
 
+/* Asynchronous prefix scheduler: capacity from history, order from now.
+ *
+ * [blog] "硬件感知前缀调度器" (the asynchronous mechanism: the verify length
+ * is estimated from the confidences of earlier steps so scheduling does not
+ * stall the pipeline); [summary] section 5 (the production rule: the count
+ * comes from confidences two steps old, candidates are still ranked by the
+ * latest ones, and the early-stop break is replaced by a global search).
+ *     Theta_n = (B + S_n) * sps[B + n - 1],  S_n = sum of the n largest
+ *               surv_hist values,  Theta_0 = B * sps[B - 1],
+ *     n*      = the first n attaining max Theta_n, 0 <= n <= min(B*gamma,
+ *               n_sps - B)  (no early stop),
+ * then the top n* candidates of surv, sorted (surv descending, b ascending,
+ * j ascending), are admitted: K[b] = their count for request b (a prefix).
+ * theta receives Theta_{n*}.  surv_hist: float [B][gamma], the same request
+ * slots two steps earlier (same value rules as surv).  Other arguments and
+ * limits as for dspark_schedule. */
+int dspark_schedule_async(dspark_ctx* ctx, hipStream_t stream,
+                          int B, int gamma, const float* surv,
+                          const float* surv_hist, const float* sps, int n_sps,
+                          int32_t* K, int32_t* n_selected, double* theta);
+
 /* Lossless speculative verification with residual resampling and a bonus.
  *
  * [blog] "形式化定义"; [summary] sections 1 and 4.  For request b with verify

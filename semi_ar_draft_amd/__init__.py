@@ -22,7 +22,7 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 
 EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
-    "dspark_draft_markov", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_verify",
+    "dspark_draft_markov", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
     "dspark_timing_enable", "dspark_timing_read",
 )
 KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
@@ -74,6 +74,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp]
     lib.dspark_schedule.restype = _i32
     lib.dspark_schedule.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp]
+    lib.dspark_schedule_async.restype = _i32
+    lib.dspark_schedule_async.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp]
     lib.dspark_verify.restype = _i32
     lib.dspark_verify.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -285,6 +287,26 @@ class Context:
         self._rc(self.lib.dspark_schedule(
             self._h, _stream(dev, stream), B, gamma, surv.data_ptr(), sps.data_ptr(), sps.shape[0],
             K.data_ptr(), n_sel.data_ptr(), theta.data_ptr()))
+        return K, n_sel, theta
+
+    # -- dspark_schedule_async ------------------------------------------------------
+    def schedule_async(self, surv, surv_hist, sps, out=None, stream=None):
+        """Capacity from ``surv_hist`` (two steps earlier), order from ``surv``."""
+        dev = self.device
+        _need(surv, "surv", torch.float32, dev, 2)
+        _need(surv_hist, "surv_hist", torch.float32, dev, 2)
+        _need(sps, "sps", torch.float32, dev, 1)
+        B, gamma = surv.shape
+        if tuple(surv_hist.shape) != (B, gamma):
+            raise ValueError("surv_hist must have the shape of surv")
+        if out is None:
+            out = (torch.empty((B,), dtype=torch.int32, device=dev),
+                   torch.empty((1,), dtype=torch.int32, device=dev),
+                   torch.empty((1,), dtype=torch.float64, device=dev))
+        K, n_sel, theta = out
+        self._rc(self.lib.dspark_schedule_async(
+            self._h, _stream(dev, stream), B, gamma, surv.data_ptr(), surv_hist.data_ptr(), sps.data_ptr(),
+            sps.shape[0], K.data_ptr(), n_sel.data_ptr(), theta.data_ptr()))
         return K, n_sel, theta
 
     # -- dspark_verify ------------------------------------------------------------

@@ -428,6 +428,30 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 4 * hs, pl.grid, pl.n_vc);
 }
 
+int schedule_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv, const float* hist,
+                    const float* sps, int n_sps, int32_t* K, int32_t* n_selected, double* theta) {
+  if (B < 1 || gamma < 1 || gamma > kMaxGamma) return fail(c, DSPARK_EINVAL, "bad shape B=%d gamma=%d", B, gamma);
+  if ((long)B * gamma > 4096) return fail(c, DSPARK_EINVAL, "B * gamma must be <= 4096");
+  if (n_sps < B) return fail(c, DSPARK_EINVAL, "n_sps (%d) must be >= B (%d)", n_sps, B);
+  if (!surv || !sps || !K || !n_selected || !theta) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  SchedArgs a;
+  a.B = B;
+  a.gamma = gamma;
+  a.n_sps = n_sps;
+  a.surv = surv;
+  a.surv_hist = hist;
+  a.sps = sps;
+  a.K = K;
+  a.n_selected = n_selected;
+  a.theta = theta;
+  int rc;
+  if ((rc = klaunch(c, DSPARK_K_SCHEDULE, schedule_kernel(hist ? 1 : 0), dim3(1), dim3(kSchedThreads), &a, stream)))
+    return rc;
+  return DSPARK_OK;
+}
+
 extern "C" {
 
 int dspark_version(void) { return kVersion; }
@@ -639,24 +663,15 @@ int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V
 int dspark_schedule(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv,
                     const float* sps, int n_sps, int32_t* K, int32_t* n_selected, double* theta) {
   if (!c) return DSPARK_EINVAL;
-  if (B < 1 || gamma < 1 || gamma > kMaxGamma) return fail(c, DSPARK_EINVAL, "bad shape B=%d gamma=%d", B, gamma);
-  if ((long)B * gamma > 4096) return fail(c, DSPARK_EINVAL, "B * gamma must be <= 4096");
-  if (n_sps < B) return fail(c, DSPARK_EINVAL, "n_sps (%d) must be >= B (%d)", n_sps, B);
-  if (!surv || !sps || !K || !n_selected || !theta) return fail(c, DSPARK_EINVAL, "null pointer argument");
-  DeviceGuard dg(c->device);
-  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
-  SchedArgs a;
-  a.B = B;
-  a.gamma = gamma;
-  a.n_sps = n_sps;
-  a.surv = surv;
-  a.sps = sps;
-  a.K = K;
-  a.n_selected = n_selected;
-  a.theta = theta;
-  int rc;
-  if ((rc = klaunch(c, DSPARK_K_SCHEDULE, schedule_kernel(), dim3(1), dim3(kSchedThreads), &a, stream))) return rc;
-  return DSPARK_OK;
+  return schedule_common(c, stream, B, gamma, surv, nullptr, sps, n_sps, K, n_selected, theta);
+}
+
+int dspark_schedule_async(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv,
+                          const float* surv_hist, const float* sps, int n_sps, int32_t* K, int32_t* n_selected,
+                          double* theta) {
+  if (!c) return DSPARK_EINVAL;
+  if (!surv_hist) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  return schedule_common(c, stream, B, gamma, surv, surv_hist, sps, n_sps, K, n_selected, theta);
 }
 
 int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,

@@ -111,6 +111,7 @@ struct ConfArgs {
 struct SchedArgs {
   int B, gamma, n_sps;
   const float* surv;
+  const float* surv_hist;        // asynchronous rule: survivals two steps earlier
   const float* sps;
   int32_t* K;
   int32_t* n_selected;
@@ -149,7 +150,7 @@ const void* confidence_kernel();
 const void* gru_init_kernel();
 const void* gru_step_kernel(int r);
 const void* survival_kernel();
-const void* schedule_kernel();
+const void* schedule_kernel(int async);
 
 constexpr int kSchedMaxKeys = 8192;
 constexpr int kSchedThreads = 1024;

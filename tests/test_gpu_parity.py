@@ -162,6 +162,34 @@ def test_schedule_kernel(ctx, B, G, n_sps, ties):
     assert float(theta.item()) == s.theta
 
 
+@pytest.mark.parametrize("B,G,n_sps,ties", SCHED)
+def test_schedule_async_kernel(ctx, B, G, n_sps, ties):
+    now = synth.survival_rows(B, G, seed=B * 37 + G, ties=ties)
+    hist = synth.survival_rows(B, G, seed=B * 41 + G + 1, ties=ties)
+    sps = synth.sps_table(n_sps)
+    print(f"async schedule B={B} gamma={G} n_sps={n_sps} ties={ties}", flush=True)
+    K, nsel, theta = ctx.schedule_async(now.cuda(), hist.cuda(), sps.cuda())
+    torch.cuda.synchronize()
+    s = oracle.schedule_async(now, hist, sps)
+    assert int(nsel.item()) == s.n_selected
+    assert float(theta.item()) == s.theta
+    assert np.array_equal(K.cpu().numpy(), s.K)
+
+
+def test_schedule_async_kernel_jagged_table(ctx):
+    """A table with a dip right after the first admissions: the global search
+    goes past it (the synchronous kernel on the same survivals stops before)."""
+    a = synth.survival_rows(256, 16, seed=3)
+    sps = torch.linspace(1000.0, 700.0, 4096)
+    sps[256 + 10:256 + 200] *= 0.9
+    K, nsel, theta = ctx.schedule_async(a.cuda(), a.cuda(), sps.cuda())
+    Ks, nsels, _ = ctx.schedule(a.cuda(), sps.cuda())
+    s = oracle.schedule_async(a, a, sps)
+    assert np.array_equal(K.cpu().numpy(), s.K)
+    assert int(nsel.item()) == s.n_selected and float(theta.item()) == s.theta
+    assert int(nsel.item()) > int(nsels.item())
+
+
 def test_schedule_kernel_flat_and_steep_tables(ctx):
     surv = synth.survival_rows(200, 7, seed=5)
     for sps in (torch.full((4096,), 3.0), torch.linspace(100.0, 1.0, 4096),
