@@ -267,6 +267,28 @@ int dspark_verify(dspark_ctx* ctx, hipStream_t stream,
                   float temperature, uint64_t seed,
                   int32_t* accept_len, int32_t* out_tokens);
 
+/* Lossless verification over a flattened (packed) target.
+ *
+ * [summary] section 5 (the variable-length verify batch: every request's
+ * rows to verify are laid end to end and a marker / offset tensor records
+ * which request and position each row belongs to).  As dspark_verify, but
+ * the target rows of request b, positions 1 .. K[b] + 1, are rows
+ * t_offsets[b] .. t_offsets[b] + K[b] of a packed float array of n_rows
+ * rows, row stride t_row_stride (>= V, multiple of 4; 16-byte aligned
+ * pointer): no padding rows are stored for positions past K[b] + 1.  K is
+ * required.  A row index outside [0, n_rows) is flagged (reported by
+ * dspark_check as a packed-row error) and replaced by row 0. */
+int dspark_verify_packed(dspark_ctx* ctx, hipStream_t stream,
+                         int B, int gamma, int V, int r, dspark_dtype wdtype,
+                         const float* target, int64_t t_row_stride,
+                         const int32_t* t_offsets, int n_rows,
+                         const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                         const void* W1, const void* W2, const int32_t* anchor,
+                         const int32_t* tokens, const float* lse, const float* ytok,
+                         const float* states, const int32_t* K, const uint32_t* req_ids,
+                         float temperature, uint64_t seed,
+                         int32_t* accept_len, int32_t* out_tokens);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
     "dspark_draft_markov", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
+    "dspark_verify_packed",
     "dspark_timing_enable", "dspark_timing_read",
 )
 KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
@@ -80,6 +81,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_verify.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
         _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
+        _vp, _vp, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp]
+    lib.dspark_verify_packed.restype = _i32
+    lib.dspark_verify_packed.argtypes = [
+        _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+        _vp, _i64, _vp, _i32, _vp, _i64, _i64, _vp, _vp, _vp,
         _vp, _vp, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp]
     if path is None:
         _lib = lib
@@ -357,6 +363,55 @@ class Context:
             target.data_ptr(), tsb, tsk, U.data_ptr(), usb, usk, _ptr(W1), W2.data_ptr(),
             _ptr(anchor), tokens.data_ptr(), lse.data_ptr(), ytok.data_ptr(), _ptr(states), _ptr(K),
             _ptr(req_ids), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+            acc.data_ptr(), toks.data_ptr()))
+        return acc, toks
+
+
+    # -- dspark_verify_packed -------------------------------------------------------
+    def verify_packed(self, target, t_offsets, U, W1, W2, anchor, tokens, lse, ytok, K, req_ids,
+                      temperature: float, seed: int, out=None, stream=None, states=None):
+        """``target`` [n_rows][V] packed: request b's rows 1 .. K[b]+1 start at
+        row t_offsets[b]."""
+        dev = self.device
+        _need(target, "target", torch.float32, dev, 2, contiguous=False)
+        if target.stride(1) != 1:
+            raise ValueError("target rows must be contiguous over the vocabulary")
+        n_rows, V = target.shape
+        usb, usk = _logits3(U, "U", dev)
+        B = U.shape[0]
+        _need(tokens, "tokens", torch.int32, dev, 2)
+        gamma = tokens.shape[1]
+        _need(t_offsets, "t_offsets", torch.int32, dev, 1)
+        _len(t_offsets, B, "t_offsets")
+        _need(K, "K", torch.int32, dev, 1)
+        _len(K, B, "K")
+        _need(W2, "W2", None, dev, 2)
+        r = W2.shape[1]
+        if W2.shape != (V, r):
+            raise ValueError("W2 must be [V][r]")
+        if states is None or W1 is not None:
+            _need(W1, "W1", W2.dtype, dev, 2)
+        if states is None or anchor is not None:
+            _need(anchor, "anchor", torch.int32, dev, 1)
+        if states is not None:
+            _need(states, "states", torch.float32, dev, 3)
+            if tuple(states.shape) != (gamma, B, r):
+                raise ValueError("states must be [gamma][B][r]")
+        for t, nm in ((tokens, "tokens"), (lse, "lse"), (ytok, "ytok")):
+            if tuple(t.shape) != (B, gamma):
+                raise ValueError(f"{nm} must be [B][gamma]")
+        if req_ids is not None:
+            _need(req_ids, "req_ids", torch.int32, dev, 1)
+            _len(req_ids, B, "req_ids")
+        if out is None:
+            out = (torch.empty((B,), dtype=torch.int32, device=dev),
+                   torch.empty((B, gamma + 1), dtype=torch.int32, device=dev))
+        acc, toks = out
+        self._rc(self.lib.dspark_verify_packed(
+            self._h, _stream(dev, stream), B, gamma, V, r, _wdtype(W2),
+            target.data_ptr(), target.stride(0), t_offsets.data_ptr(), n_rows, U.data_ptr(), usb, usk,
+            _ptr(W1), W2.data_ptr(), _ptr(anchor), tokens.data_ptr(), lse.data_ptr(), ytok.data_ptr(),
+            _ptr(states), K.data_ptr(), _ptr(req_ids), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
             acc.data_ptr(), toks.data_ptr()))
         return acc, toks
 

@@ -452,6 +452,174 @@ int schedule_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, const f
   return DSPARK_OK;
 }
 
+// Verification of either target layout (toffs null: strided rows; else
+// packed rows, request b's rows 1 .. K_b + 1 from row toffs[b] on).
+int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
+                  const float* target, int64_t t_stride_b, int64_t t_stride_k, const int32_t* toffs, int t_rows,
+                  const float* U,
+                  int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
+                  const int32_t* anchor, const int32_t* tokens, const float* lse, const float* ytok,
+                  const float* states, const int32_t* K, const uint32_t* req_ids, float temperature,
+                  uint64_t seed, int32_t* accept_len, int32_t* out_tokens) {
+  int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
+  if (rc) return rc;
+  if (!toffs) {
+    if ((rc = check_stream_rows(c, "target", target, t_stride_b, t_stride_k, B, gamma + 1, V))) return rc;
+  } else {
+    if (!target) return fail(c, DSPARK_EINVAL, "target is NULL");
+    if (!aligned16(target)) return fail(c, DSPARK_EINVAL, "target must be 16-byte aligned");
+    if (t_stride_k < V || (t_stride_k & 3)) return fail(c, DSPARK_EINVAL, "target row stride must be >= V and a multiple of 4");
+  }
+  const bool greedy = temperature == 0.0f;
+  if (!greedy && (rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
+  if (!tokens || !accept_len || !out_tokens) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  if (!greedy && (!W2 || !lse || !ytok || (!states && (!W1 || !anchor))))
+    return fail(c, DSPARK_EINVAL, "sampling verification needs U, W2, lse, ytok and W1 + anchor or states");
+  if (!greedy && ((W1 && !aligned16(W1)) || !aligned16(W2) || (states && !aligned16(states))))
+    return fail(c, DSPARK_EINVAL, "W1, W2 and states must be 16-byte aligned");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+
+  const int rows = B * (gamma + 1);
+  // windows of target rows: the first for every request, each later one only
+  // for requests that kept every draft so far
+  int win_lo[9], win_hi[9];
+  int n_win = 0;
+  {
+    int lo = 1;
+    for (int i = 0; i < 8 && c->verify_win[i] > 0 && c->verify_win[i] < gamma + 1; ++i) {
+      win_lo[n_win] = lo;
+      win_hi[n_win] = c->verify_win[i];
+      lo = c->verify_win[i] + 1;
+      ++n_win;
+    }
+    win_lo[n_win] = lo;
+    win_hi[n_win] = gamma + 1;
+    ++n_win;
+  }
+  const int n_chunks = ((V >> 2) + kRowsThreads * kRowsPer - 1) / (kRowsThreads * kRowsPer);
+  const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
+  const size_t n_rowpart = (size_t)rows * n_chunks;
+  const size_t n_respart = (size_t)B * pl.n_vc;
+  size_t off = 0;
+  const size_t off_rpf = off;
+  off += align256(n_rowpart * sizeof(float4));
+  const size_t off_rpi = off;
+  off += align256(n_rowpart * sizeof(int));
+  const size_t off_spf = off;
+  off += align256(n_respart * sizeof(float4));
+  const size_t off_spi = off;
+  off += align256(n_respart * sizeof(int2));
+  const size_t off_rk = off;
+  off += align256((size_t)B * sizeof(int32_t));
+  const size_t off_rlt = off;
+  off += align256((size_t)B * sizeof(float));
+  const size_t off_vs = off;
+  off += align256((size_t)B * sizeof(int2));
+  if ((rc = ensure_ws(c, off))) return rc;
+  char* ws = static_cast<char*>(c->ws);
+  float4* rpf = reinterpret_cast<float4*>(ws + off_rpf);
+  int* rpi = reinterpret_cast<int*>(ws + off_rpi);
+  float4* spf = reinterpret_cast<float4*>(ws + off_spf);
+  int2* spi = reinterpret_cast<int2*>(ws + off_spi);
+  int32_t* resid_k = reinterpret_cast<int32_t*>(ws + off_rk);
+  float* resid_lt = reinterpret_cast<float*>(ws + off_rlt);
+  int2* vstate = reinterpret_cast<int2*>(ws + off_vs);
+
+  const float invT = greedy ? 1.0f : 1.0f / temperature;
+  for (int w = 0; w < n_win; ++w) {
+    const int nrows = win_hi[w] - win_lo[w] + 1;
+    VerifyArgs va;
+    memset(&va, 0, sizeof(va));
+    va.B = B;
+    va.gamma = gamma;
+    va.V = V;
+    va.n_chunks = n_chunks;
+    va.greedy = greedy;
+    va.lo = win_lo[w];
+    va.hi = win_hi[w];
+    va.first = w == 0;
+    va.vstate = vstate;
+    va.T = target;
+    va.tsb = t_stride_b;
+    va.toffs = toffs;
+    va.t_rows = t_rows;
+    va.tsk = t_stride_k;
+    va.K = K;
+    va.req = req_ids;
+    va.tokens = tokens;
+    va.lse = lse;
+    va.ytok = ytok;
+    va.invT = invT;
+    va.s2 = greedy ? kLog2e : kLog2e / temperature;
+    va.seed = seed;
+    va.pf = rpf;
+    va.pi = rpi;
+    va.accept_len = accept_len;
+    va.out_tokens = out_tokens;
+    va.resid_k = resid_k;
+    va.resid_lt = resid_lt;
+    va.err = c->dev_err;
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), dim3(n_chunks, B * nrows), dim3(kRowsThreads), &va,
+                      stream)))
+      return rc;
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &va, stream))) return rc;
+  }
+  if (greedy) return DSPARK_OK;
+
+  SweepArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.B = B;
+  sa.gamma = gamma;
+  sa.V = V;
+  sa.k = 0;
+  sa.n_rg = pl.n_rg;
+  sa.n_vc = pl.n_vc;
+  sa.n_tiles = pl.n_tiles;
+  sa.xcd_remap = 1;
+  sa.U = U;
+  sa.usb = u_stride_b;
+  sa.usk = u_stride_k;
+  sa.T = target;
+  sa.tsb = t_stride_b;
+  sa.toffs = toffs;
+  sa.t_rows = t_rows;
+  sa.tsk = t_stride_k;
+  sa.W1 = W1;
+  sa.W2 = W2;
+  sa.anchor = anchor;
+  sa.tokens = tokens;
+  sa.req = req_ids;
+  sa.resid_k = resid_k;
+  sa.lse = lse;
+  sa.resid_lt = resid_lt;
+  sa.invT = invT;
+  sa.s2 = kLog2e / temperature;
+  sa.seed = seed;
+  sa.pf = spf;
+  sa.pi = spi;
+  sa.hstate = states;
+  sa.err = c->dev_err;
+  const void* rfn = sweep_kernel((int)wdtype, r, kModeResidual, pl.shared ? c->resid_depth : 0,
+                                 pl.shared ? c->resid_nt : 1, states ? 1 : 0);
+  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, rfn, dim3(pl.grid), dim3(256), &sa, stream))) return rc;
+
+  CombineArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.B = B;
+  ca.gamma = gamma;
+  ca.V = V;
+  ca.n_vc = pl.n_vc;
+  ca.pf = spf;
+  ca.pi = spi;
+  ca.resid_k = resid_k;
+  ca.accept_len = accept_len;
+  ca.out_tokens = out_tokens;
+  ca.err = c->dev_err;
+  if ((rc = klaunch(c, DSPARK_K_RESID_COMBINE, combine_resid_kernel(), dim3(B), dim3(256), &ca, stream))) return rc;
+  return DSPARK_OK;
+}
+
 extern "C" {
 
 int dspark_version(void) { return kVersion; }
@@ -550,9 +718,10 @@ int dspark_check(dspark_ctx* c, hipStream_t stream) {
   DSPARK_HIP(c, hipMemcpy(&flag, c->dev_err, sizeof(flag), hipMemcpyDeviceToHost));
   if (flag) {
     DSPARK_HIP(c, hipMemset(c->dev_err, 0, sizeof(int32_t)));
-    return fail(c, DSPARK_EDEVICE, "device error flag 0x%x:%s%s", flag,
+    return fail(c, DSPARK_EDEVICE, "device error flag 0x%x:%s%s%s", flag,
                 (flag & kErrToken) ? " token id out of range" : "",
-                (flag & kErrK) ? " verify length out of range" : "");
+                (flag & kErrK) ? " verify length out of range" : "",
+                (flag & kErrRow) ? " packed target row out of range" : "");
   }
   c->err.clear();
   return DSPARK_OK;
@@ -681,153 +850,23 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
                   const float* states, const int32_t* K, const uint32_t* req_ids, float temperature,
                   uint64_t seed, int32_t* accept_len, int32_t* out_tokens) {
   if (!c) return DSPARK_EINVAL;
-  int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
-  if (rc) return rc;
-  if ((rc = check_stream_rows(c, "target", target, t_stride_b, t_stride_k, B, gamma + 1, V))) return rc;
-  const bool greedy = temperature == 0.0f;
-  if (!greedy && (rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
-  if (!tokens || !accept_len || !out_tokens) return fail(c, DSPARK_EINVAL, "null pointer argument");
-  if (!greedy && (!W2 || !lse || !ytok || (!states && (!W1 || !anchor))))
-    return fail(c, DSPARK_EINVAL, "sampling verification needs U, W2, lse, ytok and W1 + anchor or states");
-  if (!greedy && ((W1 && !aligned16(W1)) || !aligned16(W2) || (states && !aligned16(states))))
-    return fail(c, DSPARK_EINVAL, "W1, W2 and states must be 16-byte aligned");
-  DeviceGuard dg(c->device);
-  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  return verify_common(c, stream, B, gamma, V, r, wdtype, target, t_stride_b, t_stride_k, nullptr, 0, U, u_stride_b,
+                       u_stride_k, W1, W2, anchor, tokens, lse, ytok, states, K, req_ids, temperature, seed,
+                       accept_len, out_tokens);
+}
 
-  const int rows = B * (gamma + 1);
-  // windows of target rows: the first for every request, each later one only
-  // for requests that kept every draft so far
-  int win_lo[9], win_hi[9];
-  int n_win = 0;
-  {
-    int lo = 1;
-    for (int i = 0; i < 8 && c->verify_win[i] > 0 && c->verify_win[i] < gamma + 1; ++i) {
-      win_lo[n_win] = lo;
-      win_hi[n_win] = c->verify_win[i];
-      lo = c->verify_win[i] + 1;
-      ++n_win;
-    }
-    win_lo[n_win] = lo;
-    win_hi[n_win] = gamma + 1;
-    ++n_win;
-  }
-  const int n_chunks = ((V >> 2) + kRowsThreads * kRowsPer - 1) / (kRowsThreads * kRowsPer);
-  const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
-  const size_t n_rowpart = (size_t)rows * n_chunks;
-  const size_t n_respart = (size_t)B * pl.n_vc;
-  size_t off = 0;
-  const size_t off_rpf = off;
-  off += align256(n_rowpart * sizeof(float4));
-  const size_t off_rpi = off;
-  off += align256(n_rowpart * sizeof(int));
-  const size_t off_spf = off;
-  off += align256(n_respart * sizeof(float4));
-  const size_t off_spi = off;
-  off += align256(n_respart * sizeof(int2));
-  const size_t off_rk = off;
-  off += align256((size_t)B * sizeof(int32_t));
-  const size_t off_rlt = off;
-  off += align256((size_t)B * sizeof(float));
-  const size_t off_vs = off;
-  off += align256((size_t)B * sizeof(int2));
-  if ((rc = ensure_ws(c, off))) return rc;
-  char* ws = static_cast<char*>(c->ws);
-  float4* rpf = reinterpret_cast<float4*>(ws + off_rpf);
-  int* rpi = reinterpret_cast<int*>(ws + off_rpi);
-  float4* spf = reinterpret_cast<float4*>(ws + off_spf);
-  int2* spi = reinterpret_cast<int2*>(ws + off_spi);
-  int32_t* resid_k = reinterpret_cast<int32_t*>(ws + off_rk);
-  float* resid_lt = reinterpret_cast<float*>(ws + off_rlt);
-  int2* vstate = reinterpret_cast<int2*>(ws + off_vs);
-
-  const float invT = greedy ? 1.0f : 1.0f / temperature;
-  for (int w = 0; w < n_win; ++w) {
-    const int nrows = win_hi[w] - win_lo[w] + 1;
-    VerifyArgs va;
-    memset(&va, 0, sizeof(va));
-    va.B = B;
-    va.gamma = gamma;
-    va.V = V;
-    va.n_chunks = n_chunks;
-    va.greedy = greedy;
-    va.lo = win_lo[w];
-    va.hi = win_hi[w];
-    va.first = w == 0;
-    va.vstate = vstate;
-    va.T = target;
-    va.tsb = t_stride_b;
-    va.tsk = t_stride_k;
-    va.K = K;
-    va.req = req_ids;
-    va.tokens = tokens;
-    va.lse = lse;
-    va.ytok = ytok;
-    va.invT = invT;
-    va.s2 = greedy ? kLog2e : kLog2e / temperature;
-    va.seed = seed;
-    va.pf = rpf;
-    va.pi = rpi;
-    va.accept_len = accept_len;
-    va.out_tokens = out_tokens;
-    va.resid_k = resid_k;
-    va.resid_lt = resid_lt;
-    va.err = c->dev_err;
-    if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), dim3(n_chunks, B * nrows), dim3(kRowsThreads), &va,
-                      stream)))
-      return rc;
-    if ((rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &va, stream))) return rc;
-  }
-  if (greedy) return DSPARK_OK;
-
-  SweepArgs sa;
-  memset(&sa, 0, sizeof(sa));
-  sa.B = B;
-  sa.gamma = gamma;
-  sa.V = V;
-  sa.k = 0;
-  sa.n_rg = pl.n_rg;
-  sa.n_vc = pl.n_vc;
-  sa.n_tiles = pl.n_tiles;
-  sa.xcd_remap = 1;
-  sa.U = U;
-  sa.usb = u_stride_b;
-  sa.usk = u_stride_k;
-  sa.T = target;
-  sa.tsb = t_stride_b;
-  sa.tsk = t_stride_k;
-  sa.W1 = W1;
-  sa.W2 = W2;
-  sa.anchor = anchor;
-  sa.tokens = tokens;
-  sa.req = req_ids;
-  sa.resid_k = resid_k;
-  sa.lse = lse;
-  sa.resid_lt = resid_lt;
-  sa.invT = invT;
-  sa.s2 = kLog2e / temperature;
-  sa.seed = seed;
-  sa.pf = spf;
-  sa.pi = spi;
-  sa.hstate = states;
-  sa.err = c->dev_err;
-  const void* rfn = sweep_kernel((int)wdtype, r, kModeResidual, pl.shared ? c->resid_depth : 0,
-                                 pl.shared ? c->resid_nt : 1, states ? 1 : 0);
-  if ((rc = klaunch(c, DSPARK_K_RESID_SWEEP, rfn, dim3(pl.grid), dim3(256), &sa, stream))) return rc;
-
-  CombineArgs ca;
-  memset(&ca, 0, sizeof(ca));
-  ca.B = B;
-  ca.gamma = gamma;
-  ca.V = V;
-  ca.n_vc = pl.n_vc;
-  ca.pf = spf;
-  ca.pi = spi;
-  ca.resid_k = resid_k;
-  ca.accept_len = accept_len;
-  ca.out_tokens = out_tokens;
-  ca.err = c->dev_err;
-  if ((rc = klaunch(c, DSPARK_K_RESID_COMBINE, combine_resid_kernel(), dim3(B), dim3(256), &ca, stream))) return rc;
-  return DSPARK_OK;
+int dspark_verify_packed(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
+                         const float* target, int64_t t_row_stride, const int32_t* t_offsets, int n_rows,
+                         const float* U, int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
+                         const int32_t* anchor, const int32_t* tokens, const float* lse, const float* ytok,
+                         const float* states, const int32_t* K, const uint32_t* req_ids, float temperature,
+                         uint64_t seed, int32_t* accept_len, int32_t* out_tokens) {
+  if (!c) return DSPARK_EINVAL;
+  if (!t_offsets || !K) return fail(c, DSPARK_EINVAL, "the packed layout needs t_offsets and K");
+  if (n_rows < 1) return fail(c, DSPARK_EINVAL, "n_rows must be >= 1");
+  return verify_common(c, stream, B, gamma, V, r, wdtype, target, 0, t_row_stride, t_offsets, n_rows, U, u_stride_b,
+                       u_stride_k, W1, W2, anchor, tokens, lse, ytok, states, K, req_ids, temperature, seed,
+                       accept_len, out_tokens);
 }
 
 }  // extern "C"

@@ -19,6 +19,22 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Device error flag bits.
 constexpr int kErrToken = 1;    // a token id outside [0, V)
 constexpr int kErrK = 2;        // a verify length outside [0, gamma]
+constexpr int kErrRow = 4;      // a packed target row outside [0, n_rows)
+
+// Element offset of target row (b, k) (k 1-based): strided [B][gamma+1][V]
+// placement, or the packed layout where request b's rows 1 .. K_b + 1 start
+// at row toffs[b] of an array of n_rows rows.  A packed row outside the
+// array is flagged and replaced by row 0 (in bounds; results then invalid).
+__device__ __forceinline__ int64_t target_row(const int32_t* toffs, int n_rows, int64_t tsb, int64_t tsk, int b,
+                                              int k, int32_t* err) {
+  if (!toffs) return (int64_t)b * tsb + (int64_t)(k - 1) * tsk;
+  int64_t r = (int64_t)toffs[b] + (k - 1);
+  if (r < 0 || r >= n_rows) {
+    atomicOr(err, kErrRow);
+    r = 0;
+  }
+  return r * tsk;
+}
 
 // ---------------------------------------------------------------------------
 // Counter-based random numbers.

@@ -26,6 +26,8 @@ struct SweepArgs {
   int64_t usb, usk;
   const float* T;                // target logits (residual mode)
   int64_t tsb, tsk;
+  const int32_t* toffs;          // packed target rows: first row of each request, or null
+  int t_rows;                    // rows of the packed target
   const void* W1;
   const void* W2;
   const int32_t* anchor;
@@ -78,6 +80,8 @@ struct VerifyArgs {
   int2* vstate;                  // per request {accepted so far, next row (0 = done)}
   const float* T;
   int64_t tsb, tsk;
+  const int32_t* toffs;          // packed target rows: first row of each request, or null
+  int t_rows;                    // rows of the packed target
   const int32_t* K;
   const uint32_t* req;
   const int32_t* tokens;

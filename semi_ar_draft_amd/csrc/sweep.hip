@@ -244,7 +244,7 @@ struct WaveRows {
         v = v && k > 0 && k <= a.gamma;
       }
       uoff[nb] = v ? (int64_t)b * a.usb + (int64_t)(k - 1) * a.usk : 0;
-      toff[nb] = (v && MODE == kModeResidual) ? (int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk : 0;
+      toff[nb] = (v && MODE == kModeResidual) ? target_row(a.toffs, a.t_rows, a.tsb, a.tsk, b, k, a.err) : 0;
       ok[nb] = v;
       rows[nb] = b;
       kk[nb] = k;

@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArg
   if (k > kb + 1) return;
   const int64_t row = (int64_t)b * (a.gamma + 1) + (k - 1);
   const bool bonus = (k == kb + 1);
-  const float4* p = reinterpret_cast<const float4*>(a.T + (int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk);
+  const float4* p =
+      reinterpret_cast<const float4*>(a.T + target_row(a.toffs, a.t_rows, a.tsb, a.tsk, b, k, a.err));
   const int nv4 = a.V >> 2;
   const int c0 = chunk * kRowsThreads * kRowsPer;
   const int c1 = min(nv4, c0 + kRowsThreads * kRowsPer);
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
       x = 0;
     }
     if (!a.greedy) {
-      tx = a.T[(int64_t)b * a.tsb + (int64_t)(k - 1) * a.tsk + x];
+      tx = a.T[target_row(a.toffs, a.t_rows, a.tsb, a.tsk, b, k, a.err) + x];
       const int64_t o = (int64_t)b * a.gamma + k - 1;
       lpd = a.ytok[o] - a.lse[o];
     }

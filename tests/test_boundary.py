@@ -60,6 +60,8 @@ def test_null_context_is_rejected_everywhere():
     assert lib.dspark_schedule_async(None, None, 1, 1, None, None, None, 1, None, None, None) == dk.DSPARK_EINVAL
     assert lib.dspark_verify(None, None, 1, 1, 16, 32, 1, None, 32, 16, None, 16, 16, None, None,
                              None, None, None, None, None, None, None, 0.0, 0, None, None) == dk.DSPARK_EINVAL
+    assert lib.dspark_verify_packed(None, None, 1, 1, 16, 32, 1, None, 16, None, 1, None, 16, 16, None, None,
+                                    None, None, None, None, None, None, None, 0.0, 0, None, None) == dk.DSPARK_EINVAL
     assert lib.dspark_draft_rnn(None, None, 1, 1, 16, 32, 1, None, 16, 16, None, None, None, None, None,
                                 None, None, None, 0.0, 0, None, None, None, None) == dk.DSPARK_EINVAL
 
