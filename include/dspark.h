@@ -99,7 +99,8 @@ enum {
   DSPARK_K_RESID_SWEEP = 7,    /* MFMA residual sweep */
   DSPARK_K_RESID_COMBINE = 8,
   DSPARK_K_GRU = 9,            /* GRU head: s_0 fill and state updates */
-  DSPARK_K_COUNT = 10
+  DSPARK_K_DIAG = 10,          /* diagnostic passes (dspark_accept_prob) */
+  DSPARK_K_COUNT = 11
 };
 int dspark_timing_enable(dspark_ctx* ctx, int enable);
 int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
@@ -266,6 +267,29 @@ int dspark_verify(dspark_ctx* ctx, hipStream_t stream,
                   const float* states, const int32_t* K, const uint32_t* req_ids,
                   float temperature, uint64_t seed,
                   int32_t* accept_len, int32_t* out_tokens);
+
+/* Diagnostics: per-position acceptance probabilities.
+ *
+ * [summary] section 4 (the confidence head is trained toward the true
+ * acceptance rate, the total-variation distance between the draft and the
+ * target distributions) and [blog] "置信度头" (c_k is P(position k accepted |
+ * the earlier ones were)).  Under the lossless rule the drafted token at
+ * position k is kept with probability
+ *     alpha[b][k-1] = sum_v min(p_d(v), p_t(v)) = 1 - TV(p_d, p_t)
+ * given its prefix, p_d the draft law (U and the bias of the head that
+ * drafted: W1 + anchor + tokens for the Markov head, states for the GRU
+ * head), p_t = softmax(target[b][k-1] / T).  Averaged over requests it
+ * gives the acceptance curve per position.  A diagnostic pass outside the
+ * step: it reads every target row 1..gamma and rebuilds every draft row.
+ * Arguments as for dspark_verify (target needs only gamma rows);
+ * temperature > 0; alpha: float [B][gamma]. */
+int dspark_accept_prob(dspark_ctx* ctx, hipStream_t stream,
+                       int B, int gamma, int V, int r, dspark_dtype wdtype,
+                       const float* target, int64_t t_stride_b, int64_t t_stride_k,
+                       const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                       const void* W1, const void* W2, const int32_t* anchor,
+                       const int32_t* tokens, const float* lse, const float* states,
+                       float temperature, float* alpha);
 
 /* Lossless verification over a flattened (packed) target.
  *

@@ -152,3 +152,38 @@ def verify(target, tokens, lse_d, ytok, U, W1, W2, anchor, K, req_ids,
             out[b, A] = star
         acc[b] = A
     return VerifyResult(acc, out, margin, final_margin, lse_t, resid_row)
+
+
+def accept_prob(target, tokens, lse_d, U, W1, W2, anchor, temperature: float, gamma: int,
+                states=None) -> np.ndarray:
+    """Per-position acceptance probability alpha[b, k-1] = sum_v min(p_d(v), p_t(v)).
+
+    [summary] section 4 (the confidence head is trained toward the true
+    acceptance rate, the total-variation distance between the draft and the
+    target distributions) and [blog] "置信度头" (c_k targets P(accept k | all
+    before accepted)): with the lossless rule, position k is kept with
+    probability sum_v min(p_d, p_t) = 1 - TV(p_d, p_t) given its prefix.
+    p_d is rebuilt from U and the bias of the given head (Markov: W1 of the
+    previous drafted token, anchor at k = 1; GRU: ``states``); lse_d is the
+    draft log-normaliser the draft returned.  Sampling temperatures only.
+    """
+    tok = _ints(tokens)
+    anc = _ints(anchor) if anchor is not None else None
+    lse_d = np.asarray(lse_d, dtype=np.float64)
+    B = tok.shape[0]
+    T = float(temperature)
+    W1d = decode_weights(W1) if states is None else None
+    W2d = decode_weights(W2)
+    out = np.zeros((B, gamma))
+    for b in range(B):
+        for k in range(1, gamma + 1):
+            if states is None:
+                prev = int(anc[b]) if k == 1 else int(tok[b, k - 2])
+                bias = markov_bias(W1d, W2d, np.array([prev]))[0]
+            else:
+                bias = W2d @ np.asarray(states[b, k - 1], dtype=np.float64)
+            z = _row(U, b, k - 1) + bias
+            lpd = z / T - lse_d[b, k - 1]
+            lpt = target_logprobs(_row(target, b, k - 1), T)
+            out[b, k - 1] = np.minimum(np.exp(lpd), np.exp(lpt)).sum()
+    return out

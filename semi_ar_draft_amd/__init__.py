@@ -23,11 +23,11 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
     "dspark_draft_markov", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
-    "dspark_verify_packed",
+    "dspark_verify_packed", "dspark_accept_prob",
     "dspark_timing_enable", "dspark_timing_read",
 )
 KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
-                  "verify_rows", "verify_decide", "resid_sweep", "resid_combine", "gru")
+                  "verify_rows", "verify_decide", "resid_sweep", "resid_combine", "gru", "diag")
 
 _lib = None
 _vp, _i32, _i64, _u64, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
@@ -87,6 +87,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
         _vp, _i64, _vp, _i32, _vp, _i64, _i64, _vp, _vp, _vp,
         _vp, _vp, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp]
+    lib.dspark_accept_prob.restype = _i32
+    lib.dspark_accept_prob.argtypes = [
+        _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+        _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp]
     if path is None:
         _lib = lib
     return lib
@@ -414,6 +418,33 @@ class Context:
             _ptr(states), K.data_ptr(), _ptr(req_ids), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
             acc.data_ptr(), toks.data_ptr()))
         return acc, toks
+
+
+    # -- dspark_accept_prob ---------------------------------------------------------
+    def accept_prob(self, target, U, W1, W2, anchor, tokens, lse, temperature: float, states=None,
+                    out=None, stream=None):
+        """alpha[b][k-1] = sum_v min(p_d, p_t): the acceptance probability of every drafted position."""
+        dev = self.device
+        tsb, tsk = _logits3(target, "target", dev)
+        usb, usk = _logits3(U, "U", dev)
+        B, _, V = target.shape
+        _need(tokens, "tokens", torch.int32, dev, 2)
+        gamma = tokens.shape[1]
+        _need(W2, "W2", None, dev, 2)
+        r = W2.shape[1]
+        _need(lse, "lse", torch.float32, dev, 2)
+        if states is None:
+            _need(W1, "W1", W2.dtype, dev, 2)
+            _need(anchor, "anchor", torch.int32, dev, 1)
+        else:
+            _need(states, "states", torch.float32, dev, 3)
+        if out is None:
+            out = torch.empty((B, gamma), dtype=torch.float32, device=dev)
+        self._rc(self.lib.dspark_accept_prob(
+            self._h, _stream(dev, stream), B, gamma, V, r, _wdtype(W2), target.data_ptr(), tsb, tsk,
+            U.data_ptr(), usb, usk, _ptr(W1), W2.data_ptr(), _ptr(anchor), tokens.data_ptr(), lse.data_ptr(),
+            _ptr(states), float(temperature), out.data_ptr()))
+        return out
 
 
 __all__ = ["Context", "DSparkError", "load_library", "LIB_PATH", "EXPORTS", "KERNEL_CLASSES",

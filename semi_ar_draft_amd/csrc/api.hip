@@ -620,6 +620,113 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   return DSPARK_OK;
 }
 
+// Diagnostic pass: per-position acceptance probabilities.
+int accept_prob_impl(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
+                     const float* target, int64_t t_stride_b, int64_t t_stride_k, const float* U,
+                     int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2, const int32_t* anchor,
+                     const int32_t* tokens, const float* lse, const float* states, float temperature, float* alpha) {
+  int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
+  if (rc) return rc;
+  if (!(temperature > 0.0f)) return fail(c, DSPARK_EINVAL, "acceptance probabilities need temperature > 0");
+  if ((rc = check_stream_rows(c, "target", target, t_stride_b, t_stride_k, B, gamma, V))) return rc;
+  if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
+  if (!W2 || !tokens || !lse || !alpha || (!states && (!W1 || !anchor)))
+    return fail(c, DSPARK_EINVAL, "null pointer argument");
+  if ((W1 && !aligned16(W1)) || !aligned16(W2) || (states && !aligned16(states)))
+    return fail(c, DSPARK_EINVAL, "W1, W2 and states must be 16-byte aligned");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+
+  const int rows = B * (gamma + 1);
+  const int n_chunks = ((V >> 2) + kRowsThreads * kRowsPer - 1) / (kRowsThreads * kRowsPer);
+  const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
+  const size_t n_rowpart = (size_t)rows * n_chunks;
+  const size_t npos = (size_t)B * pl.n_vc;
+  size_t off = 0;
+  const size_t off_rpf = off;
+  off += align256(n_rowpart * sizeof(float4));
+  const size_t off_rpi = off;
+  off += align256(n_rowpart * sizeof(int));
+  const size_t off_lse = off;
+  off += align256((size_t)B * gamma * sizeof(float));
+  const size_t off_spf = off;
+  off += align256(npos * gamma * sizeof(float4));
+  if ((rc = ensure_ws(c, off))) return rc;
+  char* ws = static_cast<char*>(c->ws);
+  float4* rpf = reinterpret_cast<float4*>(ws + off_rpf);
+  int* rpi = reinterpret_cast<int*>(ws + off_rpi);
+  float* row_lse = reinterpret_cast<float*>(ws + off_lse);
+  float4* spf = reinterpret_cast<float4*>(ws + off_spf);
+
+  // 1. log-normaliser of every target row 1..gamma
+  VerifyArgs va;
+  memset(&va, 0, sizeof(va));
+  va.B = B;
+  va.gamma = gamma;
+  va.V = V;
+  va.n_chunks = n_chunks;
+  va.lo = 1;
+  va.hi = gamma;
+  va.first = 1;
+  va.T = target;
+  va.tsb = t_stride_b;
+  va.tsk = t_stride_k;
+  va.s2 = kLog2e / temperature;
+  va.pf = rpf;
+  va.pi = rpi;
+  va.row_lse = row_lse;
+  va.err = c->dev_err;
+  if ((rc = klaunch(c, DSPARK_K_DIAG, verify_rows_kernel(), dim3(n_chunks, B * gamma), dim3(kRowsThreads), &va,
+                    stream)))
+    return rc;
+  if ((rc = klaunch(c, DSPARK_K_DIAG, rows_lse_kernel(), dim3(B, gamma), dim3(64), &va, stream))) return rc;
+
+  // 2. per position, sum over the vocabulary of min(p_t, p_d), the draft row
+  //    rebuilt on MFMA as in the draft
+  SweepArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.B = B;
+  sa.gamma = gamma;
+  sa.V = V;
+  sa.n_rg = pl.n_rg;
+  sa.n_vc = pl.n_vc;
+  sa.n_tiles = pl.n_tiles;
+  sa.xcd_remap = 1;
+  sa.U = U;
+  sa.usb = u_stride_b;
+  sa.usk = u_stride_k;
+  sa.T = target;
+  sa.tsb = t_stride_b;
+  sa.tsk = t_stride_k;
+  sa.W1 = W1;
+  sa.W2 = W2;
+  sa.anchor = anchor;
+  sa.tokens = tokens;
+  sa.lse = lse;
+  sa.resid_lt = row_lse;
+  sa.hstate = states;
+  sa.invT = 1.0f / temperature;
+  sa.s2 = kLog2e / temperature;
+  sa.err = c->dev_err;
+  const void* fn = sweep_kernel((int)wdtype, r, kModeAlpha, pl.shared ? c->resid_depth : 0,
+                                pl.shared ? c->resid_nt : 1, states ? 1 : 0);
+  for (int k = 1; k <= gamma; ++k) {
+    sa.k = k;
+    sa.pf = spf + (size_t)(k - 1) * npos;
+    if ((rc = klaunch(c, DSPARK_K_DIAG, fn, dim3(pl.grid), dim3(256), &sa, stream))) return rc;
+  }
+  CombineArgs ca;
+  memset(&ca, 0, sizeof(ca));
+  ca.B = B;
+  ca.gamma = gamma;
+  ca.V = V;
+  ca.n_vc = pl.n_vc;
+  ca.pf = spf;
+  ca.lse = alpha;
+  ca.err = c->dev_err;
+  return klaunch(c, DSPARK_K_DIAG, combine_alpha_kernel(), dim3(B, gamma), dim3(256), &ca, stream);
+}
+
 extern "C" {
 
 int dspark_version(void) { return kVersion; }
@@ -853,6 +960,16 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   return verify_common(c, stream, B, gamma, V, r, wdtype, target, t_stride_b, t_stride_k, nullptr, 0, U, u_stride_b,
                        u_stride_k, W1, W2, anchor, tokens, lse, ytok, states, K, req_ids, temperature, seed,
                        accept_len, out_tokens);
+}
+
+int dspark_accept_prob(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
+                       const float* target, int64_t t_stride_b, int64_t t_stride_k, const float* U,
+                       int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
+                       const int32_t* anchor, const int32_t* tokens, const float* lse, const float* states,
+                       float temperature, float* alpha) {
+  if (!c) return DSPARK_EINVAL;
+  return accept_prob_impl(c, stream, B, gamma, V, r, wdtype, target, t_stride_b, t_stride_k, U, u_stride_b,
+                          u_stride_k, W1, W2, anchor, tokens, lse, states, temperature, alpha);
 }
 
 int dspark_verify_packed(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,

@@ -16,7 +16,10 @@ constexpr int kTileV = 16;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBestGroups = 16;
 
-enum SweepMode : int { kModeDraftGreedy = 0, kModeDraftSample = 1, kModeResidual = 2 };
+// kModeAlpha: the acceptance probability sum_v min(p_t, p_d) of every
+// request at one position (a diagnostic pass; resid_lt then holds the
+// target log-normalisers [B][gamma]).
+enum SweepMode : int { kModeDraftGreedy = 0, kModeDraftSample = 1, kModeResidual = 2, kModeAlpha = 3 };
 
 struct SweepArgs {
   int B, gamma, V, k;            // k: 1-based draft position (draft modes)
@@ -95,6 +98,7 @@ struct VerifyArgs {
   int32_t* out_tokens;
   int32_t* resid_k;
   float* resid_lt;
+  float* row_lse;                // diagnostic pass: ln sum exp(t/T) of rows 1..gamma, [B][gamma]
   int32_t* err;
 };
 
@@ -148,6 +152,8 @@ struct GruArgs {
 const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs);
 const void* combine_draft_kernel();
 const void* combine_resid_kernel();
+const void* combine_alpha_kernel();
+const void* rows_lse_kernel();
 const void* verify_rows_kernel();
 const void* verify_decide_kernel();
 const void* confidence_kernel();

@@ -136,6 +136,17 @@ __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const f
         }
       }
     }
+  } else if constexpr (MODE == kModeAlpha) {
+    // acceptance probability: sum over v of min(p_t(v), p_d(v))
+    const float tv[4] = {t.x, t.y, t.z, t.w};
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pt = fast_exp2(__builtin_fmaf(tv[i], invT, -lt) * kLog2e);
+      const float pd = fast_exp2(__builtin_fmaf(z[i], invT, -ld) * kLog2e);
+      acc += fminf(pt, pd);
+    }
+    st.s += acc;
   } else {
     // residual: weights r_v = max(0, p_t - p_d) with mass R; the fallback
     // (empty residual) draws from p_t with mass P, sharing the group's
@@ -176,6 +187,10 @@ __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const f
 
 template <int MODE>
 __device__ __forceinline__ void lane_merge(LaneState& st, int mask) {
+  if constexpr (MODE == kModeAlpha) {
+    st.s += shfl_xor(st.s, mask);
+    return;
+  }
   if constexpr (MODE != kModeResidual) {
     const float m2 = shfl_xor(st.m, mask);
     const float s2 = shfl_xor(st.s, mask);
@@ -244,7 +259,9 @@ struct WaveRows {
         v = v && k > 0 && k <= a.gamma;
       }
       uoff[nb] = v ? (int64_t)b * a.usb + (int64_t)(k - 1) * a.usk : 0;
-      toff[nb] = (v && MODE == kModeResidual) ? target_row(a.toffs, a.t_rows, a.tsb, a.tsk, b, k, a.err) : 0;
+      toff[nb] = (v && (MODE == kModeResidual || MODE == kModeAlpha))
+                     ? target_row(a.toffs, a.t_rows, a.tsb, a.tsk, b, k, a.err)
+                     : 0;
       ok[nb] = v;
       rows[nb] = b;
       kk[nb] = k;
@@ -257,7 +274,7 @@ struct WaveRows {
   // row (q = 0..3) read a quarter of the groups each and share the maximum.
   __device__ __forceinline__ void setup_rest(const SweepArgs& a, int q) {
     unsigned long long pb[2] = {0ull, 0ull};
-    if (HS == 0 && MODE != kModeResidual && a.best_prev) {
+    if (HS == 0 && MODE != kModeResidual && MODE != kModeAlpha && a.best_prev) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if (ok[nb]) {
@@ -284,7 +301,7 @@ struct WaveRows {
       if (ok[nb] && HS == 0) {
         if (k == 1)
           prev = a.anchor[b];
-        else if (MODE != kModeResidual && a.best_prev)
+        else if (MODE != kModeResidual && MODE != kModeAlpha && a.best_prev)
           prev = best_index(pb[nb]);
         else
           prev = a.tokens[(int64_t)b * a.gamma + k - 2];
@@ -294,7 +311,7 @@ struct WaveRows {
         }
       }
       if (ok[nb]) {
-        if constexpr (MODE != kModeDraftGreedy) {
+        if constexpr (MODE == kModeDraftSample || MODE == kModeResidual) {
           const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
           const uint64_t key =
               stream_key(a.seed, req, (uint32_t)k, MODE == kModeResidual ? kResid : kDraft);
@@ -304,6 +321,10 @@ struct WaveRows {
         if constexpr (MODE == kModeResidual) {
           ld[nb] = a.lse[(int64_t)b * a.gamma + k - 1];
           lt[nb] = a.resid_lt[b];
+        }
+        if constexpr (MODE == kModeAlpha) {
+          ld[nb] = a.lse[(int64_t)b * a.gamma + k - 1];
+          lt[nb] = a.resid_lt[(int64_t)b * a.gamma + k - 1];   // target log-normaliser of row (b, k)
         }
       }
       if constexpr (HS == 0) {
@@ -330,7 +351,7 @@ struct WaveRows {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       uu[nb] = *reinterpret_cast<const float4*>(a.U + uoff[nb] + v0 + 4 * q);
-      if constexpr (MODE == kModeResidual)
+      if constexpr (MODE == kModeResidual || MODE == kModeAlpha)
         tt[nb] = *reinterpret_cast<const float4*>(a.T + toff[nb] + v0 + 4 * q);
       else
         tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -369,7 +390,9 @@ struct WaveRows {
       lane_merge<MODE>(st[nb], 32);
       if (q == 0 && ok[nb]) {
         const int64_t o = (int64_t)rows[nb] * a.n_vc + vc;
-        if constexpr (MODE == kModeResidual) {
+        if constexpr (MODE == kModeAlpha) {
+          a.pf[o] = make_float4(st[nb].s, 0.f, 0.f, 0.f);
+        } else if constexpr (MODE == kModeResidual) {
           a.pf[o] = make_float4(st[nb].key, st[nb].fkey, 0.f, 0.f);
           a.pi[o] = make_int2(st[nb].idx, st[nb].fidx);
         } else {
@@ -499,7 +522,7 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   constexpr int kTileBytes = kTileV * kRowBytes;
   constexpr int kW2Bytes = NT * kTileBytes;             // W2 per step
   constexpr int kW2Inst = kW2Bytes / (kWavesPerBlock * 1024);   // 1 KB per wave instruction
-  constexpr bool kResid = MODE == kModeResidual;
+  constexpr bool kResid = MODE == kModeResidual || MODE == kModeAlpha;   // target rows ride along
   constexpr int kFPR = 4 * NT;                          // float4 per U row per step
   constexpr int kRPI = 16 / NT;                         // U rows per load instruction
   constexpr int kSwzShift = 2 / NT;
@@ -526,7 +549,7 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   WR w;
   w.setup_rows(a, g * kWavesPerBlock + wid, j);
   const bool wave_active = __any(w.ok[0] || w.ok[1]);
-  if constexpr (kResid) {
+  if constexpr (MODE == kModeResidual) {
     if (!__syncthreads_or(wave_active)) return;          // uniform over the block
   }
   LaneState st[2];
@@ -737,11 +760,33 @@ __global__ __launch_bounds__(kCombineThreads) void combine_resid_impl(const Comb
   }
 }
 
+// One 256-thread workgroup per (request, position): the acceptance
+// probability of the position is the sum of its chunk partials.
+__global__ __launch_bounds__(kCombineThreads) void combine_alpha_impl(const CombineArgs a) {
+  const int b = blockIdx.x;
+  const int k = blockIdx.y + 1;
+  const int64_t base = ((int64_t)(k - 1) * a.B + b) * a.n_vc;
+  float acc = 0.0f;
+  for (int i = threadIdx.x; i < a.n_vc; i += kCombineThreads) acc += a.pf[base + i].x;
+#pragma unroll
+  for (int mask = 1; mask < 64; mask <<= 1) acc += shfl_xor(acc, mask);
+  __shared__ float red[kCombineThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kCombineThreads / 64; ++w) tot += red[w];
+    a.lse[(int64_t)b * a.gamma + k - 1] = tot;      // the alpha output
+  }
+}
+
 template <int R, int D, int NT, int HS>
 const void* shared_for(int mode) {
   if (mode == kModeDraftGreedy) return (const void*)&sweep_shared_impl<R, kModeDraftGreedy, D, NT, HS>;
   if (mode == kModeDraftSample) return (const void*)&sweep_shared_impl<R, kModeDraftSample, D, NT, HS>;
   if (mode == kModeResidual) return (const void*)&sweep_shared_impl<R, kModeResidual, D, NT, HS>;
+  if (mode == kModeAlpha) return (const void*)&sweep_shared_impl<R, kModeAlpha, D, NT, HS>;
   return nullptr;
 }
 
@@ -770,6 +815,7 @@ const void* private_for(int mode) {
   if (mode == kModeDraftGreedy) return (const void*)&sweep_private_impl<WT, R, kModeDraftGreedy, HS>;
   if (mode == kModeDraftSample) return (const void*)&sweep_private_impl<WT, R, kModeDraftSample, HS>;
   if (mode == kModeResidual) return (const void*)&sweep_private_impl<WT, R, kModeResidual, HS>;
+  if (mode == kModeAlpha) return (const void*)&sweep_private_impl<WT, R, kModeAlpha, HS>;
   return nullptr;
 }
 
@@ -798,5 +844,6 @@ const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs)
 
 const void* combine_draft_kernel() { return (const void*)&combine_draft_impl; }
 const void* combine_resid_kernel() { return (const void*)&combine_resid_impl; }
+const void* combine_alpha_kernel() { return (const void*)&combine_alpha_impl; }
 
 }  // namespace dspark

@@ -256,8 +256,24 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
   }
 }
 
+// Diagnostic pass: the log-normaliser of every target row 1..gamma from its
+// chunk partials (one wave per row).
+__global__ __launch_bounds__(64) void rows_lse_impl(const VerifyArgs a) {
+  const int b = blockIdx.x;
+  const int k = blockIdx.y + 1;
+  const int64_t base = ((int64_t)b * (a.gamma + 1) + (k - 1)) * a.n_chunks;
+  RowState st{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+  for (int c = threadIdx.x; c < a.n_chunks; c += 64) {
+    const float4 q = a.pf[base + c];
+    row_merge(st, RowState{q.x, q.y, q.z, a.pi[base + c]});
+  }
+  wave_row_reduce(st);
+  if (threadIdx.x == 0) a.row_lse[(int64_t)b * a.gamma + k - 1] = (st.m + fast_log2(st.s)) * kLn2;
+}
+
 }  // namespace
 
+const void* rows_lse_kernel() { return (const void*)&rows_lse_impl; }
 const void* verify_rows_kernel() { return (const void*)&verify_rows_impl; }
 const void* verify_decide_kernel() { return (const void*)&verify_decide_impl; }
 

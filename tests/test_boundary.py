@@ -62,6 +62,8 @@ def test_null_context_is_rejected_everywhere():
                              None, None, None, None, None, None, None, 0.0, 0, None, None) == dk.DSPARK_EINVAL
     assert lib.dspark_verify_packed(None, None, 1, 1, 16, 32, 1, None, 16, None, 1, None, 16, 16, None, None,
                                     None, None, None, None, None, None, None, 0.0, 0, None, None) == dk.DSPARK_EINVAL
+    assert lib.dspark_accept_prob(None, None, 1, 1, 16, 32, 1, None, 16, 16, None, 16, 16, None, None, None,
+                                  None, None, None, 1.0, None) == dk.DSPARK_EINVAL
     assert lib.dspark_draft_rnn(None, None, 1, 1, 16, 32, 1, None, 16, 16, None, None, None, None, None,
                                 None, None, None, 0.0, 0, None, None, None, None) == dk.DSPARK_EINVAL
 

@@ -178,3 +178,38 @@ def test_bonus_uses_row_after_last_verified():
                                     oracle.row_key(5, int(inp["req_ids"][b]) & 0xFFFFFFFF, 3, oracle.BONUS))
         assert r.out_tokens[b, 2] == bonus
         assert np.all(r.out_tokens[b, 3:] == -1)
+
+
+def test_accept_prob_is_one_minus_total_variation_and_matches_acceptance():
+    """alpha = sum min(p_d, p_t) = 1 - TV (closed form on the rebuilt laws) and is the
+    empirical first-position acceptance rate of the oracle's own sampler."""
+    V, gamma, n, T = 3, 2, 30000, 1.0
+    U, tgt, W1, W2, d, r = _mc_run(5, n, T, V, gamma)
+    a = oracle.accept_prob(tgt.repeat(2, 1, 1), d.tokens[:2], d.lse[:2], U.repeat(2, 1, 1), W1, W2,
+                           np.full(2, 1), T, gamma)
+    pd1 = _pd(U, W1, W2, 1, 1, T)
+    pt1 = softmax(tgt[0, 0].double().numpy() / T)
+    assert abs(a[0, 0] - (1 - 0.5 * np.abs(pd1 - pt1).sum())) < 1e-12
+    emp = np.mean(r.accept_len >= 1)
+    assert abs(emp - a[0, 0]) < 5 * np.sqrt(a[0, 0] * (1 - a[0, 0]) / n)
+    # position 2 given x_1: the same identity with the conditional draft law
+    for i in range(2):
+        pd2 = _pd(U, W1, W2, 2, int(d.tokens[i, 0]), T)
+        pt2 = softmax(tgt[0, 1].double().numpy() / T)
+        assert abs(a[i, 1] - np.minimum(pd2, pt2).sum()) < 1e-12
+
+
+def test_accept_prob_limits():
+    wl = synth.WORKLOADS["sample"].with_(B=4, V=300, conf=False)
+    inp = synth.make_inputs(wl)
+    W = torch.zeros_like(inp["W1"])
+    d = oracle.draft_markov(inp["U"], W, W, inp["anchor"], inp["req_ids"], 1.0, 5, 7)
+    same = oracle.accept_prob(inp["U"], d.tokens, d.lse, inp["U"], W, W, inp["anchor"], 1.0, 7)
+    assert np.allclose(same, 1.0, atol=1e-12)          # identical laws: always accepted
+    far = inp["U"].clone()
+    far[:, :, :150] -= 60.0                           # target mass on the upper half only
+    U2 = inp["U"].clone()
+    U2[:, :, 150:] -= 60.0                            # draft mass on the lower half only
+    d2 = oracle.draft_markov(U2, W, W, inp["anchor"], inp["req_ids"], 1.0, 5, 7)
+    tiny = oracle.accept_prob(far, d2.tokens, d2.lse, U2, W, W, inp["anchor"], 1.0, 7)
+    assert np.all(tiny < 1e-20)
