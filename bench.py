@@ -38,6 +38,9 @@ def parse():
                     help="repeat the CPU oracle step (new seed each pass) until this much time has passed")
     ap.add_argument("--cpu-max-passes", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-diag", action="store_true",
+                    help="skip timing the acceptance-probability diagnostic pass")
+    ap.add_argument("--diag-calls", type=int, default=10)
     ap.add_argument("--no-timing-pass", action="store_true",
                     help="skip the per-kernel event pass (used under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -247,6 +250,39 @@ def main():
         print(f"[bench] kernels: " + ", ".join(f"{k} {v['avg_us']:.1f}us x{v['launches_per_step']:.0f}"
                                              for k, v in per_kernel.items()), file=sys.stderr, flush=True)
 
+    # ---- diagnostic pass (outside the step): acceptance probability of
+    #      every drafted position of the last step, sum_v min(p_d, p_t) ----
+    diag = None
+    if T > 0 and not args.no_diag:
+        alpha = torch.empty((B, G), dtype=torch.float32, device=dev)
+
+        def diag_call():
+            ctx.accept_prob(d["target"], d["U"], d["W1"], d["W2"], d["anchor"], tok, lse, T, states=states,
+                            out=alpha)
+
+        diag_call()
+        ctx.check()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.diag_calls):
+            diag_call()
+        g1.record()
+        torch.cuda.synchronize()
+        ctx.check()
+        us = g0.elapsed_time(g1) * 1e3 / args.diag_calls
+        wb = 2 if d["W2"].dtype == torch.bfloat16 else 4
+        # per position: the target row twice (its log-normaliser must be known
+        # before the min can be taken), U, W2 and the bias vectors
+        db = G * (8.0 * B * V + sweep_bytes(B, V, r, wb, 4 if gru is not None else None))
+        diag = {"kernel": "dspark_accept_prob (target rows + log-normalisers + gamma alpha sweeps + combine)",
+                "us_per_call": round(us, 2), "positions_per_s": round(B * G / (us * 1e-6), 1),
+                "alg_bytes_per_call": db, "alg_GBps": round(db / (us * 1e-6) / 1e9, 1),
+                "frac_hbm": round(db / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                "mean_alpha_per_position": [round(float(x), 4) for x in alpha.mean(0).cpu()]}
+        print(f"[bench] accept_prob: {us:.1f} us/call, {diag['alg_GBps']} GB/s", file=sys.stderr, flush=True)
+
     # step-level algorithmic bytes (what one step must move at least)
     wbytes = 2 if d["W1"].dtype == torch.bfloat16 else 4
     n_rej_all = float((A < Ks).sum().item()) / args.steps
@@ -299,6 +335,7 @@ def main():
         "accepted_per_step": float(A.sum().item()) / args.steps,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "accept_prob": diag,
         "per_kernel": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                        for k, v in per_kernel.items()},
         "ms_per_step_event_pass": None if ms_per_step_timed_pass is None else round(ms_per_step_timed_pass, 4),
