@@ -82,6 +82,11 @@ struct LaneState {
   float zb;         // z at the best key (sampling draft)
   float fkey;       // residual: fallback key (draw from p_t)
   int fidx;
+  // draft modes, during the range: the leading group (first entry g, its
+  // four z values) and, sampling, its mass relative to 2^m and its E
+  int g;
+  float zg[4];
+  float sb, eb;
 };
 
 __device__ __forceinline__ void lane_init(LaneState& st) {
@@ -92,51 +97,110 @@ __device__ __forceinline__ void lane_init(LaneState& st) {
   st.zb = 0.0f;
   st.fkey = -INFINITY;
   st.fidx = 0x7fffffff;
+  st.g = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.zg[i] = 0.0f;
+  st.sb = 0.0f;
+  st.eb = 1.0f;
 }
 
-// Fold four z values (vocabulary v0..v0+3 of one request, one race group;
-// z = U + bias came out of the MFMA, whose accumulator was initialised with
-// U) into the state.
+// Draft modes: fold the NTL tiles of one step (per lane and request row,
+// NTL groups of four consecutive vocabulary entries, z = U + bias straight
+// from the MFMA, whose accumulator was initialised with U) into the state:
+// one max and one rescale per row and step for the online log-sum-exp, and
+// the leading group of the range so far, tracked without branches (with 64
+// lanes per wave some lane nearly always finds a new leader, so a branch
+// would be taken on almost every step).  Only the leading group's four z
+// values are kept; the entry within it is resolved once, at the end of the
+// range (resolve_draft).
 //
-// Sampling draws by the group race (common.hpp): the group's mass relative
-// to the running max is the softmax term already at hand, so a group costs
-// one hash, one log and a compare; the exact key and the member choice are
-// formed only for the rare groups that beat the running best.
+// Greedy: the group with the largest z (first such group on ties).
+// Sampling, the group race (common.hpp): group g of mass S_g relative to 2^m
+// leads while S_g / E_g is the largest, compared as S_g E_b > E_g S_b with
+// the leader's S_b rescaled together with the running max (so no log is
+// taken per group, only E_g = -log2 u).
+template <int MODE, int NTL>
+__device__ __forceinline__ void fold_draft(LaneState& st, const f32x4_t (&z)[NTL], int v0, uint32_t klo,
+                                           uint32_t khi, float s2) {
+  float zt[NTL];
+#pragma unroll
+  for (int h = 0; h < NTL; ++h) zt[h] = fmaxf(fmaxf(z[h][0], z[h][1]), fmaxf(z[h][2], z[h][3]));
+  float zmax = zt[0];
+#pragma unroll
+  for (int h = 1; h < NTL; ++h) zmax = fmaxf(zmax, zt[h]);
+  const float mn = fmaxf(st.m, zmax * s2);
+  float S[NTL];
+  float tot = 0.0f;
+#pragma unroll
+  for (int h = 0; h < NTL; ++h) {
+    float e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = fast_exp2(__builtin_fmaf(z[h][i], s2, -mn));
+    S[h] = (e[0] + e[1]) + (e[2] + e[3]);
+    tot += S[h];
+  }
+  const float resc = fast_exp2(st.m - mn);
+  st.s = __builtin_fmaf(st.s, resc, tot);
+  st.m = mn;
+  if constexpr (MODE == kModeDraftGreedy) {
+#pragma unroll
+    for (int h = 0; h < NTL; ++h) {
+      const bool lead = zt[h] > st.key;
+      st.key = lead ? zt[h] : st.key;
+      st.g = lead ? v0 + kTileV * h : st.g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.zg[i] = lead ? z[h][i] : st.zg[i];
+    }
+  } else {
+    st.sb *= resc;
+#pragma unroll
+    for (int h = 0; h < NTL; ++h) {
+      const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + kTileV * h))));
+      const bool lead = S[h] * st.eb > E * st.sb;
+      st.sb = lead ? S[h] : st.sb;
+      st.eb = lead ? E : st.eb;
+      st.g = lead ? v0 + kTileV * h : st.g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.zg[i] = lead ? z[h][i] : st.zg[i];
+    }
+  }
+}
+
+// End of a range: turn the leading group into (key, idx, zb).  Greedy: the
+// lowest entry holding the maximum.  Sampling: the key log2 S_b + m - log2 E_b
+// and the entry drawn within the group by inverting its CDF at u(g + 1) (the
+// weights exp2(z s2) relative to the group's own maximum).
+template <int MODE>
+__device__ __forceinline__ void resolve_draft(LaneState& st, uint32_t klo, uint32_t khi, float s2) {
+  if (st.g < 0) return;                                  // empty range
+  if constexpr (MODE == kModeDraftGreedy) {
+    int i = 3;
+#pragma unroll
+    for (int k = 2; k >= 0; --k) i = (st.zg[k] == st.key) ? k : i;
+    st.idx = st.g + i;
+    st.zb = st.key;
+  } else {
+    const float zm = fmaxf(fmaxf(st.zg[0], st.zg[1]), fmaxf(st.zg[2], st.zg[3]));
+    float e[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e[k] = fast_exp2((st.zg[k] - zm) * s2);
+    const float S = (e[0] + e[1]) + (e[2] + e[3]);
+    const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(st.g + 1))) * S;
+    const int i = group_pick(c, e[0], e[1], e[2], e[3]);
+    st.key = fast_log2(st.sb) + st.m - fast_log2(st.eb);
+    st.idx = st.g + i;
+    // selects rather than an indexed read (which would put the state in scratch)
+    st.zb = i == 0 ? st.zg[0] : (i == 1 ? st.zg[1] : (i == 2 ? st.zg[2] : st.zg[3]));
+  }
+}
+
+// Residual and acceptance-probability modes: fold four values (one race
+// group) of z = U + bias and of the target row into the state.
 template <int MODE>
 __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const float4 t, int v0,
                                          uint32_t klo, uint32_t khi, float invT, float s2, float ld,
                                          float lt) {
-  if constexpr (MODE == kModeDraftGreedy || MODE == kModeDraftSample) {
-    const float zt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    const float mn = fmaxf(st.m, zt * s2);
-    float e[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = fast_exp2(__builtin_fmaf(z[i], s2, -mn));
-    const float S = (e[0] + e[1]) + (e[2] + e[3]);
-    st.s = st.s * fast_exp2(st.m - mn) + S;
-    st.m = mn;
-    if constexpr (MODE == kModeDraftGreedy) {
-      if (zt > st.key) {
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          if (z[i] == zt) st.idx = v0 + i;   // lowest index of the group maximum
-        }
-        st.key = zt;
-      }
-    } else {
-      const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)v0)));
-      if (E < S * fast_exp2(mn - st.key)) {
-        const float key = fast_log2(S) + mn - fast_log2(E);
-        if (key > st.key) {
-          const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + 1))) * S;
-          const int i = group_pick(c, e[0], e[1], e[2], e[3]);
-          st.key = key;
-          st.idx = v0 + i;
-          st.zb = z[i];
-        }
-      }
-    }
-  } else if constexpr (MODE == kModeAlpha) {
+  if constexpr (MODE == kModeAlpha) {
     // acceptance probability: sum over v of min(p_t(v), p_d(v))
     const float tv[4] = {t.x, t.y, t.z, t.w};
     float acc = 0.0f;
@@ -358,11 +422,8 @@ struct WaveRows {
     }
   }
 
-  // z = U + bias for both blocks (U initialises the accumulators), then fold.
-  __device__ __forceinline__ void compute(const SweepArgs& a, LaneState (&st)[2], int t, int q,
-                                          const FragT (&A)[NS], const float4 (&uu)[2],
-                                          const float4 (&tt)[2]) const {
-    f32x4_t acc[2];
+  // z = U + bias of one tile for both blocks (U initialises the accumulators).
+  __device__ __forceinline__ void mma_tile(f32x4_t (&acc)[2], const FragT (&A)[NS], const float4 (&uu)[2]) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) acc[nb] = f32x4_t{uu[nb].x, uu[nb].y, uu[nb].z, uu[nb].w};
 #pragma unroll
@@ -377,15 +438,42 @@ struct WaveRows {
         for (int nb = 0; nb < 2; ++nb) acc[nb] = F::mma(A[s], Hlo[nb][s], acc[nb]);
       }
     }
-    const int vb = t * kTileV + 4 * q;
+  }
+
+  // Draft modes: fold NTL consecutive tiles (acc[h][nb], tile t + h).
+  template <int NTL>
+  __device__ __forceinline__ void fold(const SweepArgs& a, LaneState (&st)[2], const f32x4_t (&acc)[NTL][2], int t,
+                                       int q) const {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      epilogue<MODE>(st[nb], acc[nb], tt[nb], vb, klo[nb], khi[nb], a.invT, a.s2, ld[nb], lt[nb]);
+    for (int nb = 0; nb < 2; ++nb) {
+      f32x4_t z[NTL];
+#pragma unroll
+      for (int h = 0; h < NTL; ++h) z[h] = acc[h][nb];
+      fold_draft<MODE, NTL>(st[nb], z, t * kTileV + 4 * q, klo[nb], khi[nb], a.s2);
+    }
+  }
+
+  // One tile: z = U + bias, then fold.
+  __device__ __forceinline__ void compute(const SweepArgs& a, LaneState (&st)[2], int t, int q,
+                                          const FragT (&A)[NS], const float4 (&uu)[2],
+                                          const float4 (&tt)[2]) const {
+    f32x4_t acc[1][2];
+    mma_tile(acc[0], A, uu);
+    if constexpr (MODE == kModeDraftGreedy || MODE == kModeDraftSample) {
+      fold<1>(a, st, acc, t, q);
+    } else {
+      const int vb = t * kTileV + 4 * q;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        epilogue<MODE>(st[nb], acc[0][nb], tt[nb], vb, klo[nb], khi[nb], a.invT, a.s2, ld[nb], lt[nb]);
+    }
   }
 
   __device__ __forceinline__ void finish(const SweepArgs& a, LaneState (&st)[2], int q, int vc) const {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
+      if constexpr (MODE == kModeDraftGreedy || MODE == kModeDraftSample)
+        resolve_draft<MODE>(st[nb], klo[nb], khi[nb], a.s2);
       lane_merge<MODE>(st[nb], 16);
       lane_merge<MODE>(st[nb], 32);
       if (q == 0 && ok[nb]) {
@@ -606,26 +694,47 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
       for (int m = 0; m < kUInst; ++m) dma16(a.T + toff_d[m] + vcol[m], base + t_lds + m * 1024);
     }
   };
+  // operands of tile h of the step in slot sl
+  auto load_tile = [&](int h, const unsigned char* sl, FragT (&A)[NS], float4 (&uu)[2], float4 (&tt)[2]) {
+    const unsigned char* row = sl + (h * kTileV + j) * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) A[s] = *reinterpret_cast<const FragT*>(row + (((4 * s + q) ^ j) * 16));
+    const int col = (4 * h + q) ^ ((j >> kSwzShift) & (kFPR - 1));
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int off = wid * kWaveRowBytes + ((nb * 16 + j) * kFPR + col) * 16;
+      uu[nb] = *reinterpret_cast<const float4*>(sl + kUOff + off);
+      if constexpr (kResid)
+        tt[nb] = *reinterpret_cast<const float4*>(sl + kTOff + off);
+      else
+        tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
   auto compute = [&](int t, const unsigned char* sl) {
-#pragma unroll
-    for (int h = 0; h < NT; ++h) {
-      if (t + h >= t1) break;                            // uniform over the block
+    if constexpr (!kResid && NT == 2) {
+      // draft: both tiles through the MFMA, then one fold for the step
+      f32x4_t acc[NT][2];
       FragT A[NS];
-      const unsigned char* row = sl + (h * kTileV + j) * kRowBytes;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) A[s] = *reinterpret_cast<const FragT*>(row + (((4 * s + q) ^ j) * 16));
       float4 uu[2], tt[2];
-      const int col = (4 * h + q) ^ ((j >> kSwzShift) & (kFPR - 1));
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int off = wid * kWaveRowBytes + ((nb * 16 + j) * kFPR + col) * 16;
-        uu[nb] = *reinterpret_cast<const float4*>(sl + kUOff + off);
-        if constexpr (kResid)
-          tt[nb] = *reinterpret_cast<const float4*>(sl + kTOff + off);
-        else
-          tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
+      load_tile(0, sl, A, uu, tt);
+      w.mma_tile(acc[0], A, uu);
+      if (t + 1 < t1) {                                  // uniform over the block
+        load_tile(1, sl, A, uu, tt);
+        w.mma_tile(acc[1], A, uu);
+        w.template fold<2>(a, st, acc, t, q);
+      } else {
+        const f32x4_t acc1[1][2] = {{acc[0][0], acc[0][1]}};
+        w.template fold<1>(a, st, acc1, t, q);
       }
-      w.compute(a, st, t + h, q, A, uu, tt);
+    } else {
+#pragma unroll
+      for (int h = 0; h < NT; ++h) {
+        if (t + h >= t1) break;                          // uniform over the block
+        FragT A[NS];
+        float4 uu[2], tt[2];
+        load_tile(h, sl, A, uu, tt);
+        w.compute(a, st, t + h, q, A, uu, tt);
+      }
     }
   };
 
