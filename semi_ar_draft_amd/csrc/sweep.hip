@@ -337,6 +337,33 @@ struct WaveRows {
   // maximum over the previous position's slot groups: the four lanes of a
   // row (q = 0..3) read a quarter of the groups each and share the maximum.
   __device__ __forceinline__ void setup_rest(const SweepArgs& a, int q) {
+    // loads that do not depend on the previous token go out first (the
+    // error-flag atomic below would otherwise keep them behind the chain)
+    uint32_t req[2] = {0u, 0u};
+    int given[2] = {0, 0};                               // anchor, or the drafted previous token
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int b = rows[nb];
+      const int k = kk[nb];
+      ld[nb] = lt[nb] = 0.0f;
+      if (ok[nb]) {
+        if constexpr (MODE == kModeDraftSample || MODE == kModeResidual) req[nb] = a.req ? a.req[b] : (uint32_t)b;
+        if (HS == 0) {
+          if (k == 1)
+            given[nb] = a.anchor[b];
+          else if (MODE == kModeResidual || MODE == kModeAlpha || !a.best_prev)
+            given[nb] = a.tokens[(int64_t)b * a.gamma + k - 2];
+        }
+        if constexpr (MODE == kModeResidual) {
+          ld[nb] = a.lse[(int64_t)b * a.gamma + k - 1];
+          lt[nb] = a.resid_lt[b];
+        }
+        if constexpr (MODE == kModeAlpha) {
+          ld[nb] = a.lse[(int64_t)b * a.gamma + k - 1];
+          lt[nb] = a.resid_lt[(int64_t)b * a.gamma + k - 1];   // target log-normaliser of row (b, k)
+        }
+      }
+    }
     unsigned long long pb[2] = {0ull, 0ull};
     if (HS == 0 && MODE != kModeResidual && MODE != kModeAlpha && a.best_prev) {
 #pragma unroll
@@ -361,14 +388,11 @@ struct WaveRows {
       const int k = kk[nb];
       int prev = 0;
       klo[nb] = khi[nb] = 0;
-      ld[nb] = lt[nb] = 0.0f;
       if (ok[nb] && HS == 0) {
-        if (k == 1)
-          prev = a.anchor[b];
-        else if (MODE != kModeResidual && MODE != kModeAlpha && a.best_prev)
+        if (k != 1 && MODE != kModeResidual && MODE != kModeAlpha && a.best_prev)
           prev = best_index(pb[nb]);
         else
-          prev = a.tokens[(int64_t)b * a.gamma + k - 2];
+          prev = given[nb];
         if ((unsigned)prev >= (unsigned)a.V) {
           atomicOr(a.err, kErrToken);
           prev = 0;
@@ -376,22 +400,32 @@ struct WaveRows {
       }
       if (ok[nb]) {
         if constexpr (MODE == kModeDraftSample || MODE == kModeResidual) {
-          const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
           const uint64_t key =
-              stream_key(a.seed, req, (uint32_t)k, MODE == kModeResidual ? kResid : kDraft);
+              stream_key(a.seed, req[nb], (uint32_t)k, MODE == kModeResidual ? kResid : kDraft);
           klo[nb] = (uint32_t)key;
           khi[nb] = (uint32_t)(key >> 32);
         }
-        if constexpr (MODE == kModeResidual) {
-          ld[nb] = a.lse[(int64_t)b * a.gamma + k - 1];
-          lt[nb] = a.resid_lt[b];
-        }
-        if constexpr (MODE == kModeAlpha) {
-          ld[nb] = a.lse[(int64_t)b * a.gamma + k - 1];
-          lt[nb] = a.resid_lt[(int64_t)b * a.gamma + k - 1];   // target log-normaliser of row (b, k)
-        }
       }
-      if constexpr (HS == 0) {
+      if constexpr (HS == 0 && sizeof(FragT) == 16) {
+        // bf16: the B fragment of lane (j, q) at step s is 16 bytes of row j;
+        // loaded directly, every quarter-wave would touch 16 rows.  Instead
+        // lane L loads that part of row L / 4 which lane (L / 4, L % 4)
+        // needs (a quarter-wave reads 4 rows x 64 contiguous bytes), and a
+        // lane transpose (ds_bpermute) hands it over: lane (j, q) takes lane
+        // 4 j + q's word.
+        const int lane = threadIdx.x & 63;               // = 16 q + j
+        const int src_prev = __shfl(prev, lane >> 2, 64);
+        const WT* w1row = static_cast<const WT*>(a.W1) + (int64_t)src_prev * R;
+        const int from = 4 * (4 * (lane & 15) + q);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          union { FragT f; int w[4]; } x, y;
+          x.f = F::load(w1row, s, lane & 3);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) y.w[d] = __builtin_amdgcn_ds_bpermute(from, x.w[d]);
+          H[nb][s] = y.f;
+        }
+      } else if constexpr (HS == 0) {
         const WT* w1row = static_cast<const WT*>(a.W1) + (int64_t)prev * R;
 #pragma unroll
         for (int s = 0; s < NS; ++s) H[nb][s] = F::load(w1row, s, q);
