@@ -91,8 +91,8 @@ int dspark_check(dspark_ctx* ctx, hipStream_t stream);
 enum {
   DSPARK_K_DRAFT_SWEEP = 0,    /* MFMA bias + vocabulary sweep of one position */
   DSPARK_K_DRAFT_COMBINE = 1,  /* cross-chunk merge of one position */
-  DSPARK_K_CONFIDENCE = 2,
-  DSPARK_K_SURVIVAL = 3,
+  DSPARK_K_CONFIDENCE = 2,     /* confidences and survival products (one launch) */
+  DSPARK_K_SURVIVAL = 3,       /* kept for numbering; nothing is launched in it */
   DSPARK_K_SCHEDULE = 4,
   DSPARK_K_VERIFY_ROWS = 5,    /* streaming pass over target rows */
   DSPARK_K_VERIFY_DECIDE = 6,  /* per-request merge of its rows + accept tests */

@@ -19,7 +19,6 @@ using namespace dspark;
 namespace {
 
 constexpr int kVersion = 100;
-constexpr int kMaxGamma = 32;
 
 struct KernelNode {
   int cls;
@@ -931,9 +930,8 @@ int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V
   a.surv = surv;
   a.err = c->dev_err;
   int rc;
-  if ((rc = klaunch(c, DSPARK_K_CONFIDENCE, confidence_kernel(), dim3(B * gamma), dim3(256), &a, stream))) return rc;
-  if ((rc = klaunch(c, DSPARK_K_SURVIVAL, survival_kernel(), dim3((B + 255) / 256), dim3(256), &a, stream))) return rc;
-  return DSPARK_OK;
+  // confidences and survival products in one launch, a workgroup per request
+  return klaunch(c, DSPARK_K_CONFIDENCE, confidence_kernel(), dim3(B), dim3(1024), &a, stream);
 }
 
 int dspark_schedule(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv,

@@ -102,6 +102,8 @@ struct VerifyArgs {
   int32_t* err;
 };
 
+constexpr int kMaxGamma = 32;   // longest draft (positions per request)
+
 struct ConfArgs {
   int B, gamma, V, dh, de;
   const uint16_t* h;
@@ -159,7 +161,6 @@ const void* verify_decide_kernel();
 const void* confidence_kernel();
 const void* gru_init_kernel();
 const void* gru_step_kernel(int r);
-const void* survival_kernel();
 const void* schedule_kernel(int async);
 
 constexpr int kSchedMaxKeys = 8192;
