@@ -62,7 +62,9 @@ int dspark_version(void);
 
 /* Create a context bound to HIP device `device`.  It owns a growable device
  * workspace (cross-block partial results, scheduler scratch), a cache of
- * instantiated HIP graphs for the draft loop, and a device error flag.
+ * instantiated HIP graphs for the draft loop (used when the environment sets
+ * DSPARK_GRAPH=1; by default the loop is launched kernel by kernel, which
+ * leaves no idle gap after the loop), and a device error flag.
  * Returns DSPARK_EINVAL for a null `out`, DSPARK_EHIP if the device cannot be
  * used.  On failure *out is set to NULL. */
 int dspark_create(dspark_ctx** out, int device);

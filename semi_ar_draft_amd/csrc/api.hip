@@ -47,7 +47,7 @@ struct dspark_ctx {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   int32_t* dev_err = nullptr;
-  bool use_graph = true;
+  bool use_graph = false;
   int sweep_waves_per_cu = 8;     // occupancy target of the vocabulary sweeps
   // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
   int draft_nt = 2, draft_depth = 1;
@@ -750,8 +750,12 @@ int dspark_create(dspark_ctx** out, int device) {
     delete c;
     return DSPARK_EHIP;
   }
+  // The draft loop goes kernel by kernel by default: on this runtime a
+  // stream operation after a graph launch starts ~9 us after the graph's
+  // last kernel, more than the graph saves on eight launches of 8-30 us.
+  // DSPARK_GRAPH=1 runs it through a cached graph instead.
   const char* g = getenv("DSPARK_GRAPH");
-  if (g && g[0] == '0') c->use_graph = false;
+  if (g && g[0] == '1') c->use_graph = true;
   // tuning knob: target resident waves per CU for the vocabulary sweeps
   const char* w = getenv("DSPARK_SWEEP_WAVES_PER_CU");
   if (w) {

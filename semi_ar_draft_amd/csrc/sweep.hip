@@ -87,6 +87,11 @@ struct LaneState {
   int g;
   float zg[4];
   float sb, eb;
+  // residual, the fallback race on p_t: leading group, its four p_t values,
+  // its mass and its E (the race on max(0, p_t - p_d) uses g, zg, sb, eb)
+  int gf;
+  float zf[4];
+  float pb, ebf;
 };
 
 __device__ __forceinline__ void lane_init(LaneState& st) {
@@ -102,6 +107,11 @@ __device__ __forceinline__ void lane_init(LaneState& st) {
   for (int i = 0; i < 4; ++i) st.zg[i] = 0.0f;
   st.sb = 0.0f;
   st.eb = 1.0f;
+  st.gf = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.zf[i] = 0.0f;
+  st.pb = 0.0f;
+  st.ebf = 1.0f;
 }
 
 // Draft modes: fold the NTL tiles of one step (per lane and request row,
@@ -214,7 +224,9 @@ __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const f
   } else {
     // residual: weights r_v = max(0, p_t - p_d) with mass R; the fallback
     // (empty residual) draws from p_t with mass P, sharing the group's
-    // uniforms.  Keys log2 R - log2 E and log2 P - log2 E.
+    // uniforms.  Both races track their leading group without branches
+    // (R E_b > E R_b; the probabilities need no running rescale); the keys
+    // and the entries within the groups are resolved at the end of the range.
     const float tv[4] = {t.x, t.y, t.z, t.w};
     float pt[4], r[4];
 #pragma unroll
@@ -226,26 +238,34 @@ __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const f
     const float R = (r[0] + r[1]) + (r[2] + r[3]);
     const float P = (pt[0] + pt[1]) + (pt[2] + pt[3]);
     const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)v0)));
-    const bool cr = R > 0.0f && R > E * fast_exp2(st.key);
-    const bool cf = P > E * fast_exp2(st.fkey);
-    if (cr || cf) {
-      const float lE = fast_log2(E);
-      const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + 1)));
-      if (cr) {
-        const float key = fast_log2(R) - lE;
-        if (key > st.key) {
-          st.key = key;
-          st.idx = v0 + group_pick(c * R, r[0], r[1], r[2], r[3]);
-        }
-      }
-      if (cf) {
-        const float fkey = fast_log2(P) - lE;
-        if (fkey > st.fkey) {
-          st.fkey = fkey;
-          st.fidx = v0 + group_pick(c * P, pt[0], pt[1], pt[2], pt[3]);
-        }
-      }
+    const bool lr = R * st.eb > E * st.sb;
+    st.sb = lr ? R : st.sb;
+    st.eb = lr ? E : st.eb;
+    st.g = lr ? v0 : st.g;
+    const bool lf = P * st.ebf > E * st.pb;
+    st.pb = lf ? P : st.pb;
+    st.ebf = lf ? E : st.ebf;
+    st.gf = lf ? v0 : st.gf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      st.zg[i] = lr ? r[i] : st.zg[i];
+      st.zf[i] = lf ? pt[i] : st.zf[i];
     }
+  }
+}
+
+// End of a residual range: the keys log2 R_b - log2 E_b (and for p_t) and the
+// entries drawn within the leading groups at u(g + 1).
+__device__ __forceinline__ void resolve_resid(LaneState& st, uint32_t klo, uint32_t khi) {
+  if (st.g >= 0) {
+    const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(st.g + 1))) * st.sb;
+    st.key = fast_log2(st.sb) - fast_log2(st.eb);
+    st.idx = st.g + group_pick(c, st.zg[0], st.zg[1], st.zg[2], st.zg[3]);
+  }
+  if (st.gf >= 0) {
+    const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(st.gf + 1))) * st.pb;
+    st.fkey = fast_log2(st.pb) - fast_log2(st.ebf);
+    st.fidx = st.gf + group_pick(c, st.zf[0], st.zf[1], st.zf[2], st.zf[3]);
   }
 }
 
@@ -508,6 +528,8 @@ struct WaveRows {
     for (int nb = 0; nb < 2; ++nb) {
       if constexpr (MODE == kModeDraftGreedy || MODE == kModeDraftSample)
         resolve_draft<MODE>(st[nb], klo[nb], khi[nb], a.s2);
+      else if constexpr (MODE == kModeResidual)
+        resolve_resid(st[nb], klo[nb], khi[nb]);
       lane_merge<MODE>(st[nb], 16);
       lane_merge<MODE>(st[nb], 32);
       if (q == 0 && ok[nb]) {

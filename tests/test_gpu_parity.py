@@ -253,7 +253,7 @@ def test_full_sched_shape_sampled(ctx):
 def test_graph_and_direct_launch_agree(ctx, full_sample):
     _, d = full_sample
     a = gpu_step(ctx, d, seed=7)
-    os.environ["DSPARK_GRAPH"] = "0"
+    os.environ["DSPARK_GRAPH"] = "1"
     try:
         c2 = dk.Context(0)
     finally:
