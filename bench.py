@@ -220,6 +220,39 @@ def main():
         # dominant kernel: the draft sweep (gamma launches per step)
         sw = per_kernel["draft_sweep"]
         b_sweep = sweep_bytes(B, V, r, wbytes, 4 if gru is not None else None)
+        # sw["avg_us"]: the library's timing events, attached to each dispatch
+        # (hipExtLaunchKernel), bracket the kernel's execution alone.
+        sweep_timing = "library timing events attached to each sweep dispatch, averaged over the timed steps"
+        if gru is None and G >= 3:
+            # Cross-check, and the cost per launch inside the chain: draft
+            # calls of gamma and of gamma' < gamma positions back to back, one
+            # event pair per batch; the difference over gamma - gamma' is one
+            # sweep plus the dispatch gap before it (the combine cancels).
+            # gamma' >= 3 keeps the calls GPU-bound.
+            g2 = max(3, G // 2)
+            o2 = (torch.empty((B, g2), dtype=torch.int32, device=dev),
+                  torch.empty((B, g2), dtype=torch.float32, device=dev),
+                  torch.empty((B, g2), dtype=torch.float32, device=dev))
+
+            def draft_batch(g, out, n=50):
+                for i in range(3):
+                    ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, 7000 + i, g, out=out)
+                torch.cuda.synchronize()
+                a0 = torch.cuda.Event(enable_timing=True)
+                a1 = torch.cuda.Event(enable_timing=True)
+                a0.record()
+                for i in range(n):
+                    ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, 8000 + i, g, out=out)
+                a1.record()
+                torch.cuda.synchronize()
+                return 1e3 * a0.elapsed_time(a1) / n
+
+            if g2 < G:
+                t_full = draft_batch(G, (tok, lse, ytok))
+                t_part = draft_batch(g2, o2)
+                sw["in_chain_us"] = (t_full - t_part) / (G - g2)
+                sw["in_chain_timing"] = (f"draft calls of {G} and {g2} positions back to back, one event pair per "
+                                         f"50 calls: ({t_full:.1f} - {t_part:.1f}) us / {G - g2}")
         sw["alg_bytes"] = b_sweep
         sw["alg_GBps"] = b_sweep / (sw["avg_us"] * 1e-6) / 1e9
         sw["mfma_TFLOPs"] = 2.0 * B * r * V / (sw["avg_us"] * 1e-6) / 1e12
@@ -248,6 +281,7 @@ def main():
                     "kernel": ("draft_sweep (MFMA Markov bias + vocabulary sweep, one position)" if gru is None
                                else "draft_sweep (MFMA GRU-state bias + vocabulary sweep, one position)"),
                     "alg_bytes_per_launch": b_sweep, "avg_launch_us": round(sw["avg_us"], 2),
+                    "timing": sweep_timing,
                     "mfma_util": round(sw["mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 5)}
         print(f"[bench] kernels: " + ", ".join(f"{k} {v['avg_us']:.1f}us x{v['launches_per_step']:.0f}"
                                              for k, v in per_kernel.items()), file=sys.stderr, flush=True)

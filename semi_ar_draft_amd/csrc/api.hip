@@ -1,5 +1,6 @@
 // C ABI of libdspark: context, argument checks, workspace, launch plans and
 // the HIP-graph cache of the sequential draft loop.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -223,12 +224,13 @@ int klaunch(dspark_ctx* c, int cls, const void* fn, dim3 grid, dim3 block, void*
     DSPARK_HIP(c, launch(fn, grid, block, arg, s));
     return DSPARK_OK;
   }
+  // events attached to the dispatch itself: they bracket the kernel's
+  // execution, not the queue's stream-ordering gap before it
   hipEvent_t a, b;
   DSPARK_HIP(c, take_event(c, &a));
   DSPARK_HIP(c, take_event(c, &b));
-  DSPARK_HIP(c, hipEventRecord(a, s));
-  DSPARK_HIP(c, launch(fn, grid, block, arg, s));
-  DSPARK_HIP(c, hipEventRecord(b, s));
+  void* params[] = {arg};
+  DSPARK_HIP(c, hipExtLaunchKernel(fn, grid, block, params, 0, s, a, b, 0));
   c->pending.push_back({cls, a, b});
   return DSPARK_OK;
 }
