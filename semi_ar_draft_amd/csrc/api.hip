@@ -52,6 +52,9 @@ struct dspark_ctx {
   int sweep_waves_per_cu = 8;     // occupancy target of the vocabulary sweeps
   // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
   int draft_nt = 2, draft_depth = 1;
+  // the GRU head's sweep holds its state as hi + lo fragments: with two-tile
+  // steps it needs 268 VGPRs (one wave per SIMD), with one-tile steps 236
+  int gru_nt = 1, gru_depth = 1;
   int resid_nt = 1, resid_depth = 1;
   // verify: last target row of each window but the final one (window k covers
   // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list
@@ -383,7 +386,8 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   ca.err = c->dev_err;
 
   const int hs = gru ? 1 : 0;
-  const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, c->draft_depth, c->draft_nt, hs)
+  const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, hs ? c->gru_depth : c->draft_depth,
+                                             hs ? c->gru_nt : c->draft_nt, hs)
                               : sweep_kernel((int)wdtype, r, mode, 0, 1, hs);
   // Markov: gamma sweeps, each taking x_{k-1} from the previous position's
   // running bests.  GRU: s_0 fill, then per position the sweep (bias from
@@ -774,6 +778,7 @@ int dspark_create(dspark_ctx** out, int device) {
     depth = v[2] - '0';
   };
   ring_knob("DSPARK_DRAFT_RING", c->draft_nt, c->draft_depth);
+  ring_knob("DSPARK_GRU_RING", c->gru_nt, c->gru_depth);
   ring_knob("DSPARK_RESID_RING", c->resid_nt, c->resid_depth);
   // verify windows: "e1,e2,..." increasing last rows of all windows but the final one
   const char* vw = getenv("DSPARK_VERIFY_WINDOWS");

@@ -449,6 +449,28 @@ struct WaveRows {
         const WT* w1row = static_cast<const WT*>(a.W1) + (int64_t)prev * R;
 #pragma unroll
         for (int s = 0; s < NS; ++s) H[nb][s] = F::load(w1row, s, q);
+      } else if constexpr (sizeof(FragT) == 16) {
+        // state of position k (inactive rows: request 0, position 1), loaded
+        // like the W1 rows above: lane L reads that part of row L / 4 which
+        // lane (L / 4, L % 4) needs, splits it, and the lane transpose hands
+        // over the hi and lo fragments
+        const int lane = threadIdx.x & 63;
+        const int srow_idx = ok[nb] ? (k - 1) * a.B + b : 0;
+        const int src_row = __shfl(srow_idx, lane >> 2, 64);
+        const float* srow = a.hstate + (int64_t)src_row * R;
+        const int from = 4 * (4 * (lane & 15) + q);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          union { FragT f; int w[4]; } xh, xl, yh, yl;
+          F::split(srow, s, lane & 3, xh.f, xl.f);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            yh.w[d] = __builtin_amdgcn_ds_bpermute(from, xh.w[d]);
+            yl.w[d] = __builtin_amdgcn_ds_bpermute(from, xl.w[d]);
+          }
+          H[nb][s] = yh.f;
+          Hlo[nb][kLo ? s : 0] = yl.f;
+        }
       } else {
         // state of position k (inactive rows: request 0, position 1)
         const float* srow = a.hstate + ((int64_t)(ok[nb] ? k - 1 : 0) * a.B + (ok[nb] ? b : 0)) * R;
