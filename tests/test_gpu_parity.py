@@ -91,6 +91,12 @@ SMALL = [
     ("bf16_sample_T07_r128", "sample", dict(B=70, V=3008, r=128, temperature=0.7, d_h=32, d_e=96, sts=True)),
     ("bf16_sample_r32_gamma3", "sample", dict(B=17, gamma=3, V=2000, r=32, d_h=16, d_e=16)),
     ("bf16_sample_B1_gamma1", "sample", dict(B=1, gamma=1, V=160, d_h=8, d_e=8)),
+    # longest draft: 33 target rows per request, the confidence kernel's
+    # position loop wraps (64 half-dots over 16 waves)
+    ("bf16_sample_gamma32", "sample", dict(B=36, gamma=32, V=1040, r=64, d_h=16, d_e=24, sts=True)),
+    ("bf16_greedy_gamma32", "greedy", dict(B=20, gamma=32, V=1056, r=32, peak=None)),
+    # shared-tile sweeps (B > 64) with a long draft and a ragged last chunk
+    ("bf16_sample_shared_gamma16", "sample", dict(B=100, gamma=16, V=2064, d_h=32, d_e=32, sts=True)),
 ]
 
 
