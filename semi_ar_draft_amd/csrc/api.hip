@@ -940,7 +940,6 @@ int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V
   a.conf = conf;
   a.surv = surv;
   a.err = c->dev_err;
-  int rc;
   // confidences and survival products in one launch, a workgroup per request
   return klaunch(c, DSPARK_K_CONFIDENCE, confidence_kernel(), dim3(B), dim3(1024), &a, stream);
 }

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kConfThreads) void confidence_impl(const ConfArgs a
     if (lane == 0) part[k - 1][w & 1] = acc;
   }
   __syncthreads();
-  if (threadIdx.x < a.gamma) {
+  if ((int)threadIdx.x < a.gamma) {
     const int k = threadIdx.x + 1;
     const float l = (part[k - 1][0] + part[k - 1][1]) + a.bc;
     const float T = a.sts ? a.sts[k - 1] : 1.0f;

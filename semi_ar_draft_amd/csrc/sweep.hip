@@ -208,8 +208,7 @@ __device__ __forceinline__ void resolve_draft(LaneState& st, uint32_t klo, uint3
 // group) of z = U + bias and of the target row into the state.
 template <int MODE>
 __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const float4 t, int v0,
-                                         uint32_t klo, uint32_t khi, float invT, float s2, float ld,
-                                         float lt) {
+                                         uint32_t klo, uint32_t khi, float invT, float ld, float lt) {
   if constexpr (MODE == kModeAlpha) {
     // acceptance probability: sum over v of min(p_t(v), p_d(v))
     const float tv[4] = {t.x, t.y, t.z, t.w};
@@ -541,7 +540,7 @@ struct WaveRows {
       const int vb = t * kTileV + 4 * q;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        epilogue<MODE>(st[nb], acc[0][nb], tt[nb], vb, klo[nb], khi[nb], a.invT, a.s2, ld[nb], lt[nb]);
+        epilogue<MODE>(st[nb], acc[0][nb], tt[nb], vb, klo[nb], khi[nb], a.invT, ld[nb], lt[nb]);
     }
   }
 
