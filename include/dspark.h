@@ -84,9 +84,10 @@ const char* dspark_last_error(const dspark_ctx* ctx);
 int dspark_check(dspark_ctx* ctx, hipStream_t stream);
 
 /* Kernel timing for benchmarks (not needed for correct use).
- * While enabled, every kernel the context launches is bracketed by a pair of
- * HIP events recorded on the launch stream, and the draft loop is launched
- * kernel by kernel instead of through its graph.  dspark_timing_read waits
+ * While enabled, every kernel the context launches carries a start and a
+ * stop HIP event attached to its dispatch (they bracket the kernel's
+ * execution, not the queue's ordering gap before it), and the draft loop is
+ * launched kernel by kernel even where a graph was requested.  dspark_timing_read waits
  * for the recorded events, writes per-kernel-class totals (milliseconds) and
  * launch counts into arrays of DSPARK_K_COUNT entries, and forgets them.
  * Errors: DSPARK_EINVAL for null arguments, DSPARK_EHIP if an event fails. */
