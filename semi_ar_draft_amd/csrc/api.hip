@@ -452,6 +452,13 @@ int schedule_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, const f
   a.n_selected = n_selected;
   a.theta = theta;
   int rc;
+  // keys by rank (one or two sets of 4096), then the scan / stop / count
+  if ((rc = ensure_ws(c, 2 * 4096 * sizeof(uint64_t)))) return rc;
+  a.sorted = static_cast<uint64_t*>(c->ws);
+  const int n = B * gamma;
+  if ((rc = klaunch(c, DSPARK_K_SCHEDULE, schedule_rank_kernel(), dim3((n + 15) / 16, hist ? 2 : 1),
+                    dim3(kSchedThreads), &a, stream)))
+    return rc;
   if ((rc = klaunch(c, DSPARK_K_SCHEDULE, schedule_kernel(hist ? 1 : 0), dim3(1), dim3(kSchedThreads), &a, stream)))
     return rc;
   return DSPARK_OK;

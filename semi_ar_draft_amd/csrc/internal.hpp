@@ -126,6 +126,7 @@ struct SchedArgs {
   int32_t* K;
   int32_t* n_selected;
   double* theta;
+  uint64_t* sorted;              // [2][4096] keys by rank (set 1: current survivals, asynchronous rule)
 };
 
 // GRU head recurrence (position k: states[k] = GRU(states[k-1], W1[x_k])).
@@ -162,6 +163,7 @@ const void* confidence_kernel();
 const void* gru_init_kernel();
 const void* gru_step_kernel(int r);
 const void* schedule_kernel(int async);
+const void* schedule_rank_kernel();
 
 constexpr int kSchedMaxKeys = 8192;
 constexpr int kSchedThreads = 1024;

@@ -1,5 +1,6 @@
-// Hardware-aware prefix scheduler: greedy admission with early stop, in one
-// workgroup.
+// Hardware-aware prefix scheduler: greedy admission with early stop.  The
+// candidates are ranked by a kernel spread over the chip, then one workgroup
+// scans the sorted list, finds the stop and counts K_b.
 //
 // [blog] "硬件感知前缀调度器" steps 1-4: build every (request, length)
 // candidate with its survival a, sort from high to low, admit greedily while
@@ -28,35 +29,53 @@ __device__ __forceinline__ float key_value(uint64_t k) {
   return __uint_as_float(~(uint32_t)(k >> 32));
 }
 
-// Keys of the survivals in src, padded with the largest key, sorted
-// ascending in LDS (bitonic).
-__device__ void sort_keys(uint64_t* keys, const float* src, int n, int n_pad) {
-  const int tid = threadIdx.x;
-  for (int i = tid; i < n_pad; i += kSchedThreads) {
-    uint64_t key = ~0ull;
-    if (i < n) {
-      float v = src[i];
-      v = (v > 0.0f) ? v : 0.0f;    // NaN, negatives and -0 read as +0
-      key = ((uint64_t)(~__float_as_uint(v)) << 32) | (uint32_t)i;
-    }
-    keys[i] = key;
-  }
+__device__ __forceinline__ uint64_t sched_key(float v, int i) {
+  v = (v > 0.0f) ? v : 0.0f;        // NaN, negatives and -0 read as +0
+  return ((uint64_t)(~__float_as_uint(v)) << 32) | (uint32_t)i;
+}
+
+// Sorting by ranking, spread over the whole chip: a sort inside the
+// scheduler's single workgroup is one CU's work (a bitonic network over 4096
+// keys took ~30 us).  Workgroup (g, set) ranks keys 16 g .. 16 g + 15 of
+// the set against all n keys (the keys are distinct: the index is their low
+// word): thread t compares key t % 16 with every 64th key, the counts merge
+// by shuffles and across waves, and the key is stored at its rank.  Set 0:
+// the survivals the count is chosen from (the older ones under the
+// asynchronous rule); set 1: the current survivals (asynchronous rule only).
+constexpr int kRankKeys = 16;
+
+__global__ __launch_bounds__(kSchedThreads) void sched_rank_impl(const SchedArgs a) {
+  __shared__ uint64_t all[kSchedKeys];
+  __shared__ int part[kSchedThreads / 64][kRankKeys];
+  const int n = a.B * a.gamma;
+  const int set = blockIdx.y;
+  const float* src = (set == 0 && a.surv_hist) ? a.surv_hist : a.surv;
+  for (int j = threadIdx.x; j < n; j += kSchedThreads) all[j] = sched_key(src[j], j);
   __syncthreads();
-  for (int size = 2; size <= n_pad; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < (n_pad >> 1); t += kSchedThreads) {
-        const int i = 2 * t - (t & (stride - 1));
-        const int jx = i + stride;
-        const uint64_t ki = keys[i], kj = keys[jx];
-        const bool up = (i & size) == 0;
-        if ((ki > kj) == up) {
-          keys[i] = kj;
-          keys[jx] = ki;
-        }
-      }
-      __syncthreads();
-    }
+  const int ks = threadIdx.x % kRankKeys;
+  const int jg = threadIdx.x / kRankKeys;
+  const int i = blockIdx.x * kRankKeys + ks;
+  const uint64_t ki = i < n ? all[i] : 0ull;
+  int cnt = 0;
+  for (int j = jg; j < n; j += kSchedThreads / kRankKeys) cnt += all[j] < ki ? 1 : 0;
+  // lane = 16 (jg mod 4) + ks: the four j-groups of a wave differ in lane bits 4, 5
+  cnt += __shfl_xor(cnt, 16, 64);
+  cnt += __shfl_xor(cnt, 32, 64);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane < kRankKeys) part[wid][lane] = cnt;
+  __syncthreads();
+  if ((int)threadIdx.x < kRankKeys && i < n) {
+    int r = 0;
+#pragma unroll
+    for (int w = 0; w < kSchedThreads / 64; ++w) r += part[w][threadIdx.x];
+    a.sorted[(size_t)set * kSchedKeys + r] = ki;
   }
+}
+
+// The ranked keys of one set into LDS, padded with the largest key.
+__device__ __forceinline__ void load_sorted(uint64_t* keys, const uint64_t* sorted, int n, int n_pad) {
+  for (int i = threadIdx.x; i < n_pad; i += kSchedThreads) keys[i] = i < n ? sorted[i] : ~0ull;
+  __syncthreads();
 }
 
 // Exclusive prefix (float64) of this thread's segment of the sorted list.
@@ -106,7 +125,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_impl(const SchedArgs a
   int n_pad = 2;
   while (n_pad < n) n_pad <<= 1;
   if (tid == 0) first_stop = 0x7fffffff;
-  sort_keys(keys, ASYNC ? a.surv_hist : a.surv, n, n_pad);
+  load_sorted(keys, a.sorted, n, n_pad);
   // each thread: a contiguous segment of the sorted list
   const int seg = (n_pad >= kSchedThreads) ? n_pad / kSchedThreads : 1;
   const int p0 = tid * seg;
@@ -172,7 +191,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_impl(const SchedArgs a
     }
     __syncthreads();
     // rank the current survivals; the admitted set is their top n*
-    sort_keys(keys, a.surv, n, n_pad);
+    load_sorted(keys, a.sorted + kSchedKeys, n, n_pad);
     for (int e = 0; e < seg; ++e) {
       const int p = p0 + e;
       bidx[e] = p < n ? (int)((uint32_t)keys[p]) / a.gamma : -1;
@@ -208,6 +227,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_impl(const SchedArgs a
 }
 
 }  // namespace
+
+const void* schedule_rank_kernel() { return (const void*)&sched_rank_impl; }
 
 const void* schedule_kernel(int async) {
   return async ? (const void*)&schedule_impl<1> : (const void*)&schedule_impl<0>;
