@@ -605,26 +605,78 @@ __global__ __launch_bounds__(256) void sweep_private_impl(const SweepArgs a) {
   const int t0 = (int)((int64_t)a.n_tiles * vc / a.n_vc);
   const int t1 = (int)((int64_t)a.n_tiles * (vc + 1) / a.n_vc);
   const WT* __restrict__ W2 = static_cast<const WT*>(a.W2);
-  auto load_a = [&](int t, FragT (&A)[NS]) {
-    const WT* w2row = W2 + (int64_t)(t * kTileV + j) * R;
+  // bf16 weights: a direct load of the MFMA fragments (and of U) has every
+  // quarter-wave touch 16 rows; instead lane L loads what lane (L / 4, L % 4)
+  // needs (4 rows x 64 contiguous bytes per quarter-wave) and the lane
+  // transpose (ds_bpermute) at use time hands it over, so the loads of the
+  // next tile stay in flight meanwhile.
+  constexpr bool kT = sizeof(FragT) == 16;
+  const int src_lane = kT ? (lane >> 2) : j;
+  const int src_q = kT ? (lane & 3) : q;
+  const int from = 4 * (4 * j + q);
+  int64_t uoff_t[2], toff_t[2];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) A[s] = F::load(w2row, s, q);
+  for (int nb = 0; nb < 2; ++nb) {
+    uoff_t[nb] = kT ? __shfl(w.uoff[nb], src_lane, 64) : w.uoff[nb];
+    toff_t[nb] = kT ? __shfl(w.toff[nb], src_lane, 64) : w.toff[nb];
+  }
+  auto load_a = [&](int t, FragT (&A)[NS]) {
+    const WT* w2row = W2 + (int64_t)(t * kTileV + src_lane) * R;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) A[s] = F::load(w2row, s, src_q);
+  };
+  auto load_ut = [&](int t, float4 (&uu)[2], float4 (&tt)[2]) {
+    const int v0 = t * kTileV + 4 * src_q;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      uu[nb] = *reinterpret_cast<const float4*>(a.U + uoff_t[nb] + v0);
+      if constexpr (MODE == kModeResidual || MODE == kModeAlpha)
+        tt[nb] = *reinterpret_cast<const float4*>(a.T + toff_t[nb] + v0);
+      else
+        tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto xpose4 = [&](float4& v) {
+    if constexpr (kT) {
+      v.x = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(v.x)));
+      v.y = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(v.y)));
+      v.z = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(v.z)));
+      v.w = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(v.w)));
+    }
+  };
+  auto compute_t = [&](int t, FragT (&A)[NS], float4 (&uu)[2], float4 (&tt)[2]) {
+    if constexpr (kT) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        union { FragT f; int w[4]; } x;
+        x.f = A[s];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) x.w[d] = __builtin_amdgcn_ds_bpermute(from, x.w[d]);
+        A[s] = x.f;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        xpose4(uu[nb]);
+        if constexpr (MODE == kModeResidual || MODE == kModeAlpha) xpose4(tt[nb]);
+      }
+    }
+    w.compute(a, st, t, q, A, uu, tt);
   };
   if (t0 < t1) {
     FragT A0[NS], A1[NS];
     float4 u0[2], u1[2], x0[2], x1[2];
     load_a(t0, A0);
-    w.load_ut(a, t0, q, u0, x0);
+    load_ut(t0, u0, x0);
     for (int t = t0; t < t1; t += 2) {
       const int tn = min(t + 1, t1 - 1);
       load_a(tn, A1);
-      w.load_ut(a, tn, q, u1, x1);
-      w.compute(a, st, t, q, A0, u0, x0);
+      load_ut(tn, u1, x1);
+      compute_t(t, A0, u0, x0);
       if (t + 1 >= t1) break;
       const int tn2 = min(t + 2, t1 - 1);
       load_a(tn2, A0);
-      w.load_ut(a, tn2, q, u0, x0);
-      w.compute(a, st, t + 1, q, A1, u1, x1);
+      load_ut(tn2, u0, x0);
+      compute_t(t + 1, A1, u1, x1);
     }
   }
   w.finish(a, st, q, vc);
