@@ -423,7 +423,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
     if (gru && k < gamma) {
       ga.k = k;
       ga.best = sa.best;
-      set_node(n, DSPARK_K_GRU, gru_step_kernel(r), dim3(r / 16, (B + 15) / 16), dim3(64), ga);
+      set_node(n, DSPARK_K_GRU, gru_step_kernel(r), dim3(r / 16, (B + 15) / 16), dim3(gru_step_threads(r)), ga);
       nodes.push_back(n);
     }
   }

@@ -44,15 +44,23 @@ __device__ __forceinline__ void split8(const float* p, bf16x8_t& hi, bf16x8_t& l
   }
 }
 
-// One wave per 16 hidden units x 16 requests: the six gate products
-// (W_i{r,z,n} x and W_h{r,z,n} s) are 16 x 16 x r MFMA tiles with the weight
-// rows as the A operand and the request's input row / state as B (split into
-// hi + lo bf16); lane l then holds units j0 + 4(l/16) + i of request
-// b0 + l % 16 for all six products and applies the cell.
+// One workgroup per 16 hidden units x 16 requests, kGruWaves(R) waves
+// splitting the K (= r) dimension: wave w takes K steps w NS/KW ..
+// (w+1) NS/KW - 1 of the six gate products (W_i{r,z,n} x and W_h{r,z,n} s,
+// 16 x 16 x r MFMA tiles with the weight rows as the A operand and the
+// request's input row / state as B, split into hi + lo bf16).  The partial
+// products meet in LDS and wave 0 adds them in wave order; its lane l then
+// holds units j0 + 4(l/16) + i of request b0 + l % 16 and applies the cell.
 template <int R>
-__global__ __launch_bounds__(64) void gru_step_impl(const GruArgs a) {
+constexpr int gru_waves() { return R / 32 >= 4 ? 4 : R / 32; }
+
+template <int R>
+__global__ __launch_bounds__(64 * gru_waves<R>()) void gru_step_impl(const GruArgs a) {
   constexpr int NS = R / 32;
-  const int lane = threadIdx.x;
+  constexpr int KW = gru_waves<R>();
+  constexpr int SPW = NS / KW;           // K steps per wave
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
   const int n = lane & 15;
   const int q = lane >> 4;
   const int j0 = blockIdx.x * kGruTile;
@@ -75,20 +83,21 @@ __global__ __launch_bounds__(64) void gru_step_impl(const GruArgs a) {
   }
   int tok = best_index(m);
   if ((unsigned)tok >= (unsigned)a.V) {
-    if (ok && q == 0) atomicOr(a.err, kErrToken);
+    if (ok && q == 0 && wid == 0) atomicOr(a.err, kErrToken);
     tok = 0;
   }
   const float* srow = a.states + (int64_t)(a.k - 1) * a.B * R + (int64_t)bx * R;
-  bf16x8_t xh[NS], xl[NS], sh_[NS], sl[NS];
+  bf16x8_t xh[SPW], xl[SPW], sh_[SPW], sl[SPW];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  for (int e = 0; e < SPW; ++e) {
+    const int s = wid * SPW + e;
     if (a.w1_bf16) {
-      xh[s] = load_bf16x8(static_cast<const uint16_t*>(a.W1) + (int64_t)tok * R + 32 * s + 8 * q);
-      xl[s] = zero_bf16x8();
+      xh[e] = load_bf16x8(static_cast<const uint16_t*>(a.W1) + (int64_t)tok * R + 32 * s + 8 * q);
+      xl[e] = zero_bf16x8();
     } else {
-      split8(static_cast<const float*>(a.W1) + (int64_t)tok * R + 32 * s + 8 * q, xh[s], xl[s]);
+      split8(static_cast<const float*>(a.W1) + (int64_t)tok * R + 32 * s + 8 * q, xh[e], xl[e]);
     }
-    split8(srow + 32 * s + 8 * q, sh_[s], sl[s]);
+    split8(srow + 32 * s + 8 * q, sh_[e], sl[e]);
   }
   f32x4_t gi[3], gh[3];
 #pragma unroll
@@ -98,14 +107,38 @@ __global__ __launch_bounds__(64) void gru_step_impl(const GruArgs a) {
     const uint16_t* wi = a.W_ih + (int64_t)(g * R + j0 + n) * R + 8 * q;
     const uint16_t* wh = a.W_hh + (int64_t)(g * R + j0 + n) * R + 8 * q;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int e = 0; e < SPW; ++e) {
+      const int s = wid * SPW + e;
       const bf16x8_t ai = load_bf16x8(wi + 32 * s);
       const bf16x8_t ah = load_bf16x8(wh + 32 * s);
-      gi[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, xh[s], gi[g], 0, 0, 0);
-      gi[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, xl[s], gi[g], 0, 0, 0);
-      gh[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh_[s], gh[g], 0, 0, 0);
-      gh[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl[s], gh[g], 0, 0, 0);
+      gi[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, xh[e], gi[g], 0, 0, 0);
+      gi[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ai, xl[e], gi[g], 0, 0, 0);
+      gh[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh_[e], gh[g], 0, 0, 0);
+      gh[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl[e], gh[g], 0, 0, 0);
     }
+  }
+  if constexpr (KW > 1) {
+    __shared__ float part[KW - 1][6][4][64];
+    if (wid > 0) {
+#pragma unroll
+      for (int g = 0; g < 3; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          part[wid - 1][g][i][lane] = gi[g][i];
+          part[wid - 1][3 + g][i][lane] = gh[g][i];
+        }
+    }
+    __syncthreads();
+    if (wid > 0) return;
+#pragma unroll
+    for (int w = 0; w < KW - 1; ++w)
+#pragma unroll
+      for (int g = 0; g < 3; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gi[g][i] += part[w][g][i][lane];
+          gh[g][i] += part[w][3 + g][i][lane];
+        }
   }
   if (!ok) return;
   float* out = a.states + (int64_t)a.k * a.B * R + (int64_t)b * R;
@@ -123,6 +156,8 @@ __global__ __launch_bounds__(64) void gru_step_impl(const GruArgs a) {
 }  // namespace
 
 const void* gru_init_kernel() { return (const void*)&gru_init_impl; }
+int gru_step_threads(int r) { return r >= 128 ? 256 : (r == 64 ? 128 : 64); }
+
 const void* gru_step_kernel(int r) {
   switch (r) {
     case 32: return (const void*)&gru_step_impl<32>;

@@ -162,6 +162,7 @@ const void* verify_decide_kernel();
 const void* confidence_kernel();
 const void* gru_init_kernel();
 const void* gru_step_kernel(int r);
+int gru_step_threads(int r);   // workgroup size of gru_step_kernel(r)
 const void* schedule_kernel(int async);
 const void* schedule_rank_kernel();
 
