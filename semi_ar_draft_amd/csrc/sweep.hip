@@ -484,19 +484,6 @@ struct WaveRows {
     setup_rest(a, q);
   }
 
-  __device__ __forceinline__ void load_ut(const SweepArgs& a, int t, int q, float4 (&uu)[2],
-                                          float4 (&tt)[2]) const {
-    const int v0 = t * kTileV;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      uu[nb] = *reinterpret_cast<const float4*>(a.U + uoff[nb] + v0 + 4 * q);
-      if constexpr (MODE == kModeResidual || MODE == kModeAlpha)
-        tt[nb] = *reinterpret_cast<const float4*>(a.T + toff[nb] + v0 + 4 * q);
-      else
-        tt[nb] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-
   // z = U + bias of one tile for both blocks (U initialises the accumulators).
   __device__ __forceinline__ void mma_tile(f32x4_t (&acc)[2], const FragT (&A)[NS], const float4 (&uu)[2]) const {
 #pragma unroll
