@@ -217,12 +217,23 @@ def main():
                 per_kernel[name] = {"launches_per_step": n / args.steps, "avg_us": 1e3 * ms / n,
                                     "us_per_step": 1e3 * ms / args.steps}
         wbytes = 2 if d["W1"].dtype == torch.bfloat16 else 4
-        # dominant kernel: the draft sweep (gamma launches per step)
+        # dominant kernel: the draft sweep -- one launch per position, or the
+        # whole-draft kernel (Markov head, bf16, r = 256, B <= 128): one
+        # launch for all gamma positions, W2 read once and held in registers
         sw = per_kernel["draft_sweep"]
-        b_sweep = sweep_bytes(B, V, r, wbytes, 4 if gru is not None else None)
-        # sw["avg_us"]: the library's timing events, attached to each dispatch
-        # (hipExtLaunchKernel), bracket the kernel's execution alone.
-        sweep_timing = "library timing events attached to each sweep dispatch, averaged over the timed steps"
+        whole = gru is None and G > 1 and round(sw["launches_per_step"]) == 1
+        pos_per_launch = G if whole else 1
+        if whole:
+            b_sweep = G * (4 * B * V + wbytes * B * r) + wbytes * r * V
+            # stream events around the cooperative launch (no dispatch-attached
+            # events for it): they include the ordering gap before the kernel
+            sweep_timing = ("library timing events recorded on the stream around each cooperative launch, "
+                            "averaged over the timed steps")
+        else:
+            b_sweep = sweep_bytes(B, V, r, wbytes, 4 if gru is not None else None)
+            # the library's timing events, attached to each dispatch
+            # (hipExtLaunchKernel), bracket the kernel's execution alone
+            sweep_timing = "library timing events attached to each sweep dispatch, averaged over the timed steps"
         if gru is None and G >= 3:
             # Cross-check, and the cost per launch inside the chain: draft
             # calls of gamma and of gamma' < gamma positions back to back, one
@@ -254,8 +265,9 @@ def main():
                 sw["in_chain_timing"] = (f"draft calls of {G} and {g2} positions back to back, one event pair per "
                                          f"50 calls: ({t_full:.1f} - {t_part:.1f}) us / {G - g2}")
         sw["alg_bytes"] = b_sweep
+        sw["positions_per_launch"] = pos_per_launch
         sw["alg_GBps"] = b_sweep / (sw["avg_us"] * 1e-6) / 1e9
-        sw["mfma_TFLOPs"] = 2.0 * B * r * V / (sw["avg_us"] * 1e-6) / 1e12
+        sw["mfma_TFLOPs"] = pos_per_launch * 2.0 * B * r * V / (sw["avg_us"] * 1e-6) / 1e12
         if "verify_rows" in per_kernel:
             # rows the accept decisions need: up to the first rejection, or K_b + 1
             vb = 4.0 * V * needed_rows
@@ -278,7 +290,9 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": measured_traffic(wl.name, B, V, r, T),
-                    "kernel": ("draft_sweep (MFMA Markov bias + vocabulary sweep, one position)" if gru is None
+                    "kernel": ("draft_persist (MFMA Markov bias + vocabulary sweep, all positions in one "
+                               "launch, W2 held in registers)" if whole else
+                               "draft_sweep (MFMA Markov bias + vocabulary sweep, one position)" if gru is None
                                else "draft_sweep (MFMA GRU-state bias + vocabulary sweep, one position)"),
                     "alg_bytes_per_launch": b_sweep, "avg_launch_us": round(sw["avg_us"], 2),
                     "timing": sweep_timing,
@@ -319,10 +333,11 @@ def main():
                 "mean_alpha_per_position": [round(float(x), 4) for x in alpha.mean(0).cpu()]}
         print(f"[bench] accept_prob: {us:.1f} us/call, {diag['alg_GBps']} GB/s", file=sys.stderr, flush=True)
 
-    # step-level algorithmic bytes (what one step must move at least)
+    # step-level algorithmic bytes (what one step must move at least: U of
+    # every position, W2 once, the bias vectors of every position)
     wbytes = 2 if d["W1"].dtype == torch.bfloat16 else 4
     n_rej_all = float((A < Ks).sum().item()) / args.steps
-    step_bytes = (G * sweep_bytes(B, V, r, wbytes, 4 if gru is not None else None)
+    step_bytes = (G * (4.0 * B * V + (4 if gru is not None else wbytes) * B * r) + wbytes * r * V
                   + (2.0 * B * G * (wl.d_h + wl.d_e) if has_conf else 0.0)
                   + 4.0 * V * needed_rows
                   + (8.0 * V * n_rej_all + wbytes * r * V if (T > 0 and n_rej_all > 0) else 0.0))

@@ -79,20 +79,24 @@ const char* dspark_last_error(const dspark_ctx* ctx);
 
 /* Synchronise `stream`, read and clear the device error flag.  Returns
  * DSPARK_EDEVICE if any kernel since the last check met an out-of-range
- * token id or verify length (the message names which), DSPARK_EHIP on a HIP
- * error, else DSPARK_OK. */
+ * token id or verify length, or a grid barrier of the whole-draft kernel
+ * gave up waiting (see dspark_draft_markov; the message names which),
+ * DSPARK_EHIP on a HIP error, else DSPARK_OK. */
 int dspark_check(dspark_ctx* ctx, hipStream_t stream);
 
 /* Kernel timing for benchmarks (not needed for correct use).
  * While enabled, every kernel the context launches carries a start and a
  * stop HIP event attached to its dispatch (they bracket the kernel's
- * execution, not the queue's ordering gap before it), and the draft loop is
+ * execution, not the queue's ordering gap before it; the whole-draft kernel,
+ * a cooperative launch, is bracketed by events recorded on the stream
+ * around it instead, which include that gap), and the draft loop is
  * launched kernel by kernel even where a graph was requested.  dspark_timing_read waits
  * for the recorded events, writes per-kernel-class totals (milliseconds) and
  * launch counts into arrays of DSPARK_K_COUNT entries, and forgets them.
  * Errors: DSPARK_EINVAL for null arguments, DSPARK_EHIP if an event fails. */
 enum {
-  DSPARK_K_DRAFT_SWEEP = 0,    /* MFMA bias + vocabulary sweep of one position */
+  DSPARK_K_DRAFT_SWEEP = 0,    /* MFMA bias + vocabulary sweep of one position (or of
+                                  every position: the whole-draft kernel) */
   DSPARK_K_DRAFT_COMBINE = 1,  /* cross-chunk merge of one position */
   DSPARK_K_CONFIDENCE = 2,     /* confidences and survival products (one launch) */
   DSPARK_K_SURVIVAL = 3,       /* kept for numbering; nothing is launched in it */
@@ -141,7 +145,19 @@ int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
  * anchor: int32 [B]; req_ids: uint32 [B] or NULL (then req = b).
  * tokens: int32 [B][gamma]; lse, ytok: float [B][gamma].
  * Logits must be finite.  Errors: DSPARK_EINVAL for shapes/pointers/
- * alignment/temperature < 0 or non-finite. */
+ * alignment/temperature < 0 or non-finite.
+ *
+ * Execution: one vocabulary sweep per position, each taking x_{k-1} from the
+ * previous sweep, then one merge.  For bf16 weights with r = 256, small
+ * batches (B <= 32 by default) and V <= 16 * 10 * 4 * (compute units), the
+ * whole draft instead runs as one cooperative launch (one workgroup per
+ * compute unit) that keeps W2 in registers and separates positions with a
+ * grid barrier; the results are the same function of the inputs (tokens
+ * and ytok bit-identical, lse to rounding).  Environment, read when the
+ * context is created: DSPARK_PERSIST=0 never uses it, =2 uses it for every
+ * eligible batch up to 128 requests.  The barrier's wait is bounded: a wait
+ * that does not complete (not expected while the launch is cooperative)
+ * gives up, the kernel ends and dspark_check reports DSPARK_EDEVICE. */
 int dspark_draft_markov(dspark_ctx* ctx, hipStream_t stream,
                         int B, int gamma, int V, int r, dspark_dtype wdtype,
                         const float* U, int64_t u_stride_b, int64_t u_stride_k,

@@ -50,6 +50,15 @@ struct dspark_ctx {
   int32_t* dev_err = nullptr;
   bool use_graph = false;
   int sweep_waves_per_cu = 8;     // occupancy target of the vocabulary sweeps
+  // whole-draft kernel (Markov head, bf16, r = 256): used up to persist_max_b
+  // requests (at most 128), and whether the device runs cooperative launches
+  // (-1 = not yet asked).  It keeps W2 in registers at one wave per SIMD; its
+  // fold is then issue-bound, so it wins only while the batch is small
+  // (measured: 16% faster at B = 8, 9% at B = 32, even at 48, 42% slower at 128).
+  int persist_max_b = 32;
+  int coop = -1;
+  int bar_test = 0;               // failure injection (tests): barriers time out
+  unsigned int* bar = nullptr;    // its grid barrier counter (inside dev_err's block)
   // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
   int draft_nt = 2, draft_depth = 1;
   // the GRU head's sweep holds its state as hi + lo fragments: with two-tile
@@ -221,6 +230,25 @@ hipError_t take_event(dspark_ctx* c, hipEvent_t* e) {
   return hipEventCreate(e);
 }
 
+// Cooperative launch (every workgroup resident at once); while timing is
+// enabled it is bracketed by stream events (no dispatch-attached events for
+// this launch type), which include the queue's ordering gap before it.
+int klaunch_coop(dspark_ctx* c, int cls, const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t s) {
+  void* params[] = {arg};
+  if (!c->timing) {
+    DSPARK_HIP(c, hipLaunchCooperativeKernel(fn, grid, block, params, 0, s));
+    return DSPARK_OK;
+  }
+  hipEvent_t a, b;
+  DSPARK_HIP(c, take_event(c, &a));
+  DSPARK_HIP(c, take_event(c, &b));
+  DSPARK_HIP(c, hipEventRecord(a, s));
+  DSPARK_HIP(c, hipLaunchCooperativeKernel(fn, grid, block, params, 0, s));
+  DSPARK_HIP(c, hipEventRecord(b, s));
+  c->pending.push_back({cls, a, b});
+  return DSPARK_OK;
+}
+
 // Launch one kernel; while timing is enabled, bracket it with events.
 int klaunch(dspark_ctx* c, int cls, const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t s) {
   if (!c->timing) {
@@ -319,6 +347,33 @@ int run_chain(dspark_ctx* c, hipStream_t stream, std::vector<KernelNode>& nodes,
   return DSPARK_OK;
 }
 
+// Whole-draft kernel eligibility: Markov head, bf16 weights, r = 256, a batch
+// within persist_max_b (<= 128), a vocabulary the waves' register tiles
+// cover, and a device that launches cooperatively with one such workgroup
+// per CU.
+bool use_persist(dspark_ctx* c, int B, int V, int r, int wdtype) {
+  if (wdtype != DSPARK_BF16 || r != 256 || B > c->persist_max_b || B > 128) return false;
+  if ((long)(V / kTileV) > (long)kPersistTiles * kWavesPerBlock * c->cu_count) return false;
+  if (c->coop < 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, c->device) != hipSuccess) {
+      (void)hipGetLastError();
+      v = 0;
+    }
+    int ok = v;
+    for (int m = kModeDraftGreedy; ok && m <= kModeDraftSample; ++m) {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, draft_persist_kernel(m), 256, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        nb = 0;
+      }
+      ok = nb >= 1;
+    }
+    c->coop = ok ? 1 : 0;
+  }
+  return c->coop == 1;
+}
+
 }  // namespace
 
 // The draft loop of either head: gamma sweeps (+ gamma - 1 GRU updates and
@@ -338,7 +393,9 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   const bool greedy = temperature == 0.0f;
   const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
   const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
-  const size_t npos = (size_t)B * pl.n_vc;             // partials of one position
+  const bool persist = !gru && use_persist(c, B, V, r, (int)wdtype);
+  const int n_vc = persist ? kWavesPerBlock * c->cu_count : pl.n_vc;
+  const size_t npos = (size_t)B * n_vc;                // partials of one position
   const size_t npart = npos * gamma;
   const size_t off_pi = align256(npart * sizeof(float4));
   if ((rc = ensure_ws(c, off_pi + align256(npart * sizeof(int2))))) return rc;
@@ -352,7 +409,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   sa.gamma = gamma;
   sa.V = V;
   sa.n_rg = pl.n_rg;
-  sa.n_vc = pl.n_vc;
+  sa.n_vc = n_vc;
   sa.n_tiles = pl.n_tiles;
   sa.xcd_remap = 1;
   sa.U = U;
@@ -374,7 +431,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   ca.B = B;
   ca.gamma = gamma;
   ca.V = V;
-  ca.n_vc = pl.n_vc;
+  ca.n_vc = n_vc;
   ca.greedy = greedy;
   ca.invT = sa.invT;
   ca.pf = pf;
@@ -385,6 +442,18 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   ca.ytok = ytok;
   ca.err = c->dev_err;
 
+  if (persist) {
+    // every position in one cooperative launch, then the merge (which also
+    // resets the launch's barrier counter)
+    sa.best = c->best;
+    sa.bar = c->bar;
+    sa.bar_test = c->bar_test;
+    ca.bar = c->bar;
+    rc = klaunch_coop(c, DSPARK_K_DRAFT_SWEEP, draft_persist_kernel(mode), dim3(c->cu_count), dim3(256), &sa,
+                      stream);
+    if (rc) return rc;
+    return klaunch(c, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), &ca, stream);
+  }
   const int hs = gru ? 1 : 0;
   const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, hs ? c->gru_depth : c->draft_depth,
                                              hs ? c->gru_nt : c->draft_nt, hs)
@@ -763,6 +832,17 @@ int dspark_create(dspark_ctx** out, int device) {
     delete c;
     return DSPARK_EHIP;
   }
+  c->bar = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(c->dev_err) + 128);
+  // whole-draft kernel: "0" never, "1" small batches (default), "2" every
+  // eligible batch (up to 128 requests)
+  const char* pk = getenv("DSPARK_PERSIST");
+  if (pk && pk[0] == '0' && pk[1] == 0) c->persist_max_b = 0;
+  if (pk && pk[0] == '2' && pk[1] == 0) c->persist_max_b = 128;
+  // failure injection for tests: every grid barrier of the whole-draft kernel
+  // waits for one arrival too many and gives up after 64 polls (the kernel
+  // still ends; the call's results are invalid and the error flag is raised)
+  const char* bt = getenv("DSPARK_BARRIER_TEST");
+  if (bt && bt[0] == '1' && bt[1] == 0) c->bar_test = 1;
   // The draft loop goes kernel by kernel by default: on this runtime a
   // stream operation after a graph launch starts ~9 us after the graph's
   // last kernel, more than the graph saves on eight launches of 8-30 us.
@@ -842,10 +922,11 @@ int dspark_check(dspark_ctx* c, hipStream_t stream) {
   DSPARK_HIP(c, hipMemcpy(&flag, c->dev_err, sizeof(flag), hipMemcpyDeviceToHost));
   if (flag) {
     DSPARK_HIP(c, hipMemset(c->dev_err, 0, sizeof(int32_t)));
-    return fail(c, DSPARK_EDEVICE, "device error flag 0x%x:%s%s%s", flag,
+    return fail(c, DSPARK_EDEVICE, "device error flag 0x%x:%s%s%s%s", flag,
                 (flag & kErrToken) ? " token id out of range" : "",
                 (flag & kErrK) ? " verify length out of range" : "",
-                (flag & kErrRow) ? " packed target row out of range" : "");
+                (flag & kErrRow) ? " packed target row out of range" : "",
+                (flag & kErrBarrier) ? " grid barrier timed out" : "");
   }
   c->err.clear();
   return DSPARK_OK;

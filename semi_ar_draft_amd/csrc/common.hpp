@@ -20,6 +20,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kErrToken = 1;    // a token id outside [0, V)
 constexpr int kErrK = 2;        // a verify length outside [0, gamma]
 constexpr int kErrRow = 4;      // a packed target row outside [0, n_rows)
+constexpr int kErrBarrier = 8;  // a grid barrier of the whole-draft kernel gave up waiting
 
 // Element offset of target row (b, k) (k 1-based): strided [B][gamma+1][V]
 // placement, or the packed layout where request b's rows 1 .. K_b + 1 start

@@ -53,6 +53,11 @@ struct SweepArgs {
   // GRU head: fp32 states [gamma][B][r]; position k projects hstate[k-1][b]
   // instead of W1[x_{k-1}] (kernels built with the state bias source)
   const float* hstate;
+  // whole-draft kernel: grid barrier arrival counter (zero at launch), and a
+  // failure-injection switch for tests (nonzero: every barrier waits for one
+  // arrival too many and gives up after 64 polls)
+  unsigned int* bar;
+  int bar_test;
   int32_t* err;
 };
 
@@ -62,6 +67,7 @@ struct CombineArgs {
   const float4* pf;              // draft: [gamma][B][n_vc] (every position at once)
   const int2* pi;
   unsigned long long* best;      // draft: [gamma][kBestGroups][B] running bests, cleared here
+  unsigned int* bar;             // draft: the whole-draft kernel's barrier counter, reset here (nullable)
   int32_t* tokens;               // draft: [B][gamma]
   float* lse;
   float* ytok;
@@ -153,6 +159,11 @@ struct GruArgs {
 // states in SweepArgs::hstate instead of W1 rows.  Returns nullptr if
 // unsupported.
 const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs);
+// Whole-draft kernel (Markov head, bf16, r = 256, B <= 128, V <= 16 *
+// kPersistTiles * waves): grid = one 256-thread workgroup per CU, launched
+// cooperatively; n_vc = 4 * grid.  nullptr for other modes.
+constexpr int kPersistTiles = 10;
+const void* draft_persist_kernel(int mode);
 const void* combine_draft_kernel();
 const void* combine_resid_kernel();
 const void* combine_alpha_kernel();

@@ -879,6 +879,249 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   w.finish(a, st, q, vc);
 }
 
+// Whole-draft variant (Markov head, bf16 weights, r = 256, B <= 128): one
+// launch runs every position.  Each wave owns up to kPersistTiles 16-wide
+// vocabulary tiles and keeps their W2 fragments (the MFMA A operand) in
+// registers for the whole draft, so W2 is read from memory once per call
+// instead of once per position; per position only U (and the W1 rows of the
+// previous tokens) move.  One 4-wave workgroup per CU (the grid is launched
+// cooperatively, so every workgroup is resident), and positions are separated
+// by a grid barrier (an arrival counter with a bounded spin).
+//
+// Per position: the four waves gather the 128 W1 rows of the previous tokens
+// into LDS (chunk c of row b at chunk c ^ (b & 15), which makes the B-operand
+// reads conflict free); then each wave walks its steps (request block nb of
+// 16 rows) x (tile pair p): U of the step (16 rows x 128 bytes) comes through
+// a private ring of kPersistRing LDS slots filled by direct global->LDS loads
+// that run up to kPersistRing - 1 steps ahead, across position boundaries
+// (U does not depend on the tokens).  At the end of a request block the wave
+// writes its partial and its slot-group atomic, exactly as a chunk of the
+// per-position sweep does; the partials of every position are merged by the
+// draft combine.
+constexpr int kPersistRing = 8;
+constexpr int kPersistSteps = 16 * 128;              // bytes of U per step
+constexpr unsigned kSpinLimit = 1u << 20;            // polls before a barrier gives up
+
+// Ring wait of the whole-draft kernel: a step's two loads have landed when at
+// most the loads of the D - 1 = 6 later steps are in flight.
+__device__ __forceinline__ void vm_wait12() { asm volatile("s_waitcnt vmcnt(12)" : : : "memory"); }
+
+// Grid barrier: every workgroup adds one arrival after all its waves' slot
+// atomics have completed; the counter starts at zero (the draft combine
+// resets it).  The values that cross the barrier are the slot-group atomics,
+// which are performed device-coherently, and they are read back with
+// agent-scope atomic loads (coherent, no cached copy), so each wave only
+// waits for its own memory operations (vmcnt 0) instead of a release fence:
+// a release fence at agent scope writes back the L2 from every wave, which
+// cost ~15 us per barrier here.  The partials written between barriers are
+// read only by the next kernel.  A poll that never sees `target` gives up
+// after kSpinLimit tries and raises the barrier error bit, so every wave
+// always exits.
+__device__ __forceinline__ void grid_barrier(unsigned int* bar, unsigned int target, unsigned int limit,
+                                             int32_t* err) {
+  vm_drain();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned spins = 0;
+    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > limit) {
+        atomicOr(err, kErrBarrier);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void draft_persist_impl(const SweepArgs a) {
+  constexpr int R = 256;
+  using F = Frag<uint16_t, R>;
+  using FragT = typename F::T;
+  constexpr int NS = F::NS;
+  constexpr int TW = kPersistTiles;
+  constexpr int NP = (TW + 1) / 2;
+  constexpr int NBUF = kPersistRing;
+  constexpr int D = NBUF - 1;
+  static_assert(NBUF == 8 && 2 * (D - 1) == 12, "vm_wait12 assumes 8 slots of two loads");
+  static_assert(TW % 2 == 0, "tiles come in pairs");
+  __shared__ __attribute__((aligned(16))) unsigned char hbuf[128 * R * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char uring[kWavesPerBlock * NBUF * kPersistSteps];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS bases go to M0
+  const int q = lane >> 4;
+  const int j = lane & 15;
+  const int nw = gridDim.x * kWavesPerBlock;           // = n_vc: one chunk per wave
+  const int wg = blockIdx.x * kWavesPerBlock + wid;
+  const int t0 = (int)((int64_t)a.n_tiles * wg / nw);
+  const int t1 = (int)((int64_t)a.n_tiles * (wg + 1) / nw);
+  const int ntw = t1 - t0;                             // 0 .. TW (checked by the host)
+  const int np = (ntw + 1) / 2;                        // tile pairs = steps per request block
+  const int nbq = (a.B + 15) / 16;                     // request blocks
+  const uint16_t* W2 = static_cast<const uint16_t*>(a.W2);
+  const uint16_t* W1 = static_cast<const uint16_t*>(a.W1);
+
+  // W2 fragments of the wave's tiles (tiles past the range repeat the last
+  // tile of the vocabulary; they are never used)
+  FragT A[TW][NS];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int tt = min(t0 + t, a.n_tiles - 1);
+    const uint16_t* row = W2 + ((int64_t)tt * kTileV + j) * R;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) A[t][s] = F::load(row, s, q);
+  }
+  // request ids of rows lane and lane + 64 (stream keys, sampling)
+  uint32_t rid[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int b = lane + 64 * h;
+    rid[h] = (b < a.B) ? (a.req ? a.req[b] : (uint32_t)b) : 0u;
+  }
+
+  // ring cursor: the next step to load, as (position, request block, pair)
+  const uint32_t ring_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8_t*)uring + wid * NBUF * kPersistSteps);
+  int ik = 1, inb = 0, ip = 0, gi = 0;
+  const bool has_steps = np > 0;
+  auto issue_next = [&]() {
+    if (!has_steps || ik > a.gamma) return;            // uniform over the wave
+    const uint32_t dst = ring_lds + (gi & (NBUF - 1)) * kPersistSteps;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int r = m * 8 + (lane >> 3);
+      const int b = inb * 16 + r;
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int col = min((t0 + 2 * ip) * kTileV + 4 * c, t1 * kTileV - 4);
+      const float* src = a.U + (b < a.B ? (int64_t)b * a.usb : 0) + (int64_t)(ik - 1) * a.usk + col;
+      dma16(src, dst + m * 1024);
+    }
+    ++gi;
+    if (++ip == np) {
+      ip = 0;
+      if (++inb == nbq) {
+        inb = 0;
+        ++ik;
+      }
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue_next();
+
+  const uint32_t h_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8_t*)hbuf);
+  int gs = 0;                                          // next step to consume
+  for (int k = 1; k <= a.gamma; ++k) {
+    // previous tokens of rows wid*32 + (lane & 31): the anchor, or the
+    // maximum over the previous position's slot groups (each half-wave reads
+    // eight groups)
+    {
+      const int rq = wid * 32 + (lane & 31);
+      const bool act = rq < a.B;
+      int tok = 0;
+      if (k == 1) {
+        tok = act ? a.anchor[rq] : 0;
+      } else {
+        unsigned long long pb = 0ull;
+        if (act) {
+          const unsigned long long* bp = a.best + (int64_t)(k - 2) * kBestGroups * a.B;
+#pragma unroll
+          for (int i = 0; i < kBestGroups / 2; ++i) {
+            const unsigned long long v = __hip_atomic_load(
+                bp + (int64_t)((lane >> 5) * (kBestGroups / 2) + i) * a.B + rq, __ATOMIC_RELAXED,
+                __HIP_MEMORY_SCOPE_AGENT);
+            pb = v > pb ? v : pb;
+          }
+        }
+        const unsigned long long o = __shfl_xor(pb, 32, 64);
+        pb = o > pb ? o : pb;
+        tok = act ? best_index(pb) : 0;
+      }
+      if ((unsigned)tok >= (unsigned)a.V) {
+        atomicOr(a.err, kErrToken);
+        tok = 0;
+      }
+      // gather: instruction i fills rows 2i and 2i + 1 of the wave's quarter
+      // (1 KB of LDS); lane L writes chunk slot L & 31 of its row, which
+      // holds chunk (L & 31) ^ (row & 15)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = 2 * i + (lane >> 5);
+        const int b = wid * 32 + rr;
+        const int tk = __shfl(tok, rr, 64);
+        const int c = (lane & 31) ^ (b & 15);
+        dma16(W1 + (int64_t)tk * R + c * 8, h_lds + (wid * 32 + 2 * i) * 512);
+      }
+      vm_drain();
+      __syncthreads();
+    }
+
+    for (int nb = 0; nb < nbq; ++nb) {
+      const int b = nb * 16 + j;
+      const bool ok = b < a.B;
+      uint32_t klo = 0u, khi = 0u;
+      if constexpr (MODE == kModeDraftSample) {
+        const uint32_t r0 = __shfl(rid[0], b & 63, 64), r1 = __shfl(rid[1], b & 63, 64);
+        const uint64_t key = stream_key(a.seed, b < 64 ? r0 : r1, (uint32_t)k, kDraft);
+        klo = (uint32_t)key;
+        khi = (uint32_t)(key >> 32);
+      }
+      FragT Hf[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        Hf[s] = *reinterpret_cast<const FragT*>(hbuf + (nb * 16 + j) * 512 + (((4 * s + q) ^ j) * 16));
+      LaneState st;
+      lane_init(st);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (p >= np) break;                              // uniform over the wave
+        // this step's loads have landed when at most the D - 1 later steps
+        // (two loads each) are in flight
+        vm_wait12();
+        issue_next();
+        const unsigned char* sl = uring + wid * NBUF * kPersistSteps + (gs & (NBUF - 1)) * kPersistSteps;
+        ++gs;
+        f32x4_t acc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = (4 * h + q) ^ ((j >> 1) & 7);
+          const float4 u = *reinterpret_cast<const float4*>(sl + j * 128 + c * 16);
+          acc[h] = f32x4_t{u.x, u.y, u.z, u.w};
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[0] = F::mma(A[2 * p][s], Hf[s], acc[0]);
+        const int v0 = (t0 + 2 * p) * kTileV + 4 * q;
+        if (2 * p + 1 < ntw) {                           // uniform over the wave
+#pragma unroll
+          for (int s = 0; s < NS; ++s) acc[1] = F::mma(A[2 * p + 1][s], Hf[s], acc[1]);
+          const f32x4_t z2[2] = {acc[0], acc[1]};
+          fold_draft<MODE, 2>(st, z2, v0, klo, khi, a.s2);
+        } else {
+          const f32x4_t z1[1] = {acc[0]};
+          fold_draft<MODE, 1>(st, z1, v0, klo, khi, a.s2);
+        }
+      }
+      resolve_draft<MODE>(st, klo, khi, a.s2);
+      lane_merge<MODE>(st, 16);
+      lane_merge<MODE>(st, 32);
+      if (q == 0 && ok) {
+        const int64_t o = ((int64_t)(k - 1) * a.B + b) * nw + wg;
+        a.pf[o] = make_float4(st.m, st.s, st.key, st.zb);
+        a.pi[o] = make_int2(st.idx, 0);
+        unsigned long long* slot = a.best + ((int64_t)(k - 1) * kBestGroups + (wg % kBestGroups)) * a.B + b;
+        __hip_atomic_fetch_max(slot, pack_best(st.key, st.idx), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (k < a.gamma)
+      grid_barrier(a.bar, (unsigned)gridDim.x * (unsigned)k + (a.bar_test ? 1u : 0u), a.bar_test ? 64u : kSpinLimit,
+                   a.err);
+  }
+  vm_drain();                                            // no load in flight at exit
+}
+
 constexpr int kCombineThreads = 256;
 
 struct DraftPart {
@@ -931,6 +1174,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_draft_impl(const Comb
     a.lse[o] = (p.m + fast_log2(p.s)) * kLn2;
     a.ytok[o] = a.greedy ? p.key : p.zb * a.invT;
   }
+  if (a.bar && b == 0 && k == 1 && threadIdx.x == 0) *a.bar = 0u;   // grid barrier of the whole-draft kernel
   if (a.best && threadIdx.x < kBestGroups) {
     unsigned long long* slot = a.best + ((int64_t)(k - 1) * kBestGroups + threadIdx.x) * a.B + b;
     __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1064,6 +1308,12 @@ const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs)
   }
   if (wdtype == 1) return hs ? private_for_r<uint16_t, 1>(r, mode) : private_for_r<uint16_t, 0>(r, mode);
   if (wdtype == 0) return hs ? private_for_r<float, 1>(r, mode) : private_for_r<float, 0>(r, mode);
+  return nullptr;
+}
+
+const void* draft_persist_kernel(int mode) {
+  if (mode == kModeDraftGreedy) return (const void*)&draft_persist_impl<kModeDraftGreedy>;
+  if (mode == kModeDraftSample) return (const void*)&draft_persist_impl<kModeDraftSample>;
   return nullptr;
 }
 
