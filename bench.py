@@ -223,17 +223,18 @@ def main():
         sw = per_kernel["draft_sweep"]
         whole = gru is None and G > 1 and round(sw["launches_per_step"]) == 1
         pos_per_launch = G if whole else 1
+        # the library's timing events, attached to each dispatch
+        # (hipExtLaunchKernel), bracket the kernel's execution alone
+        sweep_timing = "library timing events attached to each sweep dispatch, averaged over the timed steps"
         if whole:
             b_sweep = G * (4 * B * V + wbytes * B * r) + wbytes * r * V
-            # stream events around the cooperative launch (no dispatch-attached
-            # events for it): they include the ordering gap before the kernel
-            sweep_timing = ("library timing events recorded on the stream around each cooperative launch, "
-                            "averaged over the timed steps")
+            if os.environ.get("DSPARK_PERSIST_COOP") == "1":
+                # no dispatch-attached events for a cooperative launch: stream
+                # events around it, which include the ordering gap before it
+                sweep_timing = ("library timing events recorded on the stream around each cooperative launch, "
+                                "averaged over the timed steps")
         else:
             b_sweep = sweep_bytes(B, V, r, wbytes, 4 if gru is not None else None)
-            # the library's timing events, attached to each dispatch
-            # (hipExtLaunchKernel), bracket the kernel's execution alone
-            sweep_timing = "library timing events attached to each sweep dispatch, averaged over the timed steps"
         if gru is None and G >= 3:
             # Cross-check, and the cost per launch inside the chain: draft
             # calls of gamma and of gamma' < gamma positions back to back, one

@@ -87,9 +87,10 @@ int dspark_check(dspark_ctx* ctx, hipStream_t stream);
 /* Kernel timing for benchmarks (not needed for correct use).
  * While enabled, every kernel the context launches carries a start and a
  * stop HIP event attached to its dispatch (they bracket the kernel's
- * execution, not the queue's ordering gap before it; the whole-draft kernel,
- * a cooperative launch, is bracketed by events recorded on the stream
- * around it instead, which include that gap), and the draft loop is
+ * execution, not the queue's ordering gap before it; a cooperative launch of
+ * the whole-draft kernel, DSPARK_PERSIST_COOP=1, is bracketed by events
+ * recorded on the stream around it instead, which include that gap), and
+ * the draft loop is
  * launched kernel by kernel even where a graph was requested.  dspark_timing_read waits
  * for the recorded events, writes per-kernel-class totals (milliseconds) and
  * launch counts into arrays of DSPARK_K_COUNT entries, and forgets them.
@@ -149,15 +150,20 @@ int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
  *
  * Execution: one vocabulary sweep per position, each taking x_{k-1} from the
  * previous sweep, then one merge.  For bf16 weights with r = 256, small
- * batches (B <= 32 by default) and V <= 16 * 10 * 4 * (compute units), the
- * whole draft instead runs as one cooperative launch (one workgroup per
- * compute unit) that keeps W2 in registers and separates positions with a
- * grid barrier; the results are the same function of the inputs (tokens
- * and ytok bit-identical, lse to rounding).  Environment, read when the
- * context is created: DSPARK_PERSIST=0 never uses it, =2 uses it for every
- * eligible batch up to 128 requests.  The barrier's wait is bounded: a wait
- * that does not complete (not expected while the launch is cooperative)
- * gives up, the kernel ends and dspark_check reports DSPARK_EDEVICE. */
+ * batches (B <= 48 by default) and V <= 16 * 10 * 4 * (compute units), the
+ * whole draft instead runs as one launch of one workgroup per compute unit
+ * that keeps W2 in registers and separates positions with a grid barrier;
+ * the results are the same function of the inputs (tokens and ytok
+ * bit-identical, lse to rounding).  Its workgroups must all be resident to
+ * pass a barrier: on an otherwise idle device they are; if concurrent work
+ * holds compute units, the waiting workgroups start as those units free up.
+ * The barrier's wait is bounded (about a second): a wait that does not
+ * complete gives up, the kernel ends and dspark_check reports
+ * DSPARK_EDEVICE.  Environment, read when the context is created:
+ * DSPARK_PERSIST=0 never uses this kernel, =2 uses it for every eligible
+ * batch up to 128 requests; DSPARK_PERSIST_COOP=1 launches it cooperatively
+ * (the runtime then guarantees co-residency, at ~15 us more per call), for
+ * callers that share the device with long-running kernels. */
 int dspark_draft_markov(dspark_ctx* ctx, hipStream_t stream,
                         int B, int gamma, int V, int r, dspark_dtype wdtype,
                         const float* U, int64_t u_stride_b, int64_t u_stride_k,

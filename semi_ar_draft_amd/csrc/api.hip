@@ -54,9 +54,13 @@ struct dspark_ctx {
   // requests (at most 128), and whether the device runs cooperative launches
   // (-1 = not yet asked).  It keeps W2 in registers at one wave per SIMD; its
   // fold is then issue-bound, so it wins only while the batch is small
-  // (measured: 16% faster at B = 8, 9% at B = 32, even at 48, 42% slower at 128).
-  int persist_max_b = 32;
+  // (measured draft calls against the per-position sweeps: 1.5x faster at
+  // B = 16, 1.3x at 32, 1.1x at 40-48, even at 56-64, 0.75x at 128).
+  int persist_max_b = 48;
   int coop = -1;
+  // launch it cooperatively (co-residency guaranteed by the runtime, ~15 us
+  // more per call here) instead of as a plain launch of one workgroup per CU
+  bool persist_coop = false;
   int bar_test = 0;               // failure injection (tests): barriers time out
   unsigned int* bar = nullptr;    // its grid barrier counter (inside dev_err's block)
   // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
@@ -349,14 +353,17 @@ int run_chain(dspark_ctx* c, hipStream_t stream, std::vector<KernelNode>& nodes,
 
 // Whole-draft kernel eligibility: Markov head, bf16 weights, r = 256, a batch
 // within persist_max_b (<= 128), a vocabulary the waves' register tiles
-// cover, and a device that launches cooperatively with one such workgroup
-// per CU.
+// cover, and room for one such workgroup per CU (its LDS and registers
+// admit no second one, so a grid of one workgroup per CU is resident at once
+// on an otherwise idle device; with persist_coop the device must also
+// support cooperative launches).
 bool use_persist(dspark_ctx* c, int B, int V, int r, int wdtype) {
   if (wdtype != DSPARK_BF16 || r != 256 || B > c->persist_max_b || B > 128) return false;
   if ((long)(V / kTileV) > (long)kPersistTiles * kWavesPerBlock * c->cu_count) return false;
   if (c->coop < 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, c->device) != hipSuccess) {
+    int v = 1;
+    if (c->persist_coop &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, c->device) != hipSuccess) {
       (void)hipGetLastError();
       v = 0;
     }
@@ -443,14 +450,16 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   ca.err = c->dev_err;
 
   if (persist) {
-    // every position in one cooperative launch, then the merge (which also
-    // resets the launch's barrier counter)
+    // every position in one launch of one workgroup per CU, then the merge
+    // (which also resets the launch's barrier counter)
     sa.best = c->best;
     sa.bar = c->bar;
     sa.bar_test = c->bar_test;
     ca.bar = c->bar;
-    rc = klaunch_coop(c, DSPARK_K_DRAFT_SWEEP, draft_persist_kernel(mode), dim3(c->cu_count), dim3(256), &sa,
-                      stream);
+    rc = c->persist_coop
+             ? klaunch_coop(c, DSPARK_K_DRAFT_SWEEP, draft_persist_kernel(mode), dim3(c->cu_count), dim3(256), &sa,
+                            stream)
+             : klaunch(c, DSPARK_K_DRAFT_SWEEP, draft_persist_kernel(mode), dim3(c->cu_count), dim3(256), &sa, stream);
     if (rc) return rc;
     return klaunch(c, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), &ca, stream);
   }
@@ -841,6 +850,8 @@ int dspark_create(dspark_ctx** out, int device) {
   // failure injection for tests: every grid barrier of the whole-draft kernel
   // waits for one arrival too many and gives up after 64 polls (the kernel
   // still ends; the call's results are invalid and the error flag is raised)
+  const char* pc = getenv("DSPARK_PERSIST_COOP");
+  if (pc && pc[0] == '1' && pc[1] == 0) c->persist_coop = true;
   const char* bt = getenv("DSPARK_BARRIER_TEST");
   if (bt && bt[0] == '1' && bt[1] == 0) c->bar_test = 1;
   // The draft loop goes kernel by kernel by default: on this runtime a

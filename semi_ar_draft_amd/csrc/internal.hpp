@@ -160,8 +160,8 @@ struct GruArgs {
 // unsupported.
 const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs);
 // Whole-draft kernel (Markov head, bf16, r = 256, B <= 128, V <= 16 *
-// kPersistTiles * waves): grid = one 256-thread workgroup per CU, launched
-// cooperatively; n_vc = 4 * grid.  nullptr for other modes.
+// kPersistTiles * waves): grid = one 256-thread workgroup per CU (plain or
+// cooperative launch); n_vc = 4 * grid.  nullptr for other modes.
 constexpr int kPersistTiles = 10;
 const void* draft_persist_kernel(int mode);
 const void* combine_draft_kernel();

@@ -884,9 +884,12 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
 // vocabulary tiles and keeps their W2 fragments (the MFMA A operand) in
 // registers for the whole draft, so W2 is read from memory once per call
 // instead of once per position; per position only U (and the W1 rows of the
-// previous tokens) move.  One 4-wave workgroup per CU (the grid is launched
-// cooperatively, so every workgroup is resident), and positions are separated
-// by a grid barrier (an arrival counter with a bounded spin).
+// previous tokens) move.  One 4-wave workgroup per CU: its LDS (128 KB) and
+// registers admit no second one per CU, so the grid of one per CU is resident
+// at once on an otherwise idle device (the host can also launch it
+// cooperatively); positions are separated by a grid barrier (an arrival
+// counter with a bounded spin, so a workgroup that is not yet resident delays
+// the barrier and never deadlocks it for good).
 //
 // Per position: the four waves gather the 128 W1 rows of the previous tokens
 // into LDS (chunk c of row b at chunk c ^ (b & 15), which makes the B-operand

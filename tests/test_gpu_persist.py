@@ -1,6 +1,6 @@
 """GPU parity of the whole-draft kernel (Markov head, bf16 weights, r = 256,
-B <= 128): every draft position in one cooperative launch, W2 held in
-registers, positions separated by a grid barrier.
+B <= 128): every draft position in one launch of one workgroup per CU, W2
+held in registers, positions separated by a grid barrier.
 
 By default the library uses it for small batches only; the contexts here are
 created with DSPARK_PERSIST=2, which selects it for every eligible batch, so
@@ -10,8 +10,9 @@ vocabulary tile, a long draft, the full-size sampling workload on sampled
 requests), against the per-position sweeps (greedy full size: z at the
 drafted token and the tokens are bit-identical, the MFMA sums being taken in
 the same order), at the largest vocabulary it covers and one tile past it
-(which falls back to the per-position sweeps), and with its barrier made to
-time out from the host (the kernel still ends and the error is reported).
+(which falls back to the per-position sweeps), launched cooperatively
+(identical results to the plain launch), and with its barrier made to time
+out from the host (the kernel still ends and the error is reported).
 """
 import os
 
@@ -133,6 +134,22 @@ def test_persist_vocabulary_limit(pctx):
             sctx.close()
         assert np.array_equal(a[0].cpu().numpy(), b[0].cpu().numpy())
         assert np.array_equal(a[2].cpu().numpy(), b[2].cpu().numpy())
+
+
+def test_persist_cooperative_launch_matches_plain(pctx):
+    wl = synth.WORKLOADS["sample"].with_(B=24, gamma=5, V=20480, conf=False)
+    inp = synth.make_inputs(wl, seed=13)
+    d = to_dev(inp)
+    cctx = make_ctx(DSPARK_PERSIST="2", DSPARK_PERSIST_COOP="1")
+    try:
+        print("cooperative launch of the whole-draft kernel", flush=True)
+        n_c, a = draft_launches(cctx, d, 1.0, 8, wl.gamma)
+    finally:
+        cctx.close()
+    n_p, b = draft_launches(pctx, d, 1.0, 8, wl.gamma)
+    assert n_c == 1 and n_p == 1
+    for x, y in zip(a, b):
+        assert np.array_equal(x.cpu().numpy(), y.cpu().numpy())
 
 
 def test_persist_barrier_timeout_is_reported():
