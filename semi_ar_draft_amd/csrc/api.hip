@@ -65,9 +65,10 @@ struct dspark_ctx {
   unsigned int* bar = nullptr;    // its grid barrier counter (inside dev_err's block)
   // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
   int draft_nt = 2, draft_depth = 1;
-  // the GRU head's sweep holds its state as hi + lo fragments: with two-tile
-  // steps it needs 268 VGPRs (one wave per SIMD), with one-tile steps 236
-  int gru_nt = 1, gru_depth = 1;
+  // the GRU head's sweep holds its state as hi + lo fragments, so its
+  // two-tile steps fold tile by tile (236 VGPRs: two waves per SIMD; a
+  // two-tile fold needed 268)
+  int gru_nt = 2, gru_depth = 1;
   int resid_nt = 1, resid_depth = 1;
   // verify: last target row of each window but the final one (window k covers
   // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list

@@ -827,8 +827,11 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
     }
   };
   auto compute = [&](int t, const unsigned char* sl) {
-    if constexpr (!kResid && NT == 2) {
-      // draft: both tiles through the MFMA, then one fold for the step
+    if constexpr (!kResid && NT == 2 && HS == 0) {
+      // Markov draft: both tiles through the MFMA, then one fold for the
+      // step (the GRU head, whose state fragments are twice as many, folds
+      // tile by tile below: its two-tile fold would need a second wave's
+      // registers)
       f32x4_t acc[NT][2];
       FragT A[NS];
       float4 uu[2], tt[2];
