@@ -155,15 +155,18 @@ int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
  * that keeps W2 in registers and separates positions with a grid barrier;
  * the results are the same function of the inputs (tokens and ytok
  * bit-identical, lse to rounding).  Its workgroups must all be resident to
- * pass a barrier: on an otherwise idle device they are; if concurrent work
- * holds compute units, the waiting workgroups start as those units free up.
- * The barrier's wait is bounded (about a second): a wait that does not
- * complete gives up, the kernel ends and dspark_check reports
- * DSPARK_EDEVICE.  Environment, read when the context is created:
- * DSPARK_PERSIST=0 never uses this kernel, =2 uses it for every eligible
- * batch up to 128 requests; DSPARK_PERSIST_COOP=1 launches it cooperatively
- * (the runtime then guarantees co-residency, at ~15 us more per call), for
- * callers that share the device with long-running kernels. */
+ * pass a barrier: on an otherwise idle device they are; if concurrent
+ * kernels hold compute units, the waiting workgroups start as those kernels
+ * finish.  Two such draft launches running at once on one device (calls on
+ * different streams) can each hold part of it and wait for each other.  The
+ * barrier's wait is bounded (about a second): a wait that does not complete
+ * gives up, the kernel ends and dspark_check reports DSPARK_EDEVICE.  Issue
+ * draft calls on one stream per device, or use the cooperative launch
+ * (co-residency guaranteed by the runtime).  Environment, read when the
+ * context is created: DSPARK_PERSIST=0 never uses this kernel, =2 uses it
+ * for every eligible batch up to 128 requests; DSPARK_PERSIST_COOP=1
+ * launches it cooperatively (~15 us more per call), for callers that share
+ * the device with other work. */
 int dspark_draft_markov(dspark_ctx* ctx, hipStream_t stream,
                         int B, int gamma, int V, int r, dspark_dtype wdtype,
                         const float* U, int64_t u_stride_b, int64_t u_stride_k,
