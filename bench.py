@@ -287,6 +287,9 @@ def main():
             cb = 2.0 * B * G * (wl.d_h + wl.d_e)
             per_kernel["confidence"]["alg_bytes"] = cb
             per_kernel["confidence"]["alg_GBps"] = cb / (per_kernel["confidence"]["avg_us"] * 1e-6) / 1e9
+        for v in per_kernel.values():
+            if "alg_GBps" in v:
+                v["frac_hbm"] = v["alg_GBps"] / HBM_PEAK_GBPS
         achieved = sw["alg_GBps"]
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -385,6 +388,10 @@ def main():
         "step_alg_bytes": step_bytes,
         "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "accepted_per_step": float(A.sum().item()) / args.steps,
+        # accepted drafts and emitted tokens (accepted + one correction or
+        # bonus token per request) per second of the timed steps
+        "accepted_tokens_per_s": round(float(A.sum().item()) / (elapsed_ms / 1e3), 1),
+        "emitted_tokens_per_s": round(float(A.sum().item() + B * args.steps) / (elapsed_ms / 1e3), 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "accept_prob": diag,

@@ -1,0 +1,25 @@
+"""bench.py's command-line contract on the CPU: more than one GPU is refused
+with a message (before any GPU work), and the metric line's fixed fields are
+the ones the headline is quoted with."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
+    assert p.stdout.strip() == ""
+
+
+def test_sweep_bytes_formula():
+    sys.path.insert(0, ROOT)
+    import bench
+    # U 4*B*V + W2 2*r*V + W1 rows 2*B*r at the headline shape
+    assert bench.sweep_bytes(128, 151936, 256, 2) == 155_648_000
+    # GRU head: the fp32 states replace the W1 rows
+    assert bench.sweep_bytes(256, 151936, 256, 2, 4) == 4 * 256 * 151936 + 2 * 256 * 151936 + 4 * 256 * 256
