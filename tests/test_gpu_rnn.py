@@ -146,3 +146,36 @@ def test_rnn_is_deterministic(ctx):
     b = gpu_step(ctx, d, seed=3)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def draw_rnn_cases(n=16, seed=77031):
+    """GRU-head shapes drawn once from a fixed seed: batch sizes on both sides
+    of the shared-tile threshold, one to ten positions, ragged vocabularies,
+    every rank, both W1 types, greedy and several temperatures, random K."""
+    rs = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        wdtype = "bf16" if rs.random() < 0.7 else "f32"
+        r = int(rs.choice([32, 64, 128, 256]))
+        B = int(rs.choice([1, 5, 31, 33, 64, 96, 129, 160]))
+        G = int(rs.integers(1, 11))
+        V = 16 * int(rs.integers(1, 300))
+        T = float(rs.choice([0.0, 0.7, 1.0, 1.3]))
+        cases.append((f"g{i}_{wdtype}_r{r}_B{B}_g{G}_V{V}_T{T}",
+                      dict(wdtype=wdtype, r=r, B=B, gamma=G, V=V, temperature=T)))
+    return cases
+
+
+RNN_CASES = draw_rnn_cases()
+
+
+@pytest.mark.parametrize("name,over", RNN_CASES, ids=[c[0] for c in RNN_CASES])
+def test_rnn_shape(ctx, name, over):
+    wl = synth.WORKLOADS["rnn"].with_(**over, conf=False, sts=False, sched=False,
+                                      u_std=3.0 if over["wdtype"] == "bf16" else 2.0)
+    inp = synth.make_inputs(wl, seed=wl.seed + 211)
+    rs = np.random.default_rng(len(name))
+    K = rs.integers(0, wl.gamma + 1, size=wl.B).astype(np.int32)
+    print(f"rnn shape {name}", flush=True)
+    g = gpu_step(ctx, to_dev(inp), seed=808, K=torch.from_numpy(K).cuda())
+    check(g, inp, 808, K=K)
