@@ -67,6 +67,10 @@ CASES = [
     ("sample_B100_gamma16", "sample", dict(B=100, gamma=16, V=2064, d_h=32, d_e=32, sts=True)),
     # 2560 tiles: two or three per wave
     ("sample_B128_V40960", "sample", dict(B=128, gamma=3, V=40960, d_h=16, d_e=16)),
+    # one tile in all: every wave but one owns none
+    ("sample_B3_V16", "sample", dict(B=3, gamma=3, V=16, d_h=8, d_e=8)),
+    # the longest draft: 31 barriers
+    ("greedy_B8_gamma32", "greedy", dict(B=8, gamma=32, V=1040, peak=None)),
 ]
 
 
