@@ -1,5 +1,6 @@
-// C ABI of libdspark: context, argument checks, workspace, launch plans and
-// the HIP-graph cache of the sequential draft loop.
+// C ABI of libdspark: context, argument checks, workspace, launch plans
+// (per-position sweeps or, for small batches, the whole-draft kernel) and the
+// HIP-graph cache of the sequential draft loop.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 

@@ -1,5 +1,7 @@
 // Vocabulary sweeps that carry the Markov-head bias (MFMA), for the draft
-// positions and for the verify residual draw.
+// positions, the verify residual draw and the acceptance-probability pass;
+// and, for small batches, the whole-draft kernel that runs every position of
+// a draft in one launch (draft_persist_impl, further down).
 //
 // [blog] "Markov Head：一阶转移偏置": B_k(v) = W1[x_{k-1}] . W2[:, v] with
 // W1 in R^{V x r}, W2 in R^{r x V}; [teardown] "DSpark 的解法" writes it as
