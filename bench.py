@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--diag-calls", type=int, default=10)
     ap.add_argument("--no-timing-pass", action="store_true",
                     help="skip the per-kernel event pass (used under a profiler)")
+    ap.add_argument("--draft-crossover", action="store_true",
+                    help="time draft calls of the whole-draft kernel against the per-position sweeps over batch "
+                         "sizes (instead of the step benchmark)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer a few times: the reference kernel of known "
                          "traffic used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -61,6 +64,60 @@ def copy_calibration(n_iter: int = 3):
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
                       "iterations": n_iter}))
+
+
+def draft_crossover(seed: int):
+    """Draft call time (gamma = 7, V = 151936, r = 256) of the whole-draft
+    kernel against the per-position sweeps over batch sizes, sampling and
+    greedy: the measurement behind the library's default batch bound for the
+    whole-draft kernel.  Prints one JSON line per (T, B)."""
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    import semi_ar_draft_amd as dk
+
+    def ctx_with(v):
+        old = os.environ.get("DSPARK_PERSIST")
+        os.environ["DSPARK_PERSIST"] = v
+        try:
+            return dk.Context(0)
+        finally:
+            if old is None:
+                del os.environ["DSPARK_PERSIST"]
+            else:
+                os.environ["DSPARK_PERSIST"] = old
+
+    wl = synth.WORKLOADS["sample"].with_(conf=False)
+    inp = synth.make_inputs(wl, seed=seed)
+    U, W1, W2 = inp["U"].cuda(), inp["W1"].cuda(), inp["W2"].cuda()
+    anc, req = inp["anchor"].cuda(), inp["req_ids"].cuda()
+    G = wl.gamma
+    whole, sweeps = ctx_with("2"), ctx_with("0")
+    for T in (1.0, 0.0):
+        for B in (16, 32, 48, 64, 96, 128):
+            us = []
+            for ctx in (whole, sweeps):
+                out = (torch.empty((B, G), dtype=torch.int32, device="cuda"),
+                       torch.empty((B, G), dtype=torch.float32, device="cuda"),
+                       torch.empty((B, G), dtype=torch.float32, device="cuda"))
+                for i in range(3):
+                    ctx.draft_markov(U[:B], W1, W2, anc[:B], req[:B], T, 11 + i, G, out=out)
+                ctx.check()
+                torch.cuda.synchronize()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                for i in range(30):
+                    ctx.draft_markov(U[:B], W1, W2, anc[:B], req[:B], T, 100 + i, G, out=out)
+                b.record()
+                torch.cuda.synchronize()
+                ctx.check()
+                us.append(1e3 * a.elapsed_time(b) / 30)
+            print(json.dumps({"temperature": T, "B": B, "gamma": G, "V": wl.V, "whole_draft_us": round(us[0], 1),
+                              "per_position_sweeps_us": round(us[1], 1), "speedup": round(us[1] / us[0], 3)}),
+                  flush=True)
+    whole.close()
+    sweeps.close()
 
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -104,6 +161,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.draft_crossover:
+        draft_crossover(args.seed)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
