@@ -117,3 +117,42 @@ def test_accept_prob_rejects_greedy(ctx):
     with pytest.raises(dk.DSparkError):
         ctx.accept_prob(inp["target"].cuda(), inp["U"].cuda(), inp["W1"].cuda(), inp["W2"].cuda(),
                         inp["anchor"].cuda(), tok, lse, 0.0)
+
+
+def draw_alpha_cases(n=8, seed=9091):
+    """Markov-head shapes drawn once from a fixed seed for the diagnostic
+    pass: batch sizes on both sides of the shared-tile threshold, ragged
+    vocabularies, ranks, both weight types, several temperatures."""
+    rs = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        wdtype = "bf16" if rs.random() < 0.7 else "f32"
+        r = int(rs.choice([32, 64, 128, 256]) if wdtype == "f32" else rs.choice([64, 128, 256]))
+        B = int(rs.choice([1, 7, 40, 96, 130]))
+        G = int(rs.integers(1, 9))
+        V = 16 * int(rs.integers(1, 300))
+        T = float(rs.choice([0.7, 1.0, 1.4]))
+        out.append((f"a{i}_{wdtype}_r{r}_B{B}_g{G}_V{V}_T{T}", dict(wdtype=wdtype, r=r, B=B, gamma=G, V=V,
+                                                                   temperature=T)))
+    return out
+
+
+ALPHA_CASES = draw_alpha_cases()
+
+
+@pytest.mark.parametrize("name,over", ALPHA_CASES, ids=[c[0] for c in ALPHA_CASES])
+def test_accept_prob_shape(ctx, name, over):
+    wl = synth.WORKLOADS["sample"].with_(**over, conf=False, peak=None,
+                                         u_std=3.0 if over["wdtype"] == "bf16" else 2.0)
+    inp = synth.make_inputs(wl, seed=wl.seed + 19)
+    T, seed = wl.temperature, 41
+    print(f"accept_prob shape {name}", flush=True)
+    od = oracle.draft_markov(inp["U"], inp["W1"], inp["W2"], inp["anchor"], inp["req_ids"], T, seed, wl.gamma)
+    want = oracle.accept_prob(inp["target"], od.tokens, od.lse, inp["U"], inp["W1"], inp["W2"], inp["anchor"],
+                              T, wl.gamma)
+    tok = torch.from_numpy(np.ascontiguousarray(od.tokens, dtype=np.int32)).cuda()
+    lse = torch.from_numpy(np.ascontiguousarray(od.lse, dtype=np.float32)).cuda()
+    got = ctx.accept_prob(inp["target"].cuda(), inp["U"].cuda(), inp["W1"].cuda(), inp["W2"].cuda(),
+                          inp["anchor"].cuda(), tok, lse, T)
+    ctx.check()
+    _check(got.cpu().numpy(), want, name)

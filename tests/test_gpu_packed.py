@@ -95,3 +95,52 @@ def test_packed_row_out_of_range_is_flagged(ctx):
         ctx.check()
     assert e.value.code == dk.DSPARK_EDEVICE and "packed" in str(e.value)
     ctx.check()   # the flag is cleared
+
+
+def draw_packed_cases(n=10, seed=5150):
+    """Markov-head shapes drawn once from a fixed seed for the packed layout:
+    batch sizes on both sides of the shared-tile threshold, ragged
+    vocabularies, ranks, both weight types, greedy and sampling."""
+    rs = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        wdtype = "bf16" if rs.random() < 0.7 else "f32"
+        r = int(rs.choice([64, 128, 256]))
+        B = int(rs.choice([1, 9, 33, 70, 100, 128]))
+        G = int(rs.integers(1, 10))
+        V = 16 * int(rs.integers(1, 300))
+        T = float(rs.choice([0.0, 0.8, 1.0]))
+        out.append((f"p{i}_{wdtype}_r{r}_B{B}_g{G}_V{V}_T{T}", dict(wdtype=wdtype, r=r, B=B, gamma=G, V=V,
+                                                                   temperature=T)))
+    return out
+
+
+PACKED_CASES = draw_packed_cases()
+
+
+@pytest.mark.parametrize("name,over", PACKED_CASES, ids=[c[0] for c in PACKED_CASES])
+def test_packed_shape(ctx, name, over):
+    wl = synth.WORKLOADS["sample"].with_(**over, conf=False, peak=None,
+                                         u_std=3.0 if over["wdtype"] == "bf16" else 2.0)
+    inp = synth.make_inputs(wl, seed=wl.seed + 71)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    rs = np.random.default_rng(len(name))
+    K = rs.integers(0, wl.gamma + 1, size=wl.B).astype(np.int32)
+    Kd = torch.from_numpy(K).cuda()
+    packed, offs = pack(inp["target"], K, order=list(rs.permutation(wl.B)))
+    T, seed = wl.temperature, 606
+    print(f"packed shape {name}: rows={packed.shape[0]}", flush=True)
+    tok, lse, ytok = ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, seed, wl.gamma)
+    a1, o1 = ctx.verify(d["target"], d["U"], d["W1"], d["W2"], d["anchor"], tok, lse, ytok, Kd, d["req_ids"],
+                        T, seed)
+    a2, o2 = ctx.verify_packed(packed.cuda(), torch.from_numpy(offs).cuda(), d["U"], d["W1"], d["W2"], d["anchor"],
+                               tok, lse, ytok, Kd, d["req_ids"], T, seed)
+    ctx.check()
+    assert torch.equal(a1, a2) and torch.equal(o1, o2)
+    od = oracle.draft_markov(inp["U"], inp["W1"], inp["W2"], inp["anchor"], inp["req_ids"], T, seed, wl.gamma)
+    rep, taint = compare_draft(tok.cpu().numpy(), lse.cpu().numpy(), ytok.cpu().numpy(), od)
+    ov = oracle.verify(inp["target"], od.tokens, od.lse, od.ytok, inp["U"], inp["W1"], inp["W2"], inp["anchor"], K,
+                       inp["req_ids"], T, seed, wl.gamma)
+    compare_verify(a2.cpu().numpy(), o2.cpu().numpy(), ov, taint, K, None, rep)
+    print(rep.summary(), flush=True)
+    assert rep.ok(), rep.summary()
