@@ -4,6 +4,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -74,6 +75,9 @@ struct dspark_ctx {
   // verify: last target row of each window but the final one (window k covers
   // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list
   int verify_win[8] = {3, 0, 0, 0, 0, 0, 0, 0};
+  // later windows walk a list of the pending requests (else one workgroup per
+  // row chunk of every request, most of which find it decided)
+  bool verify_list = true;
   // draft: running best (key, index) per (position, request), zero between calls
   unsigned long long* best = nullptr;
   size_t best_n = 0;
@@ -608,6 +612,8 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   off += align256((size_t)B * sizeof(float));
   const size_t off_vs = off;
   off += align256((size_t)B * sizeof(int2));
+  const size_t off_list = off;                          // two pending-request lists
+  off += 2 * align256((size_t)(B + 1) * sizeof(int));
   if ((rc = ensure_ws(c, off))) return rc;
   char* ws = static_cast<char*>(c->ws);
   float4* rpf = reinterpret_cast<float4*>(ws + off_rpf);
@@ -617,6 +623,8 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   int32_t* resid_k = reinterpret_cast<int32_t*>(ws + off_rk);
   float* resid_lt = reinterpret_cast<float*>(ws + off_rlt);
   int2* vstate = reinterpret_cast<int2*>(ws + off_vs);
+  int* lists[2] = {reinterpret_cast<int*>(ws + off_list),
+                   reinterpret_cast<int*>(ws + off_list + align256((size_t)(B + 1) * sizeof(int)))};
 
   const float invT = greedy ? 1.0f : 1.0f / temperature;
   for (int w = 0; w < n_win; ++w) {
@@ -632,6 +640,9 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
     va.hi = win_hi[w];
     va.first = w == 0;
     va.vstate = vstate;
+    // later windows walk the requests the previous window left pending
+    va.list_in = (w > 0 && c->verify_list) ? lists[(w - 1) % 2] : nullptr;
+    va.list_out = (w + 1 < n_win && c->verify_list) ? lists[w % 2] : nullptr;
     va.T = target;
     va.tsb = t_stride_b;
     va.toffs = toffs;
@@ -652,8 +663,10 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
     va.resid_k = resid_k;
     va.resid_lt = resid_lt;
     va.err = c->dev_err;
-    if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), dim3(n_chunks, B * nrows), dim3(kRowsThreads), &va,
-                      stream)))
+    const long all_tasks = (long)n_chunks * B * nrows;
+    const dim3 rgrid = va.list_in ? dim3((unsigned)std::min<long>(all_tasks, 8L * c->cu_count))
+                                  : dim3(n_chunks, B * nrows);
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), rgrid, dim3(kRowsThreads), &va, stream)))
       return rc;
     if ((rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &va, stream))) return rc;
   }
@@ -881,6 +894,8 @@ int dspark_create(dspark_ctx** out, int device) {
   ring_knob("DSPARK_GRU_RING", c->gru_nt, c->gru_depth);
   ring_knob("DSPARK_RESID_RING", c->resid_nt, c->resid_depth);
   // verify windows: "e1,e2,..." increasing last rows of all windows but the final one
+  const char* vl = getenv("DSPARK_VERIFY_LIST");
+  if (vl && vl[0] == '0' && vl[1] == 0) c->verify_list = false;
   const char* vw = getenv("DSPARK_VERIFY_WINDOWS");
   if (vw) {
     int tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};

@@ -87,6 +87,13 @@ struct VerifyArgs {
   int lo, hi;                    // 1-based rows of this window
   int first;                     // first window: every request starts at row 1
   int2* vstate;                  // per request {accepted so far, next row (0 = done)}
+  // later windows: the requests still pending ([0] = count, then their ids),
+  // appended by the previous window's decisions; null = one workgroup per
+  // (chunk, request, row) of the window.  list_out: where this window's
+  // decisions append (its count is cleared by this window's rows pass), or
+  // null for the last window.
+  const int* list_in;
+  int* list_out;
   const float* T;
   int64_t tsb, tsk;
   const int32_t* toffs;          // packed target rows: first row of each request, or null

@@ -2,7 +2,8 @@
 // (one partial per 32 KB chunk), then one wave per request that merges its
 // rows and takes its accept decisions.  Rows are taken in windows: a row
 // after a request's first rejection is never needed, so a later window only
-// reads rows of requests that have accepted every position so far.
+// reads rows of requests that have accepted every position so far (listed
+// by the previous window's decisions).
 //
 // [blog] "形式化定义": the target scores every drafted position in one pass,
 // positions are checked in order, the first rejected one is replaced by a
@@ -101,13 +102,10 @@ __device__ __forceinline__ void row_chunk(RowState& st, const float4* p, int c0,
   }
 }
 
-// One workgroup per (row chunk): the chunk's partial (max, sum, key, index).
-__global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArgs a) {
-  const int nrows = a.hi - a.lo + 1;
-  const int chunk = blockIdx.x;
-  const int b = blockIdx.y / nrows;
-  const int k = a.lo + blockIdx.y % nrows;
-  if (!a.first && a.vstate[b].y == 0) return;   // request already decided
+// The partial (max, sum, key, index) of one 32 KB chunk of target row
+// (b, k), from the whole workgroup.  Rows past K_b + 1 are skipped (the
+// condition is uniform over the workgroup).
+__device__ __forceinline__ void row_task(const VerifyArgs& a, int b, int k, int chunk, RowState* red) {
   const int kb = clamp_k(a.K, b, a.gamma, a.err, a.first && chunk == 0 && k == 1 && threadIdx.x == 0);
   if (k > kb + 1) return;
   const int64_t row = (int64_t)b * (a.gamma + 1) + (k - 1);
@@ -129,7 +127,6 @@ __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArg
   }
   // wave reduction, then across the four waves in a fixed order
   wave_row_reduce(st);
-  __shared__ RowState red[kRowsThreads / 64];
   const int wid = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wid] = st;
   __syncthreads();
@@ -140,6 +137,32 @@ __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArg
     const int64_t o = row * a.n_chunks + chunk;
     a.pf[o] = make_float4(acc.m, acc.s, acc.key, 0.f);
     a.pi[o] = acc.idx;
+  }
+  __syncthreads();                                       // red is reused by the next task
+}
+
+// Row pass of one window.  Without a work list: one workgroup per (chunk,
+// request, row).  With one (later windows): a fixed grid walks the tasks
+// (pending request, row, chunk) of the listed requests, so the requests
+// already decided cost no workgroups.
+__global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArgs a) {
+  __shared__ RowState red[kRowsThreads / 64];
+  const int nrows = a.hi - a.lo + 1;
+  if (a.list_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.list_out[0] = 0;
+  if (!a.list_in) {
+    const int chunk = blockIdx.x;
+    const int b = blockIdx.y / nrows;
+    const int k = a.lo + blockIdx.y % nrows;
+    if (!a.first && a.vstate[b].y == 0) return;   // request already decided
+    row_task(a, b, k, chunk, red);
+    return;
+  }
+  const int per = nrows * a.n_chunks;
+  const int n_tasks = a.list_in[0] * per;
+  for (int t = blockIdx.x; t < n_tasks; t += gridDim.x) {
+    const int i = t / per;
+    const int rem = t - i * per;
+    row_task(a, a.list_in[1 + i], a.lo + rem / a.n_chunks, rem % a.n_chunks, red);
   }
 }
 
@@ -237,7 +260,10 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
   } else if (kb + 1 <= a.hi) {
     final_tok = __shfl(my_star, kb + 1 - a.lo, 64);        // every draft kept: bonus from row K_b + 1
   } else {
-    if (lane == 0) a.vstate[b] = make_int2(A, a.hi + 1);    // rows left: wait for the next window
+    if (lane == 0) {
+      a.vstate[b] = make_int2(A, a.hi + 1);                // rows left: wait for the next window
+      if (a.list_out) a.list_out[1 + atomicAdd(a.list_out, 1)] = b;
+    }
     return;
   }
   for (int i = A + 1 + lane; i <= a.gamma; i += 64) out[i] = -1;
