@@ -436,7 +436,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (bf16 weights, bf16 MFMA with f32 accumulation)",
+        "dtype": "f32",
+        "dtype_detail": "f32 logits and statistics; bf16 weights through bf16 MFMA with f32 accumulation",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={B} gamma={G} V={V} r={r} T={T}"
                                + (" GRU head" if gru is not None else " Markov head")
