@@ -18,6 +18,11 @@
  *    Outputs are valid once the stream reaches the call.  Calls on one
  *    context must not run concurrently on different streams (the context's
  *    workspace is shared); a context is used by one host thread at a time.
+ *  - The calls enqueue kernels only (no memset, no host synchronisation once
+ *    the context's workspace has grown to the shape), so a caller may capture
+ *    them into a HIP graph after one call of the same shapes on the context;
+ *    a replay re-runs the captured arguments (pointers, seed).  The
+ *    cooperative launch (DSPARK_PERSIST_COOP=1) is not for capture.
  *  - Row-major layouts; strides are in elements.  Logit rows (U, target) are
  *    contiguous over the vocabulary and 16-byte aligned.
  *  - Tokens and request ids are 32-bit.  Request ids are read as unsigned.

@@ -264,7 +264,14 @@ def test_graph_and_direct_launch_agree(ctx, full_sample):
         c2 = dk.Context(0)
     finally:
         del os.environ["DSPARK_GRAPH"]
-    b = gpu_step(c2, d, seed=7)
-    c2.close()
-    for k in a:
-        assert np.array_equal(a[k], b[k]), k
+    try:
+        # several launches of the cached graph (its parameters rewritten per
+        # call), with direct-launch work between them, each against the
+        # direct result of the same seed
+        for seed in (7, 8, 7):
+            want = a if seed == 7 else gpu_step(ctx, d, seed=seed)
+            got = gpu_step(c2, d, seed=seed)
+            for k in want:
+                assert np.array_equal(want[k], got[k]), (seed, k)
+    finally:
+        c2.close()
