@@ -21,8 +21,9 @@
  *  - The calls enqueue kernels only (no memset, no host synchronisation once
  *    the context's workspace has grown to the shape), so a caller may capture
  *    them into a HIP graph after one call of the same shapes on the context;
- *    a replay re-runs the captured arguments (pointers, seed).  The
- *    cooperative launch (DSPARK_PERSIST_COOP=1) is not for capture.
+ *    a replay re-runs the captured arguments (pointers, seed).  Neither the
+ *    cooperative launch (DSPARK_PERSIST_COOP=1) nor the library's own graph
+ *    of the draft loop (DSPARK_GRAPH=1) is meant for capture.
  *  - Row-major layouts; strides are in elements.  Logit rows (U, target) are
  *    contiguous over the vocabulary and 16-byte aligned.
  *  - Tokens and request ids are 32-bit.  Request ids are read as unsigned.
