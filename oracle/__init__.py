@@ -21,7 +21,8 @@ section:
 Pins (tests/test_oracle_*.py) tie each function to something other than
 itself: published RNG test vectors, closed forms, the P3 one-hot matrix form of
 the bias, exact enumeration of the lossless law, Monte-Carlo chi-square
-against softmax / target laws, brute-force scheduling, and hand-worked
+against softmax / target laws, brute-force scheduling, scikit-learn's reliability curve (for the
+calibration error), recovery of known temperatures, and hand-worked
 fixtures under tests/golden/.
 """
 from .rng import (DRAFT, ACCEPT, RESID, BONUS, mix64, splitmix64_next, fmix32, row_key,
@@ -33,11 +34,12 @@ from .confidence import confidence, ConfidenceResult
 from .schedule import schedule, schedule_async, ScheduleResult
 from .verify import verify, VerifyResult, target_logprobs, accept_ratio, residual_weights, accept_prob
 from .step import run_step, StepResult
+from .sts_fit import ece, labels, candidate_scores, sts_fit, StsFit
 
 __all__ = [
     "DRAFT", "ACCEPT", "RESID", "BONUS", "mix64", "splitmix64_next", "fmix32", "row_key",
     "uniforms", "uniform_at", "gumbels", "race_draw", "group_keys", "decode_weights", "markov_bias", "draft_markov", "gru_cell", "draft_rnn",
     "DraftResult", "confidence", "ConfidenceResult", "schedule", "schedule_async", "ScheduleResult", "verify",
     "VerifyResult", "target_logprobs", "accept_ratio", "residual_weights", "accept_prob", "run_step",
-    "StepResult",
+    "StepResult", "ece", "labels", "candidate_scores", "sts_fit", "StsFit",
 ]

@@ -40,6 +40,17 @@ Layouts (row-major, contiguous):
   sps       : float32 [n_sps]   (SPS[N-1] for a verify batch of N tokens)
   GRU head  : W_ih, W_hh bf16 [3r][r] (gate rows in the order reset, update,
               new), b_ih, b_hh bf16 [3r], s0 bf16 [r]
+
+Calibration sets for fitting the per-position confidence temperatures
+(``sts_calibration_set``): N held-out drafts of gamma positions.  The world
+they come from: each position of each draft has a true acceptance
+probability p ~ Beta(8 m_k, 8 (1 - m_k)) with m_k = 0.85 - 0.03 (k - 1)
+(clipped to [1e-6, 1 - 1e-6]); the head reports the over-confident logit
+T*_k * ln(p / (1 - p)), rounded to float32, with T*_k ~ U[1, 2] per position
+(the spread of the STS temperatures above); acceptance events are
+independent draws u < p in position order and the accepted length is the
+number of leading accepted positions.  The candidate temperatures of the
+grid search (``sts_grid``) are 0.5, 0.55, ... (64 values, float32).
 """
 from __future__ import annotations
 
@@ -47,6 +58,7 @@ import dataclasses
 import math
 from typing import Optional
 
+import numpy as np
 import torch
 
 
@@ -192,3 +204,27 @@ def survival_rows(B: int, gamma: int, seed: int, *, ties: bool = False) -> torch
         x = torch.ceil(x * 8.0) / 8.0
     x, _ = torch.sort(x, dim=1, descending=True)
     return x.contiguous()
+
+
+def sts_calibration_set(N: int, gamma: int, seed: int, true_T=None) -> dict:
+    """Held-out drafts with labels, drawn from the world stated in the module
+    header.  Returns logit float32 [N][gamma], accept_len int32 [N] (0..gamma)
+    and true_T float64 [gamma] (the over-confidence factors of the head)."""
+    rs = np.random.default_rng(seed)
+    if true_T is None:
+        true_T = 1.0 + rs.random(gamma)
+    else:
+        true_T = np.asarray(true_T, dtype=np.float64).reshape(gamma)
+    m = 0.85 - 0.03 * np.arange(gamma)
+    p = np.clip(rs.beta(8.0 * m, 8.0 * (1.0 - m), size=(N, gamma)), 1e-6, 1.0 - 1e-6)
+    u = rs.random((N, gamma))
+    logit = (true_T[None, :] * np.log(p / (1.0 - p))).astype(np.float32)
+    # accepted length: the leading run of accepted positions
+    accept_len = np.cumprod(u < p, axis=1).sum(axis=1).astype(np.int32)
+    return {"logit": torch.from_numpy(np.ascontiguousarray(logit)),
+            "accept_len": torch.from_numpy(accept_len), "true_T": torch.from_numpy(true_T)}
+
+
+def sts_grid(n: int = 64, lo: float = 0.5, step: float = 0.05) -> torch.Tensor:
+    """Candidate temperatures lo, lo + step, ... as float32."""
+    return (lo + step * torch.arange(n, dtype=torch.float64)).to(torch.float32)
