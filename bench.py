@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--draft-crossover", action="store_true",
                     help="time draft calls of the whole-draft kernel against the per-position sweeps over batch "
                          "sizes (instead of the step benchmark)")
+    ap.add_argument("--sts-fit", action="store_true",
+                    help="time the per-position temperature fit on a held-out set of 2^20 drafts "
+                         "(gamma 7, 64 candidates, 15 bins) instead of the step benchmark; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer a few times: the reference kernel of known "
                          "traffic used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -120,6 +123,80 @@ def draft_crossover(seed: int):
     sweeps.close()
 
 
+# ALU roofline of the temperature fit's scoring pass: a candidate evaluation
+# needs at least 8 full-rate fp32 operations (scale the logit, 1 + e, times
+# the prefix, times M, floor, clamp, label - score, accumulate) and 2
+# transcendental ones (exponential, reciprocal) at a quarter of that rate:
+# 16 issue slots of one lane.  The chip issues 256 CUs x 4 SIMDs x 16 lanes
+# x 2.4 GHz = 39.3 T non-packed lane operations per second.
+ALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
+STS_SLOTS_PER_EVAL = 16
+STS_PEAK_GEVALS = ALU_LANE_OPS_PER_S / STS_SLOTS_PER_EVAL / 1e9
+
+
+def sts_fit_bench(args):
+    """Fit of the per-position confidence temperatures on a synthetic held-out
+    set: N = 2^20 drafts of gamma = 7 positions, 64 candidate temperatures,
+    15 bins.  value = candidate evaluations (N x candidates x positions) per
+    second of whole fits."""
+    import torch
+    import synth
+    import semi_ar_draft_amd as dk
+
+    N, G, n_grid, M = 1 << 20, 7, 64, 15
+    d = synth.sts_calibration_set(N, G, seed=2024)
+    grid = synth.sts_grid(n_grid)
+    l, a, gd = d["logit"].cuda(), d["accept_len"].cuda(), grid.cuda()
+    ctx = dk.Context(0)
+    out = (torch.empty((G,), dtype=torch.float32, device="cuda"), torch.empty((G,), dtype=torch.int32, device="cuda"),
+           torch.empty((G, n_grid), dtype=torch.float64, device="cuda"))
+    steps, warmup = max(args.steps, 1), max(args.warmup, 0)
+    for _ in range(warmup):
+        ctx.sts_fit(l, a, gd, M, out=out)
+    ctx.check()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ctx.sts_fit(l, a, gd, M, out=out)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    ctx.check()
+    evals = N * n_grid * G
+    # per-kernel durations: events attached to each dispatch
+    ctx.timing(True)
+    ctx.read_timing()
+    for _ in range(steps):
+        ctx.sts_fit(l, a, gd, M, out=out)
+    tm = ctx.read_timing()
+    ctx.timing(False)
+    ctx.check()
+    h_ms, h_n = tm["sts_hist"]
+    s_ms, s_n = tm["sts_select"]
+    hist_us = 1e3 * h_ms / h_n
+    achieved = N * n_grid / (hist_us * 1e-6) / 1e9          # Geval/s of one scoring pass
+    line = {
+        "metric": "STS temperature fit: candidate evaluations/sec (drafts x candidates x positions)",
+        "value": evals / (ms * 1e-3), "unit": "evaluations/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "sts_fit", "N": N, "gamma": G, "candidates": n_grid, "bins": M},
+        "roofline": {"bound": "alu", "kernel": "sts_hist", "achieved": achieved, "peak": STS_PEAK_GEVALS,
+                     "unit": "Geval/s", "frac": achieved / STS_PEAK_GEVALS, "traffic": None},
+        "kernels_us": {"sts_hist_per_position": hist_us, "sts_select_per_launch": 1e3 * s_ms / s_n},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        ns = 1 << 17
+        ll, aa, gg = d["logit"][:ns].numpy(), d["accept_len"][:ns].numpy(), grid.numpy()
+        t0 = time.perf_counter()
+        oracle.sts_fit(ll, aa, gg, M)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": ns * n_grid * G / dt, "unit": "evaluations/s", "cores": 1,
+                                "kind": "oracle", "sample": f"the first {ns} drafts of the same set, one fit"}
+    ctx.close()
+    print(json.dumps(line), flush=True)
+
+
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "draft_sweep_traffic_B128_V151936_r256_T1.json")
 
@@ -164,6 +241,12 @@ def main():
         return
     if args.draft_crossover:
         draft_crossover(args.seed)
+        return
+    if args.sts_fit:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        sts_fit_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

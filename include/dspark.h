@@ -85,7 +85,8 @@ const char* dspark_last_error(const dspark_ctx* ctx);
 
 /* Synchronise `stream`, read and clear the device error flag.  Returns
  * DSPARK_EDEVICE if any kernel since the last check met an out-of-range
- * token id or verify length, or a grid barrier of the whole-draft kernel
+ * token id, verify length or accepted length, a bad candidate temperature
+ * (dspark_sts_fit), or a grid barrier of the whole-draft kernel
  * gave up waiting (see dspark_draft_markov; the message names which),
  * DSPARK_EHIP on a HIP error, else DSPARK_OK. */
 int dspark_check(dspark_ctx* ctx, hipStream_t stream);
@@ -114,7 +115,9 @@ enum {
   DSPARK_K_RESID_COMBINE = 8,
   DSPARK_K_GRU = 9,            /* GRU head: s_0 fill and state updates */
   DSPARK_K_DIAG = 10,          /* diagnostic passes (dspark_accept_prob) */
-  DSPARK_K_COUNT = 11
+  DSPARK_K_STS_HIST = 11,      /* temperature fit: scoring pass of one position */
+  DSPARK_K_STS_SELECT = 12,    /* temperature fit: clearing and selection */
+  DSPARK_K_COUNT = 13
 };
 int dspark_timing_enable(dspark_ctx* ctx, int enable);
 int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
@@ -346,6 +349,50 @@ int dspark_verify_packed(dspark_ctx* ctx, hipStream_t stream,
                          const float* states, const int32_t* K, const uint32_t* req_ids,
                          float temperature, uint64_t seed,
                          int32_t* accept_len, int32_t* out_tokens);
+
+/* Fit the per-position confidence temperatures (sequential temperature
+ * scaling) on held-out drafts.
+ *
+ * [blog] "校准问题：原始置信度不可靠" and [summary] section 4: for k = 1 ..
+ * gamma in order, T_k is the candidate temperature whose calibrated survival
+ *     S_n(T) = prod_{i<k} sigmoid(l[n][i] / T_i) * sigmoid(l[n][k-1] / T)
+ * has the lowest expected calibration error against the labels
+ * y_n = [accept_len[n] >= k] (the first k drafted tokens of sample n were
+ * accepted); T_1 .. T_{k-1} are the temperatures already fitted.  The error
+ * is the binned one with n_bins equal-width bins on [0, 1] (sample n in bin
+ * min(floor(S_n n_bins), n_bins - 1)):
+ *     ECE = sum over bins of (n_m / N) |mean label - mean score|
+ *         = sum over bins of |sum_{n in bin} (y_n - S_n)| / N,
+ * and 0 when N == 0.  Ties go to the lowest candidate index.  The result is
+ * what dspark_confidence takes as sts_T.
+ *
+ * N >= 0 samples (at most 2^33); 1 <= gamma <= 32.
+ * logit:      float [N][stride] (stride >= gamma): the confidence head's
+ *             logits l = logit(c) before any temperature, positions 1..gamma
+ *             in columns 0..gamma-1.  May be NULL when N == 0.
+ * accept_len: int32 [N], accepted draft lengths in 0..gamma (verification
+ *             of all gamma positions).  May be NULL when N == 0.
+ * grid:       float [n_grid] candidate temperatures, each positive and
+ *             finite; 1 <= n_grid <= 256, 1 <= n_bins <= 64,
+ *             n_grid * n_bins <= 4096.
+ * T:          float [gamma] out: the fitted temperatures (values of grid).
+ * index:      int32 [gamma] out: their indices in grid.
+ * ece:        double [gamma][n_grid] out: the error of every candidate at
+ *             every position (given the earlier fitted temperatures).
+ * Arithmetic: scores in fp32 (hardware exponential and reciprocal); each
+ * sum of (y - S) is accumulated exactly as an integer of 2^-30 units
+ * (per-sample truncation), so results do not depend on the order in which
+ * the workgroups finish.  A score within a few fp32 ulps of a bin edge may
+ * fall in the neighbouring bin of an exact evaluation.
+ * Errors: DSPARK_EINVAL for shapes, limits and null pointers; ENOMEM if the
+ * workspace (8 * n_grid * n_bins bytes) cannot grow.  A candidate that is
+ * not positive and finite or an accepted length outside [0, gamma] (clamped)
+ * raises the device error flag (dspark_check).  Launches 1 + 2 gamma kernels
+ * (timing classes DSPARK_K_STS_HIST and DSPARK_K_STS_SELECT). */
+int dspark_sts_fit(dspark_ctx* ctx, hipStream_t stream, int64_t N, int gamma,
+                   const float* logit, int64_t stride, const int32_t* accept_len,
+                   const float* grid, int n_grid, int n_bins,
+                   float* T, int32_t* index, double* ece);
 
 #ifdef __cplusplus
 }

@@ -23,11 +23,11 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
     "dspark_draft_markov", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
-    "dspark_verify_packed", "dspark_accept_prob",
+    "dspark_verify_packed", "dspark_accept_prob", "dspark_sts_fit",
     "dspark_timing_enable", "dspark_timing_read",
 )
 KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
-                  "verify_rows", "verify_decide", "resid_sweep", "resid_combine", "gru", "diag")
+                  "verify_rows", "verify_decide", "resid_sweep", "resid_combine", "gru", "diag", "sts_hist", "sts_select")
 
 _lib = None
 _vp, _i32, _i64, _u64, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
@@ -91,6 +91,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_accept_prob.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
         _vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp]
+    lib.dspark_sts_fit.restype = _i32
+    lib.dspark_sts_fit.argtypes = [
+        _vp, _vp, _i64, _i32, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
     if path is None:
         _lib = lib
     return lib
@@ -445,6 +448,34 @@ class Context:
             U.data_ptr(), usb, usk, _ptr(W1), W2.data_ptr(), _ptr(anchor), tokens.data_ptr(), lse.data_ptr(),
             _ptr(states), float(temperature), out.data_ptr()))
         return out
+
+    # -- dspark_sts_fit ---------------------------------------------------------------
+    def sts_fit(self, logit, accept_len, grid, n_bins: int, out=None, stream=None):
+        """Per-position temperatures by ECE grid search on held-out drafts.
+
+        logit: float32 [N][gamma] (row stride >= gamma); accept_len: int32 [N];
+        grid: float32 [n_grid] candidates.  Returns (T float32 [gamma],
+        index int32 [gamma], ece float64 [gamma][n_grid])."""
+        dev = self.device
+        _need(logit, "logit", torch.float32, dev, 2, contiguous=False)
+        if logit.stride(1) != 1:
+            raise ValueError("logit rows must be contiguous over positions")
+        N, gamma = logit.shape
+        _need(accept_len, "accept_len", torch.int32, dev, 1)
+        _len(accept_len, N, "accept_len")
+        _need(grid, "grid", torch.float32, dev, 1)
+        n_grid = grid.shape[0]
+        if out is None:
+            out = (torch.empty((gamma,), dtype=torch.float32, device=dev),
+                   torch.empty((gamma,), dtype=torch.int32, device=dev),
+                   torch.empty((gamma, n_grid), dtype=torch.float64, device=dev))
+        T, idx, ece = out
+        stride = logit.stride(0) if N > 0 else gamma
+        self._rc(self.lib.dspark_sts_fit(
+            self._h, _stream(dev, stream), N, gamma, logit.data_ptr() if N > 0 else None, stride,
+            accept_len.data_ptr() if N > 0 else None, grid.data_ptr(), n_grid, int(n_bins),
+            T.data_ptr(), idx.data_ptr(), ece.data_ptr()))
+        return T, idx, ece
 
 
 __all__ = ["Context", "DSparkError", "load_library", "LIB_PATH", "EXPORTS", "KERNEL_CLASSES",

@@ -21,6 +21,8 @@ constexpr int kErrToken = 1;    // a token id outside [0, V)
 constexpr int kErrK = 2;        // a verify length outside [0, gamma]
 constexpr int kErrRow = 4;      // a packed target row outside [0, n_rows)
 constexpr int kErrBarrier = 8;  // a grid barrier of the whole-draft kernel gave up waiting
+constexpr int kErrGrid = 16;    // a candidate temperature that is not positive and finite
+constexpr int kErrLen = 32;     // an accepted length outside [0, gamma] (temperature fit)
 
 // Element offset of target row (b, k) (k 1-based): strided [B][gamma+1][V]
 // placement, or the packed layout where request b's rows 1 .. K_b + 1 start

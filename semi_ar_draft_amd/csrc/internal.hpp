@@ -117,6 +117,31 @@ struct VerifyArgs {
 
 constexpr int kMaxGamma = 32;   // longest draft (positions per request)
 
+// Temperature fit (sequential temperature scaling): one position k per
+// histogram pass.  hist holds n_bins x n_grid signed sums of (label - score)
+// in 2^-30 units (two's complement in 64 bits), bin-major.
+constexpr int kStsThreads = 256;
+constexpr int kStsWaves = kStsThreads / 64;
+constexpr int kStsMaxSlices = 4;                 // candidates per lane: n_grid <= 256
+constexpr int kStsMaxGrid = 64 * kStsMaxSlices;
+constexpr int kStsMaxBins = 64;
+constexpr int kStsMaxCells = 4096;               // n_bins * n_grid (32 KB of LDS)
+
+struct StsArgs {
+  int64_t N;
+  int gamma, k;                  // k: 1-based position fitted by this pass
+  int n_grid, n_bins;
+  int64_t stride;                // row stride of logit (elements)
+  const float* logit;            // [N][stride]
+  const int32_t* len;            // [N]
+  const float* grid;             // [n_grid]
+  float* T;                      // [gamma]: T[0 .. k-2] read, T[k-1] written
+  int32_t* index;                // [gamma]
+  double* ece;                   // [gamma][n_grid]
+  unsigned long long* hist;      // [n_bins][n_grid] (workspace)
+  int32_t* err;
+};
+
 struct ConfArgs {
   int B, gamma, V, dh, de;
   const uint16_t* h;
@@ -178,6 +203,10 @@ const void* rows_lse_kernel();
 const void* verify_rows_kernel();
 const void* verify_decide_kernel();
 const void* confidence_kernel();
+// temperature fit: clear the sums, one histogram pass and one selection per position
+const void* sts_clear_kernel();
+const void* sts_hist_kernel(int n_slices);   // candidates per lane: 1..4 slices of 64
+const void* sts_select_kernel();
 const void* gru_init_kernel();
 const void* gru_step_kernel(int r);
 int gru_step_threads(int r);   // workgroup size of gru_step_kernel(r)

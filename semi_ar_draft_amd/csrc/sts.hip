@@ -1,0 +1,206 @@
+// Fitting the per-position confidence temperatures (sequential temperature
+// scaling) by a grid search over candidate temperatures.
+//
+// [blog] "校准问题：原始置信度不可靠" and [summary] section 4: position by
+// position, left to right, the temperature is the candidate whose scaled
+// survival product prod_{i<k} sigmoid(l_i / T_i) * sigmoid(l_k / T) has the
+// lowest expected calibration error (ECE) against the measured acceptance of
+// positions 1..k, the earlier positions keeping the temperatures already
+// chosen.  ECE uses M equal-width bins on [0, 1] (bin min(floor(S M), M-1)).
+//
+// The work is N samples x n_grid candidates of one scaled sigmoid, a bin
+// decision and an accumulation per position: plain ALU work (an exponential
+// and a reciprocal on the transcendental unit), with 4 bytes of logit read
+// per sample and candidate row.  Two facts shape the kernels:
+//  - a bin's share of the ECE is |sum over the bin of (label - score)| / N,
+//    so one signed sum per (bin, candidate) is all that is kept; it is
+//    accumulated as a 64-bit integer of 2^-30 units, so the sums, and the
+//    choice of temperature, do not depend on the order of the atomics;
+//  - the lanes of a wave are 64 candidates and the samples are broadcast to
+//    them (readlane), so lane g always adds into column g of the histogram:
+//    the 64-bit LDS atomics of one instruction never share an address.
+#include <float.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace dspark {
+namespace {
+
+constexpr float kStsScale = 1073741824.f;      // 2^30 fixed-point units per score unit
+constexpr double kStsScaleD = 1073741824.0;
+
+// sigmoid(x / T) with c = -log2(e) / T: 1 / (1 + 2^(x c))
+__device__ __forceinline__ float scaled_sigmoid(float x, float c) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * c));
+}
+
+// Clear the (bin, candidate) sums of the call's first position.
+__global__ __launch_bounds__(256) void sts_clear_impl(StsArgs a) {
+  const int cells = a.n_bins * a.n_grid;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < cells; i += gridDim.x * 256) a.hist[i] = 0ull;
+}
+
+// One position: every wave takes blocks of 64 samples, stages each sample's
+// (logit at k, prefix under the fitted earlier temperatures, label) in LDS,
+// and then walks them one by one, all 64 lanes (NS slices of 64 candidates)
+// scoring the same sample.  Sums of (label - score) per (bin, candidate)
+// build up in LDS and are added into the global ones at the end.  Lanes
+// past the last candidate add into a spare column that is never read.
+template <int NS>
+__global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
+  __shared__ unsigned long long h[kStsMaxCells + 64];
+  __shared__ float4 samp[kStsWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int ng = a.n_grid, nb = a.n_bins;
+  const int cells = nb * ng;
+  for (int i = threadIdx.x; i < cells; i += kStsThreads) h[i] = 0ull;
+
+  // the lane's candidates g = lane + 64 s: c = -log2(e) / T_g, and the LDS
+  // byte address of (bin, g) = bin * mul + base
+  float cg[NS];
+  unsigned mul[NS], base[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int g = lane + 64 * s;
+    if (g < ng) {
+      const float t = a.grid[g];
+      if (!(t > 0.f) || !(t <= FLT_MAX)) atomicOr(a.err, kErrGrid);
+      cg[s] = -kLog2e / t;
+      mul[s] = (unsigned)ng * 8u;
+      base[s] = (unsigned)g * 8u;
+    } else {
+      cg[s] = 0.f;
+      mul[s] = 0u;
+      base[s] = (unsigned)(kStsMaxCells + lane) * 8u;
+    }
+  }
+  __syncthreads();
+
+  const float fM = (float)nb;
+  const float fTop = (float)(nb - 1);
+  const int k = a.k;
+  const int64_t N = a.N;
+  char* hb = reinterpret_cast<char*>(h);
+  for (int64_t b0 = ((int64_t)blockIdx.x * kStsWaves + wid) * 64; b0 < N;
+       b0 += (int64_t)gridDim.x * kStsWaves * 64) {
+    const int64_t n = b0 + lane;
+    float p = 0.f, l = 0.f, ys = 0.f;
+    if (n < N) {
+      const float* row = a.logit + n * a.stride;
+      float pre = 1.f;
+      for (int i = 0; i < k - 1; ++i) pre *= scaled_sigmoid(row[i], -kLog2e / a.T[i]);
+      p = pre;
+      l = row[k - 1];
+      int len = a.len[n];
+      if (len < 0 || len > a.gamma) {
+        atomicOr(a.err, kErrLen);
+        len = len < 0 ? 0 : a.gamma;
+      }
+      ys = len >= k ? kStsScale : 0.f;
+    }
+    // the wave's own staging row: its LDS accesses complete in order
+    samp[wid][lane] = make_float4(l, p, ys, 0.f);
+    __builtin_amdgcn_wave_barrier();
+    // eight samples are read ahead of their atomics; a sample past N has
+    // prefix 0, scores 0 with label 0 and so adds 0 (into bin 0)
+    for (int j0 = 0; j0 < 64; j0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = samp[wid][j0 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const float S = v[u].y * scaled_sigmoid(v[u].x, cg[s]);
+          const int bin = (int)__builtin_amdgcn_fmed3f(S * fM, 0.f, fTop);
+          const int q = (int)fmaf(S, -kStsScale, v[u].z);     // (label - S) in 2^-30 units
+          const unsigned addr = __umul24((unsigned)bin, mul[s]) + base[s];
+          atomicAdd(reinterpret_cast<unsigned long long*>(hb + addr), (unsigned long long)(long long)q);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < cells; i += kStsThreads) {
+    const unsigned long long v = h[i];
+    if (v) atomicAdd(&a.hist[i], v);
+  }
+}
+
+// One position: ECE of every candidate from the sums (clearing them for the
+// next position), the first minimiser, and its temperature.  The cells are
+// read all at once (16 independent loads per thread) into LDS as |sum|, then
+// each candidate adds its column in bin order.
+__global__ __launch_bounds__(256) void sts_select_impl(StsArgs a) {
+  __shared__ double cell[kStsMaxCells];
+  __shared__ double sv[256];
+  __shared__ int si[256];
+  const int ng = a.n_grid, nb = a.n_bins;
+  const int cells = ng * nb;
+  unsigned long long v[kStsMaxCells / 256];
+#pragma unroll
+  for (int u = 0; u < kStsMaxCells / 256; ++u) {
+    const int i = threadIdx.x + 256 * u;
+    v[u] = i < cells ? a.hist[i] : 0ull;
+  }
+#pragma unroll
+  for (int u = 0; u < kStsMaxCells / 256; ++u) {
+    const int i = threadIdx.x + 256 * u;
+    if (i < cells) {
+      const long long x = (long long)v[u];
+      cell[i] = (double)(x < 0 ? -x : x);
+      a.hist[i] = 0ull;
+    }
+  }
+  __syncthreads();
+  double bv = DBL_MAX;
+  int bi = 0x7fffffff;
+  for (int g = threadIdx.x; g < ng; g += 256) {
+    double s = 0.0;
+    for (int m = 0; m < nb; ++m) s += cell[m * ng + g];
+    const double e = a.N > 0 ? s / (kStsScaleD * (double)a.N) : 0.0;
+    a.ece[(int64_t)(a.k - 1) * ng + g] = e;
+    if (e < bv) {   // g grows along the loop: the first minimiser is kept
+      bv = e;
+      bi = g;
+    }
+  }
+  sv[threadIdx.x] = bv;
+  si[threadIdx.x] = bi;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      const double ov = sv[threadIdx.x + w];
+      const int oi = si[threadIdx.x + w];
+      if (ov < sv[threadIdx.x] || (ov == sv[threadIdx.x] && oi < si[threadIdx.x])) {
+        sv[threadIdx.x] = ov;
+        si[threadIdx.x] = oi;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int g = si[0];
+    if (g < 0 || g >= ng) g = 0;   // unreachable: every ECE is finite
+    a.T[a.k - 1] = a.grid[g];
+    a.index[a.k - 1] = g;
+  }
+}
+
+}  // namespace
+
+const void* sts_clear_kernel() { return (const void*)sts_clear_impl; }
+const void* sts_hist_kernel(int n_slices) {
+  switch (n_slices) {
+    case 1: return (const void*)sts_hist_impl<1>;
+    case 2: return (const void*)sts_hist_impl<2>;
+    case 3: return (const void*)sts_hist_impl<3>;
+    default: return (const void*)sts_hist_impl<4>;
+  }
+}
+const void* sts_select_kernel() { return (const void*)sts_select_impl; }
+
+}  // namespace dspark

@@ -44,8 +44,8 @@ Layouts (row-major, contiguous):
 Calibration sets for fitting the per-position confidence temperatures
 (``sts_calibration_set``): N held-out drafts of gamma positions.  The world
 they come from: each position of each draft has a true acceptance
-probability p ~ Beta(8 m_k, 8 (1 - m_k)) with m_k = 0.85 - 0.03 (k - 1)
-(clipped to [1e-6, 1 - 1e-6]); the head reports the over-confident logit
+probability p ~ Beta(8 m_k, 8 (1 - m_k)) with m_k = max(0.85 - 0.03 (k - 1),
+0.3) (p clipped to [1e-6, 1 - 1e-6]); the head reports the over-confident logit
 T*_k * ln(p / (1 - p)), rounded to float32, with T*_k ~ U[1, 2] per position
 (the spread of the STS temperatures above); acceptance events are
 independent draws u < p in position order and the accepted length is the
@@ -215,7 +215,7 @@ def sts_calibration_set(N: int, gamma: int, seed: int, true_T=None) -> dict:
         true_T = 1.0 + rs.random(gamma)
     else:
         true_T = np.asarray(true_T, dtype=np.float64).reshape(gamma)
-    m = 0.85 - 0.03 * np.arange(gamma)
+    m = np.maximum(0.85 - 0.03 * np.arange(gamma), 0.3)
     p = np.clip(rs.beta(8.0 * m, 8.0 * (1.0 - m), size=(N, gamma)), 1e-6, 1.0 - 1e-6)
     u = rs.random((N, gamma))
     logit = (true_T[None, :] * np.log(p / (1.0 - p))).astype(np.float32)

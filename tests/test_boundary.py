@@ -42,8 +42,18 @@ def test_library_embeds_gfx950_device_code():
     assert b"amdgcn-amd-amdhsa--gfx950" in blob
 
 
+def test_timing_classes_match_the_header():
+    import re
+    with open(HEADER) as f:
+        h = f.read()
+    n = int(re.search(r"DSPARK_K_COUNT\s*=\s*(\d+)", h).group(1))
+    assert n == len(dk.KERNEL_CLASSES)
+    ids = [int(v) for v in re.findall(r"DSPARK_K_[A-Z_]+\s*=\s*(\d+),", h)]
+    assert ids == list(range(n))
+
+
 def test_version():
-    assert dk.load_library().dspark_version() == 100
+    assert dk.load_library().dspark_version() == 101
 
 
 def test_null_context_is_rejected_everywhere():
@@ -66,6 +76,7 @@ def test_null_context_is_rejected_everywhere():
                                   None, None, None, 1.0, None) == dk.DSPARK_EINVAL
     assert lib.dspark_draft_rnn(None, None, 1, 1, 16, 32, 1, None, 16, 16, None, None, None, None, None,
                                 None, None, None, 0.0, 0, None, None, None, None) == dk.DSPARK_EINVAL
+    assert lib.dspark_sts_fit(None, None, 1, 1, None, 1, None, None, 1, 1, None, None, None) == dk.DSPARK_EINVAL
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU device node is present")
