@@ -74,9 +74,10 @@ struct dspark_ctx {
   int resid_nt = 1, resid_depth = 1;
   // temperature fit: scoring workgroups per CU (each flushes its n_bins x
   // n_grid sums into the global ones with 64-bit atomics).  Measured at 2^20
-  // drafts, 64 candidates, 15 bins: 57 / 44 / 41 / 59 us per position at
-  // 1 / 2 / 4 / 8 per CU.
-  int sts_wg_per_cu = 4;
+  // drafts, 64 candidates, 15 bins, us per position: 1024-thread workgroups
+  // 37.6 / 34.9 at 1 / 2 per CU; 512-thread 42.9 / 38.5 / 39.5 at 1 / 2 / 3;
+  // 256-thread 57 / 44 / 40 / 45 / 49 / 54 at 1 / 2 / 4 / 5 / 6 / 8.
+  int sts_wg_per_cu = 2;
   // verify: last target row of each window but the final one (window k covers
   // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list
   int verify_win[8] = {3, 0, 0, 0, 0, 0, 0, 0};
@@ -1161,7 +1162,7 @@ int dspark_sts_fit(dspark_ctx* c, hipStream_t stream, int64_t N, int gamma, cons
     return rc;
   for (int k = 1; k <= gamma; ++k) {
     a.k = k;
-    if ((rc = klaunch(c, DSPARK_K_STS_HIST, sts_hist_kernel((n_grid + 63) / 64), dim3(nwg), dim3(kStsThreads), &a, stream))) return rc;
+    if ((rc = klaunch(c, DSPARK_K_STS_HIST, sts_hist_kernel((n_grid + 63) / 64, cells), dim3(nwg), dim3(kStsThreads), &a, stream))) return rc;
     if ((rc = klaunch(c, DSPARK_K_STS_SELECT, sts_select_kernel(), dim3(1), dim3(256), &a, stream))) return rc;
   }
   return DSPARK_OK;

@@ -120,7 +120,9 @@ constexpr int kMaxGamma = 32;   // longest draft (positions per request)
 // Temperature fit (sequential temperature scaling): one position k per
 // histogram pass.  hist holds n_bins x n_grid signed sums of (label - score)
 // in 2^-30 units (two's complement in 64 bits), bin-major.
-constexpr int kStsThreads = 256;
+// 16 waves per workgroup: occupancy without more workgroups, since each
+// workgroup ends by adding its n_bins x n_grid sums into the global ones
+constexpr int kStsThreads = 1024;
 constexpr int kStsWaves = kStsThreads / 64;
 constexpr int kStsMaxSlices = 4;                 // candidates per lane: n_grid <= 256
 constexpr int kStsMaxGrid = 64 * kStsMaxSlices;
@@ -205,7 +207,7 @@ const void* verify_decide_kernel();
 const void* confidence_kernel();
 // temperature fit: clear the sums, one histogram pass and one selection per position
 const void* sts_clear_kernel();
-const void* sts_hist_kernel(int n_slices);   // candidates per lane: 1..4 slices of 64
+const void* sts_hist_kernel(int n_slices, int cells);   // 1..4 slices of 64 candidates per lane
 const void* sts_select_kernel();
 const void* gru_init_kernel();
 const void* gru_step_kernel(int r);

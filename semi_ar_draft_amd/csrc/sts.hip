@@ -47,9 +47,9 @@ __global__ __launch_bounds__(256) void sts_clear_impl(StsArgs a) {
 // scoring the same sample.  Sums of (label - score) per (bin, candidate)
 // build up in LDS and are added into the global ones at the end.  Lanes
 // past the last candidate add into a spare column that is never read.
-template <int NS>
+template <int NS, int CELLS>
 __global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
-  __shared__ unsigned long long h[kStsMaxCells + 64];
+  __shared__ unsigned long long h[CELLS + 64];
   __shared__ float4 samp[kStsWaves][64];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
     } else {
       cg[s] = 0.f;
       mul[s] = 0u;
-      base[s] = (unsigned)(kStsMaxCells + lane) * 8u;
+      base[s] = (unsigned)(CELLS + lane) * 8u;
     }
   }
   __syncthreads();
@@ -103,22 +103,32 @@ __global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
     // the wave's own staging row: its LDS accesses complete in order
     samp[wid][lane] = make_float4(l, p, ys, 0.f);
     __builtin_amdgcn_wave_barrier();
-    // eight samples are read ahead of their atomics; a sample past N has
-    // prefix 0, scores 0 with label 0 and so adds 0 (into bin 0)
+    // eight samples are read ahead of their atomics and scored phase by
+    // phase (eight independent exponentials, then reciprocals, ...), so the
+    // transcendental latencies overlap; a sample past N has prefix 0, scores
+    // 0 with label 0 and so adds 0 (into bin 0)
     for (int j0 = 0; j0 < 64; j0 += 8) {
       float4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = samp[wid][j0 + u];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int s = 0; s < NS; ++s) {
+        float S[8];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const float S = v[u].y * scaled_sigmoid(v[u].x, cg[s]);
-          const int bin = (int)__builtin_amdgcn_fmed3f(S * fM, 0.f, fTop);
-          const int q = (int)fmaf(S, -kStsScale, v[u].z);     // (label - S) in 2^-30 units
-          const unsigned addr = __umul24((unsigned)bin, mul[s]) + base[s];
-          atomicAdd(reinterpret_cast<unsigned long long*>(hb + addr), (unsigned long long)(long long)q);
+        for (int u = 0; u < 8; ++u) S[u] = __builtin_amdgcn_exp2f(v[u].x * cg[s]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) S[u] = v[u].y * __builtin_amdgcn_rcpf(1.f + S[u]);
+        unsigned addr[8];
+        int q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int bin = (int)__builtin_amdgcn_fmed3f(S[u] * fM, 0.f, fTop);
+          q[u] = (int)fmaf(S[u], -kStsScale, v[u].z);          // (label - S) in 2^-30 units
+          addr[u] = __umul24((unsigned)bin, mul[s]) + base[s];
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          atomicAdd(reinterpret_cast<unsigned long long*>(hb + addr[u]), (unsigned long long)(long long)q[u]);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -193,12 +203,21 @@ __global__ __launch_bounds__(256) void sts_select_impl(StsArgs a) {
 }  // namespace
 
 const void* sts_clear_kernel() { return (const void*)sts_clear_impl; }
-const void* sts_hist_kernel(int n_slices) {
+const void* sts_hist_kernel(int n_slices, int cells) {
+  // histogram of at most 1024 cells: 12.7 KB of LDS per workgroup instead of 37 KB
+  if (cells <= 1024) {
+    switch (n_slices) {
+      case 1: return (const void*)sts_hist_impl<1, 1024>;
+      case 2: return (const void*)sts_hist_impl<2, 1024>;
+      case 3: return (const void*)sts_hist_impl<3, 1024>;
+      default: return (const void*)sts_hist_impl<4, 1024>;
+    }
+  }
   switch (n_slices) {
-    case 1: return (const void*)sts_hist_impl<1>;
-    case 2: return (const void*)sts_hist_impl<2>;
-    case 3: return (const void*)sts_hist_impl<3>;
-    default: return (const void*)sts_hist_impl<4>;
+    case 1: return (const void*)sts_hist_impl<1, kStsMaxCells>;
+    case 2: return (const void*)sts_hist_impl<2, kStsMaxCells>;
+    case 3: return (const void*)sts_hist_impl<3, kStsMaxCells>;
+    default: return (const void*)sts_hist_impl<4, kStsMaxCells>;
   }
 }
 const void* sts_select_kernel() { return (const void*)sts_select_impl; }
