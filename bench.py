@@ -170,8 +170,7 @@ def sts_fit_bench(args):
     tm = ctx.read_timing()
     ctx.timing(False)
     ctx.check()
-    h_ms, h_n = tm["sts_hist"]
-    s_ms, s_n = tm["sts_select"]
+    h_ms, h_n = tm["sts_fit"]
     hist_us = 1e3 * h_ms / h_n
     achieved = N * n_grid / (hist_us * 1e-6) / 1e9          # Geval/s of one scoring pass
     line = {
@@ -182,7 +181,7 @@ def sts_fit_bench(args):
         "config": {"workload": "sts_fit", "N": N, "gamma": G, "candidates": n_grid, "bins": M},
         "roofline": {"bound": "alu", "kernel": "sts_hist", "achieved": achieved, "peak": STS_PEAK_GEVALS,
                      "unit": "Geval/s", "frac": achieved / STS_PEAK_GEVALS, "traffic": None},
-        "kernels_us": {"sts_hist_per_position": hist_us, "sts_select_per_launch": 1e3 * s_ms / s_n},
+        "kernels_us": {"sts_hist_per_position": hist_us},
     }
     if not args.no_cpu_baseline:
         import oracle

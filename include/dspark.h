@@ -115,9 +115,8 @@ enum {
   DSPARK_K_RESID_COMBINE = 8,
   DSPARK_K_GRU = 9,            /* GRU head: s_0 fill and state updates */
   DSPARK_K_DIAG = 10,          /* diagnostic passes (dspark_accept_prob) */
-  DSPARK_K_STS_HIST = 11,      /* temperature fit: scoring pass of one position */
-  DSPARK_K_STS_SELECT = 12,    /* temperature fit: clearing and selection */
-  DSPARK_K_COUNT = 13
+  DSPARK_K_STS = 11,           /* temperature fit: the pass of one position */
+  DSPARK_K_COUNT = 12
 };
 int dspark_timing_enable(dspark_ctx* ctx, int enable);
 int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
@@ -384,11 +383,12 @@ int dspark_verify_packed(dspark_ctx* ctx, hipStream_t stream,
  * (per-sample truncation), so results do not depend on the order in which
  * the workgroups finish.  A score within a few fp32 ulps of a bin edge may
  * fall in the neighbouring bin of an exact evaluation.
- * Errors: DSPARK_EINVAL for shapes, limits and null pointers; ENOMEM if the
- * workspace (8 * n_grid * n_bins bytes) cannot grow.  A candidate that is
- * not positive and finite or an accepted length outside [0, gamma] (clamped)
- * raises the device error flag (dspark_check).  Launches 1 + 2 gamma kernels
- * (timing classes DSPARK_K_STS_HIST and DSPARK_K_STS_SELECT). */
+ * Errors: DSPARK_EINVAL for shapes, limits and null pointers; DSPARK_ENOMEM
+ * if the context's 33 KB buffer for the sums (allocated at its first fit)
+ * cannot be allocated.  A candidate that is not positive and finite or an
+ * accepted length outside [0, gamma] (clamped) raises the device error flag
+ * (dspark_check).  Launches gamma kernels, one per position (timing class
+ * DSPARK_K_STS); the last workgroup of each selects its temperature. */
 int dspark_sts_fit(dspark_ctx* ctx, hipStream_t stream, int64_t N, int gamma,
                    const float* logit, int64_t stride, const int32_t* accept_len,
                    const float* grid, int n_grid, int n_bins,

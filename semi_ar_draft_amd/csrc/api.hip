@@ -78,6 +78,9 @@ struct dspark_ctx {
   // 37.6 / 34.9 at 1 / 2 per CU; 512-thread 42.9 / 38.5 / 39.5 at 1 / 2 / 3;
   // 256-thread 57 / 44 / 40 / 45 / 49 / 54 at 1 / 2 / 4 / 5 / 6 / 8.
   int sts_wg_per_cu = 2;
+  // its (bin, candidate) sums and finished-workgroup counter, zero between
+  // passes (allocated zeroed at the first fit)
+  unsigned long long* sts_buf = nullptr;
   // verify: last target row of each window but the final one (window k covers
   // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list
   int verify_win[8] = {3, 0, 0, 0, 0, 0, 0, 0};
@@ -945,6 +948,7 @@ void dspark_destroy(dspark_ctx* c) {
     for (auto e : c->ev_free) (void)hipEventDestroy(e);
     if (c->ws) (void)hipFree(c->ws);
     if (c->best) (void)hipFree(c->best);
+    if (c->sts_buf) (void)hipFree(c->sts_buf);
     if (c->dev_err) (void)hipFree(c->dev_err);
   }
   delete c;
@@ -1140,7 +1144,16 @@ int dspark_sts_fit(dspark_ctx* c, hipStream_t stream, int64_t N, int gamma, cons
   if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
   int rc;
   const int cells = n_grid * n_bins;
-  if ((rc = ensure_ws(c, (size_t)cells * sizeof(unsigned long long)))) return rc;
+  if (!c->sts_buf) {
+    const size_t bytes = (kStsMaxCells + 32) * sizeof(unsigned long long);
+    if (hipMalloc(&c->sts_buf, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      c->sts_buf = nullptr;
+      return fail(c, DSPARK_ENOMEM, "allocation of %zu bytes failed", bytes);
+    }
+    DSPARK_HIP(c, hipMemset(c->sts_buf, 0, bytes));
+    DSPARK_HIP(c, hipDeviceSynchronize());
+  }
   StsArgs a;
   memset(&a, 0, sizeof(a));
   a.N = N;
@@ -1154,16 +1167,16 @@ int dspark_sts_fit(dspark_ctx* c, hipStream_t stream, int64_t N, int gamma, cons
   a.T = T;
   a.index = index;
   a.ece = ece;
-  a.hist = static_cast<unsigned long long*>(c->ws);
+  a.hist = c->sts_buf;
+  a.done = reinterpret_cast<unsigned int*>(c->sts_buf + kStsMaxCells);
   a.err = c->dev_err;
   const int64_t blocks = (N + kStsWaves * 64 - 1) / (kStsWaves * 64);
   const int nwg = (int)std::max<int64_t>(1, std::min<int64_t>(blocks, (int64_t)c->sts_wg_per_cu * c->cu_count));
-  if ((rc = klaunch(c, DSPARK_K_STS_SELECT, sts_clear_kernel(), dim3((cells + 255) / 256), dim3(256), &a, stream)))
-    return rc;
   for (int k = 1; k <= gamma; ++k) {
     a.k = k;
-    if ((rc = klaunch(c, DSPARK_K_STS_HIST, sts_hist_kernel((n_grid + 63) / 64, cells), dim3(nwg), dim3(kStsThreads), &a, stream))) return rc;
-    if ((rc = klaunch(c, DSPARK_K_STS_SELECT, sts_select_kernel(), dim3(1), dim3(256), &a, stream))) return rc;
+    if ((rc = klaunch(c, DSPARK_K_STS, sts_hist_kernel((n_grid + 63) / 64, cells), dim3(nwg), dim3(kStsThreads), &a,
+                      stream)))
+      return rc;
   }
   return DSPARK_OK;
 }

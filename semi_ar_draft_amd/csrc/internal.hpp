@@ -118,8 +118,9 @@ struct VerifyArgs {
 constexpr int kMaxGamma = 32;   // longest draft (positions per request)
 
 // Temperature fit (sequential temperature scaling): one position k per
-// histogram pass.  hist holds n_bins x n_grid signed sums of (label - score)
-// in 2^-30 units (two's complement in 64 bits), bin-major.
+// pass.  hist holds n_bins x n_grid signed sums of (label - score) in 2^-30
+// units (two's complement in 64 bits), bin-major; it lives in a buffer of
+// the context that the passes leave zeroed.
 // 16 waves per workgroup: occupancy without more workgroups, since each
 // workgroup ends by adding its n_bins x n_grid sums into the global ones
 constexpr int kStsThreads = 1024;
@@ -140,7 +141,8 @@ struct StsArgs {
   float* T;                      // [gamma]: T[0 .. k-2] read, T[k-1] written
   int32_t* index;                // [gamma]
   double* ece;                   // [gamma][n_grid]
-  unsigned long long* hist;      // [n_bins][n_grid] (workspace)
+  unsigned long long* hist;      // [n_bins][n_grid], zero between positions
+  unsigned int* done;            // workgroups finished in this pass, zero between passes
   int32_t* err;
 };
 
@@ -205,10 +207,8 @@ const void* rows_lse_kernel();
 const void* verify_rows_kernel();
 const void* verify_decide_kernel();
 const void* confidence_kernel();
-// temperature fit: clear the sums, one histogram pass and one selection per position
-const void* sts_clear_kernel();
+// temperature fit: one scoring pass per position (its last workgroup selects)
 const void* sts_hist_kernel(int n_slices, int cells);   // 1..4 slices of 64 candidates per lane
-const void* sts_select_kernel();
 const void* gru_init_kernel();
 const void* gru_step_kernel(int r);
 int gru_step_threads(int r);   // workgroup size of gru_step_kernel(r)

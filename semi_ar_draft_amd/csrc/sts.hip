@@ -35,18 +35,76 @@ __device__ __forceinline__ float scaled_sigmoid(float x, float c) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * c));
 }
 
-// Clear the (bin, candidate) sums of the call's first position.
-__global__ __launch_bounds__(256) void sts_clear_impl(StsArgs a) {
-  const int cells = a.n_bins * a.n_grid;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < cells; i += gridDim.x * 256) a.hist[i] = 0ull;
+// ECE of every candidate from the global sums, which are read with
+// agent-scope atomic loads and cleared for the next position; the first
+// minimiser and its temperature.  Run by the last workgroup of a position's
+// pass; `cell` is LDS of at least n_bins x n_grid doubles.
+__device__ void select_position(const StsArgs& a, double* cell) {
+  __shared__ double sv[256];
+  __shared__ int si[256];
+  const int ng = a.n_grid, nb = a.n_bins;
+  const int cells = ng * nb;
+  constexpr int kPer = kStsMaxCells / kStsThreads;
+  unsigned long long v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + kStsThreads * u;
+    v[u] = i < cells ? __hip_atomic_load(&a.hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = threadIdx.x + kStsThreads * u;
+    if (i < cells) {
+      const long long x = (long long)v[u];
+      cell[i] = (double)(x < 0 ? -x : x);
+      __hip_atomic_store(&a.hist[i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  double bv = DBL_MAX;
+  int bi = 0x7fffffff;
+  if (threadIdx.x < 256) {
+    for (int g = threadIdx.x; g < ng; g += 256) {
+      double s = 0.0;
+      for (int m = 0; m < nb; ++m) s += cell[m * ng + g];
+      const double e = a.N > 0 ? s / (kStsScaleD * (double)a.N) : 0.0;
+      a.ece[(int64_t)(a.k - 1) * ng + g] = e;
+      if (e < bv) {   // g grows along the loop: the first minimiser is kept
+        bv = e;
+        bi = g;
+      }
+    }
+    sv[threadIdx.x] = bv;
+    si[threadIdx.x] = bi;
+  }
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      const double ov = sv[threadIdx.x + w];
+      const int oi = si[threadIdx.x + w];
+      if (ov < sv[threadIdx.x] || (ov == sv[threadIdx.x] && oi < si[threadIdx.x])) {
+        sv[threadIdx.x] = ov;
+        si[threadIdx.x] = oi;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int g = si[0];
+    if (g < 0 || g >= ng) g = 0;   // unreachable: every ECE is finite
+    a.T[a.k - 1] = a.grid[g];
+    a.index[a.k - 1] = g;
+    __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // One position: every wave takes blocks of 64 samples, stages each sample's
 // (logit at k, prefix under the fitted earlier temperatures, label) in LDS,
 // and then walks them one by one, all 64 lanes (NS slices of 64 candidates)
 // scoring the same sample.  Sums of (label - score) per (bin, candidate)
-// build up in LDS and are added into the global ones at the end.  Lanes
-// past the last candidate add into a spare column that is never read.
+// build up in LDS and are added into the global ones at the end; the last
+// workgroup to finish selects the temperature.  Lanes past the last
+// candidate add into a spare column that is never read.
 template <int NS, int CELLS>
 __global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
   __shared__ unsigned long long h[CELLS + 64];
@@ -138,71 +196,24 @@ __global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
     const unsigned long long v = h[i];
     if (v) atomicAdd(&a.hist[i], v);
   }
-}
-
-// One position: ECE of every candidate from the sums (clearing them for the
-// next position), the first minimiser, and its temperature.  The cells are
-// read all at once (16 independent loads per thread) into LDS as |sum|, then
-// each candidate adds its column in bin order.
-__global__ __launch_bounds__(256) void sts_select_impl(StsArgs a) {
-  __shared__ double cell[kStsMaxCells];
-  __shared__ double sv[256];
-  __shared__ int si[256];
-  const int ng = a.n_grid, nb = a.n_bins;
-  const int cells = ng * nb;
-  unsigned long long v[kStsMaxCells / 256];
-#pragma unroll
-  for (int u = 0; u < kStsMaxCells / 256; ++u) {
-    const int i = threadIdx.x + 256 * u;
-    v[u] = i < cells ? a.hist[i] : 0ull;
-  }
-#pragma unroll
-  for (int u = 0; u < kStsMaxCells / 256; ++u) {
-    const int i = threadIdx.x + 256 * u;
-    if (i < cells) {
-      const long long x = (long long)v[u];
-      cell[i] = (double)(x < 0 ? -x : x);
-      a.hist[i] = 0ull;
-    }
-  }
+  // the last workgroup to finish turns the sums into the position's ECE
+  // table and temperature.  The sums are device-scope atomics, performed
+  // where every XCD sees them: each wave waits until its own have been
+  // acknowledged before the workgroup is counted, and the last workgroup
+  // reads them back with agent-scope atomic loads.  (Cache write-back and
+  // invalidation fences are not needed for that, and cost 4x the pass.)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  double bv = DBL_MAX;
-  int bi = 0x7fffffff;
-  for (int g = threadIdx.x; g < ng; g += 256) {
-    double s = 0.0;
-    for (int m = 0; m < nb; ++m) s += cell[m * ng + g];
-    const double e = a.N > 0 ? s / (kStsScaleD * (double)a.N) : 0.0;
-    a.ece[(int64_t)(a.k - 1) * ng + g] = e;
-    if (e < bv) {   // g grows along the loop: the first minimiser is kept
-      bv = e;
-      bi = g;
-    }
-  }
-  sv[threadIdx.x] = bv;
-  si[threadIdx.x] = bi;
+  __shared__ int is_last;
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
-      const double ov = sv[threadIdx.x + w];
-      const int oi = si[threadIdx.x + w];
-      if (ov < sv[threadIdx.x] || (ov == sv[threadIdx.x] && oi < si[threadIdx.x])) {
-        sv[threadIdx.x] = ov;
-        si[threadIdx.x] = oi;
-      }
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    int g = si[0];
-    if (g < 0 || g >= ng) g = 0;   // unreachable: every ECE is finite
-    a.T[a.k - 1] = a.grid[g];
-    a.index[a.k - 1] = g;
-  }
+  if (!is_last) return;
+  select_position(a, reinterpret_cast<double*>(h));
 }
 
 }  // namespace
 
-const void* sts_clear_kernel() { return (const void*)sts_clear_impl; }
 const void* sts_hist_kernel(int n_slices, int cells) {
   // histogram of at most 1024 cells: 12.7 KB of LDS per workgroup instead of 37 KB
   if (cells <= 1024) {
@@ -220,6 +231,5 @@ const void* sts_hist_kernel(int n_slices, int cells) {
     default: return (const void*)sts_hist_impl<4, kStsMaxCells>;
   }
 }
-const void* sts_select_kernel() { return (const void*)sts_select_impl; }
 
 }  // namespace dspark
