@@ -180,7 +180,9 @@ def sts_fit_bench(args):
         "data": "synthetic",
         "config": {"workload": "sts_fit", "N": N, "gamma": G, "candidates": n_grid, "bins": M},
         "roofline": {"bound": "alu", "kernel": "sts_hist", "achieved": achieved, "peak": STS_PEAK_GEVALS,
-                     "unit": "Geval/s", "frac": achieved / STS_PEAK_GEVALS, "traffic": None},
+                     "unit": "Geval/s", "frac": achieved / STS_PEAK_GEVALS,
+                     "traffic": profile_traffic(STS_TRAFFIC_PROFILE, {"name": "sts_fit", "N": N, "gamma": G,
+                                                                      "candidates": n_grid, "bins": M})},
         "kernels_us": {"sts_hist_per_position": hist_us},
     }
     if not args.no_cpu_baseline:
@@ -200,18 +202,27 @@ TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "prof
                                "draft_sweep_traffic_B128_V151936_r256_T1.json")
 
 
+STS_TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                   "sts_fit_traffic_N1048576_g7_c64_b15.json")
+
+
 def measured_traffic(wl_name, B, V, r, T):
-    """HBM bytes per draft-sweep launch from the committed counter profile
+    """HBM bytes per draft-sweep launch from the committed counter profile."""
+    return profile_traffic(TRAFFIC_PROFILE, {"name": wl_name, "B": B, "V": V, "r": r, "temperature": T})
+
+
+def profile_traffic(path, workload):
+    """HBM bytes per launch of a kernel from a committed counter profile
     (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the counter
     reads for a copy kernel of known size).  None when the workload differs
     or the kernel sources have changed since the counters were taken."""
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(path) as f:
             prof = json.load(f)
     except (OSError, ValueError):
         return None
     w = prof.get("workload", {})
-    if (w.get("name"), w.get("B"), w.get("V"), w.get("r"), w.get("temperature")) != (wl_name, B, V, r, T):
+    if any(w.get(k) != v for k, v in workload.items()):
         return None
     root = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
