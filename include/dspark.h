@@ -383,6 +383,8 @@ int dspark_verify_packed(dspark_ctx* ctx, hipStream_t stream,
  * (per-sample truncation), so results do not depend on the order in which
  * the workgroups finish.  A score within a few fp32 ulps of a bin edge may
  * fall in the neighbouring bin of an exact evaluation.
+ * Tuning: DSPARK_STS_WG_PER_CU (1..16, default 2) sets the workgroups of a
+ * pass per CU; it does not change results.
  * Errors: DSPARK_EINVAL for shapes, limits and null pointers; DSPARK_ENOMEM
  * if the context's 33 KB buffer for the sums (allocated at its first fit)
  * cannot be allocated.  A candidate that is not positive and finite or an
