@@ -11,14 +11,17 @@
 // The work is N samples x n_grid candidates of one scaled sigmoid, a bin
 // decision and an accumulation per position: plain ALU work (an exponential
 // and a reciprocal on the transcendental unit), with 4 bytes of logit read
-// per sample and candidate row.  Two facts shape the kernels:
+// per sample and candidate row.  One launch per position does all of it,
+// the last workgroup to finish choosing the temperature.  Two facts shape
+// the kernel:
 //  - a bin's share of the ECE is |sum over the bin of (label - score)| / N,
 //    so one signed sum per (bin, candidate) is all that is kept; it is
 //    accumulated as a 64-bit integer of 2^-30 units, so the sums, and the
 //    choice of temperature, do not depend on the order of the atomics;
 //  - the lanes of a wave are 64 candidates and the samples are broadcast to
-//    them (readlane), so lane g always adds into column g of the histogram:
-//    the 64-bit LDS atomics of one instruction never share an address.
+//    them (LDS reads of one address), so lane g always adds into column g of
+//    the histogram: the 64-bit LDS atomics of one instruction never share an
+//    address.
 #include <float.h>
 
 #include "common.hpp"

@@ -173,3 +173,72 @@ def test_sts_fit_rejects_bad_shapes(ctx):
     wide = torch.zeros((10, 40), dtype=torch.float32, device="cuda")
     with pytest.raises(dk.DSparkError, match="gamma"):
         ctx.sts_fit(wide, ad, synth.sts_grid(10).cuda(), 10)
+
+
+def test_sts_fit_graph_capture_replays(ctx):
+    # the per-pass counter and sums are left zeroed by every pass, so a
+    # captured fit replays to the eager result, also with eager fits of
+    # another shape in between
+    d = synth.sts_calibration_set(20000, 5, seed=31)
+    e = synth.sts_calibration_set(3000, 7, seed=32)
+    grid = synth.sts_grid(48, 0.6, 0.05).cuda()
+    l, a = d["logit"].cuda(), d["accept_len"].cuda()
+    l2, a2 = e["logit"].cuda(), e["accept_len"].cuda()
+    out = (torch.empty(5, device="cuda"), torch.empty(5, dtype=torch.int32, device="cuda"),
+           torch.empty((5, 48), dtype=torch.float64, device="cuda"))
+    ctx.sts_fit(l, a, grid, 15, out=out)
+    ctx.check()
+    ref = [x.clone() for x in out]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ctx.sts_fit(l, a, grid, 15, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print("capturing a temperature fit", flush=True)
+    with torch.cuda.graph(g, stream=s):
+        ctx.sts_fit(l, a, grid, 15, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in out:
+            x.zero_()
+        ctx.sts_fit(l2, a2, grid, 12)                   # other eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, want, got in zip(("T", "index", "ece"), ref, out):
+            assert torch.equal(want, got), f"replay {rep}: {name}"
+    ctx.check()
+
+
+def test_sts_fit_two_contexts_on_two_streams():
+    d1 = synth.sts_calibration_set(50000, 7, seed=41)
+    d2 = synth.sts_calibration_set(40000, 4, seed=42)
+    grid = synth.sts_grid().cuda()
+    c1, c2 = dk.Context(0), dk.Context(0)
+    try:
+        i1 = (d1["logit"].cuda(), d1["accept_len"].cuda())
+        i2 = (d2["logit"].cuda(), d2["accept_len"].cuda())
+        r1 = [x.cpu() for x in c1.sts_fit(*i1, grid, 15)]
+        r2 = [x.cpu() for x in c2.sts_fit(*i2, grid, 10)]
+        torch.cuda.synchronize()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        print("two temperature fits on two streams", flush=True)
+        with torch.cuda.stream(s1):
+            o1 = c1.sts_fit(*i1, grid, 15, stream=s1)
+        with torch.cuda.stream(s2):
+            o2 = c2.sts_fit(*i2, grid, 10, stream=s2)
+        s1.synchronize()
+        s2.synchronize()
+        c1.check(s1)
+        c2.check(s2)
+        for want, got in zip(r1, o1):
+            assert torch.equal(want, got.cpu())
+        for want, got in zip(r2, o2):
+            assert torch.equal(want, got.cpu())
+    finally:
+        c1.close()
+        c2.close()
