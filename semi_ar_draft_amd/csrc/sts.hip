@@ -139,15 +139,17 @@ __global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
   }
   __syncthreads();
 
-  const float fM = (float)nb;
-  const float fTop = (float)(nb - 1);
+  // bin = floor(S * M * (1 - 2^-22)): below M for every S <= 1, so no clamp
+  // is needed; it differs from floor(S * M) only for scores within 2.4e-7
+  // below a bin edge, inside the fp32 error of S itself
+  const float fM = (float)nb * (1.f - 0x1p-22f);
   const int k = a.k;
   const int64_t N = a.N;
   char* hb = reinterpret_cast<char*>(h);
   for (int64_t b0 = ((int64_t)blockIdx.x * kStsWaves + wid) * 64; b0 < N;
        b0 += (int64_t)gridDim.x * kStsWaves * 64) {
     const int64_t n = b0 + lane;
-    float p = 0.f, l = 0.f, ys = 0.f;
+    float p = 0.f, l = 0.f, ys = 0.f;   // prefix, logit at k, label x 2^30
     if (n < N) {
       const float* row = a.logit + n * a.stride;
       float pre = 1.f;
@@ -161,31 +163,33 @@ __global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
       }
       ys = len >= k ? kStsScale : 0.f;
     }
-    // the wave's own staging row: its LDS accesses complete in order
-    samp[wid][lane] = make_float4(l, p, ys, 0.f);
+    // the wave's own staging row: its LDS accesses complete in order.  Per
+    // draft: logit, prefix x 2^30, label x 2^30, prefix x M'
+    samp[wid][lane] = make_float4(l, p * kStsScale, ys, p * fM);
     __builtin_amdgcn_wave_barrier();
     // eight samples are read ahead of their atomics and scored phase by
     // phase (eight independent exponentials, then reciprocals, ...), so the
     // transcendental latencies overlap; a sample past N has prefix 0, scores
-    // 0 with label 0 and so adds 0 (into bin 0)
+    // 0 with label 0 and so adds 0 (into bin 0).  With sg = sigmoid(l / T)
+    // and S = prefix * sg: q = (label - S) x 2^30 and bin = floor(S M').
     for (int j0 = 0; j0 < 64; j0 += 8) {
       float4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = samp[wid][j0 + u];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        float S[8];
+        float sg[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) S[u] = __builtin_amdgcn_exp2f(v[u].x * cg[s]);
+        for (int u = 0; u < 8; ++u) sg[u] = __builtin_amdgcn_exp2f(v[u].x * cg[s]);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) S[u] = v[u].y * __builtin_amdgcn_rcpf(1.f + S[u]);
+        for (int u = 0; u < 8; ++u) sg[u] = __builtin_amdgcn_rcpf(1.f + sg[u]);
         unsigned addr[8];
         int q[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int bin = (int)__builtin_amdgcn_fmed3f(S[u] * fM, 0.f, fTop);
-          q[u] = (int)fmaf(S[u], -kStsScale, v[u].z);          // (label - S) in 2^-30 units
-          addr[u] = __umul24((unsigned)bin, mul[s]) + base[s];
+          const unsigned bin = (unsigned)(sg[u] * v[u].w);
+          q[u] = (int)fmaf(sg[u], -v[u].y, v[u].z);            // (label - S) in 2^-30 units
+          addr[u] = __umul24(bin, mul[s]) + base[s];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
