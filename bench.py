@@ -123,15 +123,18 @@ def draft_crossover(seed: int):
     sweeps.close()
 
 
-# ALU roofline of the temperature fit's scoring pass: a candidate evaluation
-# needs at least 8 full-rate fp32 operations (scale the logit, 1 + e, times
-# the prefix, times M, floor, clamp, label - score, accumulate) and 2
-# transcendental ones (exponential, reciprocal) at a quarter of that rate:
-# 16 issue slots of one lane.  The chip issues 256 CUs x 4 SIMDs x 16 lanes
-# x 2.4 GHz = 39.3 T non-packed lane operations per second.
-ALU_LANE_OPS_PER_S = 256 * 4 * 16 * 2.4e9
-STS_SLOTS_PER_EVAL = 16
-STS_PEAK_GEVALS = ALU_LANE_OPS_PER_S / STS_SLOTS_PER_EVAL / 1e9
+# ALU roofline of the temperature fit's scoring pass.  An evaluation (one
+# draft, one candidate) needs at least: 5 fp32 operations (scale the logit,
+# 1 + e, times the prefix, times M for the bin, label - score), 2
+# transcendental ones (exponential, reciprocal) and 1 float-to-int conversion
+# (the bin); the accumulation goes to LDS, a separate pipe.  Issue rates per
+# CU per clock: 128 fp32 lanes (the published 157.3 TFLOP/s = 256 CUs x
+# 2.4 GHz x 128 lanes x 2 for an FMA), a quarter of that for the
+# transcendental instructions and half for conversions (both measured on this
+# part with independent instruction chains: 31 and ~64 lanes per CU per
+# clock).  Peak = 256 x 2.4 GHz / (5/128 + 2/32 + 1/64) evaluations per second.
+STS_CU_CYCLES_PER_EVAL = 5 / 128 + 2 / 32 + 1 / 64
+STS_PEAK_GEVALS = 256 * 2.4e9 / STS_CU_CYCLES_PER_EVAL / 1e9
 
 
 def sts_fit_bench(args):
