@@ -167,34 +167,42 @@ __global__ __launch_bounds__(kStsThreads) void sts_hist_impl(StsArgs a) {
     // draft: logit, prefix x 2^30, label x 2^30, prefix x M'
     samp[wid][lane] = make_float4(l, p * kStsScale, ys, p * fM);
     __builtin_amdgcn_wave_barrier();
-    // eight samples are read ahead of their atomics and scored phase by
-    // phase (eight independent exponentials, then reciprocals, ...), so the
-    // transcendental latencies overlap; a sample past N has prefix 0, scores
+    // Groups of four drafts, double-buffered: the next group's broadcast
+    // reads are issued before this group's atomics, so they do not wait
+    // behind them in the wave's in-order LDS queue.  A group is scored phase
+    // by phase (independent exponentials, then reciprocals, ...), so the
+    // transcendental latencies overlap.  A sample past N has prefix 0, scores
     // 0 with label 0 and so adds 0 (into bin 0).  With sg = sigmoid(l / T)
     // and S = prefix * sg: q = (label - S) x 2^30 and bin = floor(S M').
-    for (int j0 = 0; j0 < 64; j0 += 8) {
-      float4 v[8];
+    float4 v[4], vn[4] = {};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = samp[wid][j0 + u];
+    for (int u = 0; u < 4; ++u) v[u] = samp[wid][u];
+    for (int j0 = 0; j0 < 64; j0 += 4) {
+      if (j0 + 4 < 64) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vn[u] = samp[wid][j0 + 4 + u];
+      }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        float sg[8];
+        float sg[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sg[u] = __builtin_amdgcn_exp2f(v[u].x * cg[s]);
+        for (int u = 0; u < 4; ++u) sg[u] = __builtin_amdgcn_exp2f(v[u].x * cg[s]);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sg[u] = __builtin_amdgcn_rcpf(1.f + sg[u]);
-        unsigned addr[8];
-        int q[8];
+        for (int u = 0; u < 4; ++u) sg[u] = __builtin_amdgcn_rcpf(1.f + sg[u]);
+        unsigned addr[4];
+        int q[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 4; ++u) {
           const unsigned bin = (unsigned)(sg[u] * v[u].w);
           q[u] = (int)fmaf(sg[u], -v[u].y, v[u].z);            // (label - S) in 2^-30 units
           addr[u] = __umul24(bin, mul[s]) + base[s];
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 4; ++u)
           atomicAdd(reinterpret_cast<unsigned long long*>(hb + addr[u]), (unsigned long long)(long long)q[u]);
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = vn[u];
     }
     __builtin_amdgcn_wave_barrier();
   }
