@@ -111,6 +111,11 @@ CASES = [
     ("N1_g2_c7_b64", 1, 2, (7, 0.5, 0.5), 64, 0, 6),
     ("N20000_g32_c65_b15", 20000, 32, (65, 0.5, 0.05), 15, 0, 7),
     ("N4097_g5_c40_b12_strided", 4097, 5, (40, 0.6, 0.07), 12, 5, 8),
+    # the remaining (candidate slices, table size) instantiations of the pass
+    ("N999_g2_c64_b64_slices1_big", 999, 2, (64, 0.5, 0.05), 64, 0, 9),
+    ("N2500_g6_c100_b20_slices2_big", 2500, 6, (100, 0.4, 0.03), 20, 0, 10),
+    ("N1500_g3_c150_b6_slices3_small", 1500, 3, (150, 0.3, 0.02), 6, 0, 11),
+    ("N3000_g4_c256_b4_slices4_small", 3000, 4, (256, 0.3, 0.012), 4, 0, 12),
 ]
 
 
