@@ -27,7 +27,7 @@ fixtures under tests/golden/.
 """
 from .rng import (DRAFT, ACCEPT, RESID, BONUS, mix64, splitmix64_next, fmix32, row_key,
                   uniforms, uniform_at, gumbels)
-from .sampling import race_draw, group_keys
+from .sampling import gumbel_draw, gumbel_keys
 from .markov import decode_weights, markov_bias, draft_markov, DraftResult
 from .rnn import gru_cell, draft_rnn
 from .confidence import confidence, ConfidenceResult
@@ -38,7 +38,7 @@ from .sts_fit import ece, labels, candidate_scores, sts_fit, StsFit
 
 __all__ = [
     "DRAFT", "ACCEPT", "RESID", "BONUS", "mix64", "splitmix64_next", "fmix32", "row_key",
-    "uniforms", "uniform_at", "gumbels", "race_draw", "group_keys", "decode_weights", "markov_bias", "draft_markov", "gru_cell", "draft_rnn",
+    "uniforms", "uniform_at", "gumbels", "gumbel_draw", "gumbel_keys", "decode_weights", "markov_bias", "draft_markov", "gru_cell", "draft_rnn",
     "DraftResult", "confidence", "ConfidenceResult", "schedule", "schedule_async", "ScheduleResult", "verify",
     "VerifyResult", "target_logprobs", "accept_ratio", "residual_weights", "accept_prob", "run_step",
     "StepResult", "ece", "labels", "candidate_scores", "sts_fit", "StsFit",

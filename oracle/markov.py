@@ -11,8 +11,8 @@ B in R^{V x r}; its one-hot form is used as an independent pin in the tests.
 Readings:
   * the draft law is softmax((U_k + B_k) / T); T = 0 means argmax of U_k + B_k;
   * the bias is applied at every position, B_1 from the anchor token x_0;
-  * a stochastic draw takes w_v = exp(y_v), y = z / T, through the two-level
-    exponential race of ``sampling.race_draw`` with the DRAFT stream;
+  * a stochastic draw is the Gumbel-max draw of ``sampling.gumbel_draw`` on
+    y = z / T (weights w_v = exp(y_v)) with the DRAFT stream of (req, k);
   * greedy ties go to the lowest vocabulary index;
   * in greedy mode the reported log-normaliser is that of z itself (T = 1).
 """
@@ -25,7 +25,7 @@ import numpy as np
 import torch
 
 from .rng import DRAFT, row_key
-from .sampling import race_draw
+from .sampling import gumbel_draw
 
 
 def decode_weights(w) -> np.ndarray:
@@ -70,7 +70,7 @@ class DraftResult:
     tokens: np.ndarray    # int64 [B, gamma]
     lse: np.ndarray       # float64 [B, gamma]: L_d = ln sum_v exp(y_v)
     ytok: np.ndarray      # float64 [B, gamma]: y at the drafted token
-    margin: np.ndarray    # float64 [B, gamma]: greedy top-2 gap, or the race draw's margin
+    margin: np.ndarray    # float64 [B, gamma]: top-2 gap of the greedy or Gumbel-max keys
     z: Optional[np.ndarray] = None   # float64 [B, gamma, V] when kept
     states: Optional[np.ndarray] = None   # GRU head: float64 [B, gamma, r], the state position k projected
 
@@ -104,7 +104,7 @@ def draft_markov(U, W1, W2, anchor, req_ids, temperature: float, seed: int, gamm
         y = z / T if T > 0 else z
         if T > 0:
             for b in range(B):
-                x_b, m_b = race_draw(y[b], row_key(seed, int(req[b]), k, DRAFT))
+                x_b, m_b = gumbel_draw(y[b], row_key(seed, int(req[b]), k, DRAFT))
                 tokens[b, k - 1] = x_b
                 margin[b, k - 1] = m_b
             x = tokens[:, k - 1].copy()

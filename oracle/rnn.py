@@ -29,7 +29,7 @@ import torch
 
 from .markov import decode_weights, logsumexp_rows, top2_margin, _ints, DraftResult
 from .rng import DRAFT, row_key
-from .sampling import race_draw
+from .sampling import gumbel_draw
 
 
 def _sigmoid(x):
@@ -80,7 +80,7 @@ def draft_rnn(U, W1, W2, gru: dict, req_ids, temperature: float, seed: int, gamm
         y = z / T if T > 0 else z
         if T > 0:
             for b in range(B):
-                x_b, m_b = race_draw(y[b], row_key(seed, int(req[b]), k, DRAFT))
+                x_b, m_b = gumbel_draw(y[b], row_key(seed, int(req[b]), k, DRAFT))
                 tokens[b, k - 1] = x_b
                 margin[b, k - 1] = m_b
             x = tokens[:, k - 1].copy()

@@ -1,71 +1,45 @@
-"""Categorical draws by a two-level exponential race, float64 (test oracle).
+"""Categorical draws by the Gumbel-max trick, float64 (test oracle).
 
 Every stochastic choice of the step -- the draft token at each position, the
 residual token at the first rejection, the bonus token -- is a draw from a
 law proportional to nonnegative weights w_v over the vocabulary.  The pages
-fix no sampling procedure (only the laws); this is the oracle's reading,
-chosen so that one uniform of the counter stream serves four entries:
+give the laws only ([blog] "形式化定义": the draft softmax, the normalised
+residual at the first rejection, the target's law for the compensation
+token), not a procedure.  The reading taken is the textbook Gumbel-max draw
+(E. J. Gumbel 1954; e.g. Maddison, Tarlow & Minka, "A* Sampling", 2014):
 
-  * the vocabulary is cut into aligned groups G_g = {4g, .., 4g+3} (the last
-    one shorter when V is not a multiple of 4), with masses S_g = sum of w_v;
-  * group g gets the exponential variate E_g = -ln a_g, a_g the uniform of
-    element 4g of the row's stream; the group with the largest
-    ln S_g - ln E_g wins (lowest g on ties) -- the exponential race, so
-    P(g) = S_g / sum S (the minimum of E_g / S_g over independent
-    exponentials falls on g with that probability);
-  * inside the winner, the uniform c of element 4g+1 picks the first member
-    i with c * S_g < w_{4g} + .. + w_{4g+i} (inverse CDF), so
-    P(v | g) = w_v / S_g.
+    x = the lowest index v attaining  max_v ( ln w_v + g_v ),
+    g_v = -ln(-ln u_v),  u_v the row's counter-based uniforms (rng.py).
 
-Together P(v) = w_v / sum w, the law asked for.  Zero weights are never
-drawn.  The decision margin reported for parity is the smaller of the top-2
-gap of the group keys and the distance of c from the nearest inner CDF
-boundary (relative to S_g).
+Because the g_v are independent standard Gumbels, P(x = v) = w_v / sum w.
+Zero weights (ln w = -inf) are never drawn.  The decision margin reported
+for parity is the gap between the best key and the best key at any other
+index: a perturbation of every key by less than half of it cannot change
+the draw.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .rng import uniforms
-
-GROUP = 4
+from .rng import gumbels
 
 
-def group_keys(logw: np.ndarray, key: int):
-    """Per-group log-mass, race key and the row's uniforms.
+def gumbel_keys(logw: np.ndarray, key: int) -> np.ndarray:
+    """Per-entry keys ln w_v + g_v of one row (-inf where w_v = 0)."""
+    logw = np.asarray(logw, dtype=np.float64)
+    return logw + gumbels(key, logw.shape[0])
 
-    logw: [V] float64 log-weights (-inf for a zero weight).  Returns
-    (lse_g [G], race key [G], lw [G, 4] padded with -inf, u [4G]).
+
+def gumbel_draw(logw: np.ndarray, key: int) -> tuple[int, float]:
+    """Draw v ~ w_v / sum w by Gumbel-max; returns (v, margin).
+
+    logw: [V] float64 log-weights (-inf for a zero weight); key: the row's
+    64-bit stream key.
     """
-    V = logw.shape[0]
-    G = (V + GROUP - 1) // GROUP
-    lw = np.full(G * GROUP, -np.inf)
-    lw[:V] = logw
-    lw = lw.reshape(G, GROUP)
-    m = lw.max(axis=1)
-    safe = np.where(np.isfinite(m), m, 0.0)
-    with np.errstate(divide="ignore"):
-        lse = safe + np.log(np.exp(lw - safe[:, None]).sum(axis=1))
-    lse = np.where(np.isfinite(m), lse, -np.inf)
-    u = uniforms(key, G * GROUP)
-    E = -np.log(u[0::GROUP])
-    return lse, lse - np.log(E), lw, u
-
-
-def race_draw(logw: np.ndarray, key: int) -> tuple[int, float]:
-    """Draw v ~ w_v / sum w by the two-level race; returns (v, margin)."""
-    lse, gk, lw, u = group_keys(logw, key)
-    g = int(np.argmax(gk))                      # first maximum: lowest group on ties
-    if not np.isfinite(gk[g]):
+    keys = gumbel_keys(logw, key)
+    v = int(np.argmax(keys))                 # first maximum: lowest index on ties
+    if not np.isfinite(keys[v]):
         raise ValueError("all weights are zero")
-    rest = np.delete(gk, g)
-    key_margin = float(gk[g] - rest.max()) if rest.size else np.inf
-    w = np.exp(lw[g] - lse[g])                  # member weights relative to S_g
-    C = np.cumsum(w)
-    c = float(u[GROUP * g + 1])
-    hits = np.nonzero(c < C)[0]
-    i = int(hits[0]) if hits.size else int(np.nonzero(w > 0)[0][-1])
-    n_real = min(GROUP, logw.shape[0] - GROUP * g)   # members of the group (last may be short)
-    inner = C[: n_real - 1]
-    choice_margin = float(np.min(np.abs(c - inner))) if inner.size else np.inf
-    return GROUP * g + i, min(key_margin, choice_margin)
+    rest = np.delete(keys, v)
+    margin = float(keys[v] - rest.max()) if rest.size else np.inf
+    return v, margin

@@ -14,7 +14,7 @@ standard lossless rule they describe (readings):
     stream (empty residual: draw from p_t with that stream);
   * if all K_b drafts are accepted, draw the bonus from target row K_b + 1
     with the BONUS stream;
-  * every draw is the two-level exponential race of ``sampling.race_draw``;
+  * every draw is the Gumbel-max draw of ``sampling.gumbel_draw``;
   * greedy (T = 0): accept iff x_k equals the lowest-index argmax of the
     target row; the compensation / bonus token is that argmax;
   * p_t = softmax(target / T), p_d = softmax((U + bias) / T), same T.
@@ -28,7 +28,7 @@ import torch
 
 from .markov import decode_weights, markov_bias, logsumexp_rows, _ints
 from .rng import ACCEPT, RESID, BONUS, row_key, uniform_at
-from .sampling import race_draw
+from .sampling import gumbel_draw
 
 
 def _row(x, b, k) -> np.ndarray:
@@ -133,9 +133,9 @@ def verify(target, tokens, lse_d, ytok, U, W1, W2, anchor, K, req_ids,
             rkey = row_key(seed, r_id, k, RESID)
             if np.any(resid > 0):
                 with np.errstate(divide="ignore"):
-                    xr, final_margin[b] = race_draw(np.log(resid), rkey)
+                    xr, final_margin[b] = gumbel_draw(np.log(resid), rkey)
             else:
-                xr, final_margin[b] = race_draw(t / T, rkey)
+                xr, final_margin[b] = gumbel_draw(t / T, rkey)
             out[b, A] = xr
             resid_row[b] = k
             done = True
@@ -147,7 +147,7 @@ def verify(target, tokens, lse_d, ytok, U, W1, W2, anchor, K, req_ids,
                 final_margin[b] = _top2(t, star)
                 lse_t[b, Kb] = logsumexp_rows(t[None])[0]
             else:
-                star, final_margin[b] = race_draw(t / T, row_key(seed, r_id, Kb + 1, BONUS))
+                star, final_margin[b] = gumbel_draw(t / T, row_key(seed, r_id, Kb + 1, BONUS))
                 lse_t[b, Kb] = logsumexp_rows((t / T)[None])[0]
             out[b, A] = star
         acc[b] = A

@@ -174,7 +174,7 @@ def test_bonus_uses_row_after_last_verified():
                       inp["req_ids"], 1.0, 5, 7)
     for b in range(32):
         assert r.accept_len[b] == 2
-        bonus, _ = oracle.race_draw(inp["U"][b, 2].double().numpy(),
+        bonus, _ = oracle.gumbel_draw(inp["U"][b, 2].double().numpy(),
                                     oracle.row_key(5, int(inp["req_ids"][b]) & 0xFFFFFFFF, 3, oracle.BONUS))
         assert r.out_tokens[b, 2] == bonus
         assert np.all(r.out_tokens[b, 3:] == -1)
