@@ -33,13 +33,13 @@ from .rnn import gru_cell, draft_rnn
 from .confidence import confidence, ConfidenceResult
 from .schedule import schedule, schedule_async, ScheduleResult
 from .verify import verify, VerifyResult, target_logprobs, accept_ratio, residual_weights, accept_prob
-from .step import run_step, StepResult
+from .step import run_step, step_lengths, StepResult
 from .sts_fit import ece, labels, candidate_scores, sts_fit, StsFit
 
 __all__ = [
     "DRAFT", "ACCEPT", "RESID", "BONUS", "mix64", "splitmix64_next", "fmix32", "row_key",
     "uniforms", "uniform_at", "gumbels", "gumbel_draw", "gumbel_keys", "decode_weights", "markov_bias", "draft_markov", "gru_cell", "draft_rnn",
     "DraftResult", "confidence", "ConfidenceResult", "schedule", "schedule_async", "ScheduleResult", "verify",
-    "VerifyResult", "target_logprobs", "accept_ratio", "residual_weights", "accept_prob", "run_step",
+    "VerifyResult", "target_logprobs", "accept_ratio", "residual_weights", "accept_prob", "run_step", "step_lengths",
     "StepResult", "ece", "labels", "candidate_scores", "sts_fit", "StsFit",
 ]

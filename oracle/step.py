@@ -33,6 +33,26 @@ class StepResult:
     ver: VerifyResult
 
 
+def step_lengths(inp: dict, tokens) -> tuple:
+    """Confidence, survival and the scheduled verify lengths of drafted tokens.
+
+    [blog] "置信度头" and "硬件感知前缀调度器", [summary] section 4: the
+    confidence head scores every drafted position from its hidden state and
+    the previous token, the survival products rank the candidates, and the
+    synchronous greedy scheduler with early stop picks K_b.  Returns
+    (ConfidenceResult or None, ScheduleResult or None); without a table every
+    request verifies all gamma positions (K = None).
+    """
+    c = None
+    if inp.get("h") is not None:
+        c = confidence(inp["h"], inp["E"], inp["anchor"], tokens, inp["wc"], inp["bc"], inp.get("sts_T"))
+    s = None
+    if inp.get("sps") is not None:
+        # the scheduler consumes the survival values as the fp32 the boundary carries
+        s = schedule(c.surv.astype(np.float32), inp["sps"])
+    return c, s
+
+
 def run_step(inp: dict, seed: int, rows: Optional[Sequence[int]] = None) -> StepResult:
     wl = inp["wl"]
     B = inp["U"].shape[0]
@@ -51,16 +71,9 @@ def run_step(inp: dict, seed: int, rows: Optional[Sequence[int]] = None) -> Step
                          sel(inp["req_ids"]), T, seed, wl.gamma)
     else:
         d = draft_rnn(sel(inp["U"]), inp["W1"], inp["W2"], gru, sel(inp["req_ids"]), T, seed, wl.gamma)
-    c = None
-    if inp.get("h") is not None:
-        c = confidence(sel(inp["h"]), inp["E"], sel(inp["anchor"]), d.tokens, inp["wc"],
-                       inp["bc"], inp.get("sts_T"))
-    s = None
-    K = None
-    if has_sched:
-        # the scheduler consumes the survival values as the fp32 the boundary carries
-        s = schedule(c.surv.astype(np.float32), inp["sps"])
-        K = s.K
+    sub = dict(inp, h=sel(inp["h"]), anchor=sel(inp["anchor"])) if inp.get("h") is not None else inp
+    c, s = step_lengths(sub, d.tokens)
+    K = None if s is None else s.K
     v = verify(sel(inp["target"]), d.tokens, d.lse, d.ytok, sel(inp["U"]), inp["W1"], inp["W2"],
                sel(inp["anchor"]), K, sel(inp["req_ids"]), T, seed, wl.gamma, states=d.states)
     return StepResult(rows, d, c, s, v)
