@@ -130,11 +130,8 @@ int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
  *     y_v    = z_v / T                     (T = temperature; y = z if T == 0)
  *     x_k    = argmin-index argmax_v z_v                     if T == 0
  *            = draw(exp(y), stream (seed, req_b, k, DRAFT))  else
- * where draw(w, s) picks v with probability w_v / sum w by a two-level
- * exponential race over the groups {4g .. 4g+3}: S_g = sum of w over the
- * group, E_g = -ln u_s(4g), the group with the largest ln S_g - ln E_g wins
- * (lowest g on ties), and inside it the first member i with
- * u_s(4g+1) * S_g < w_4g + ... + w_{4g+i} is drawn (u_s(v): the uniform of
+ * where draw(w, s) is the Gumbel-max draw: the lowest v attaining
+ * max_v (ln w_v - ln(-ln u_s(v))), so P(v) = w_v / sum w (u_s(v): the uniform of
  * element v of stream s).  x_k feeds position k+1.  Outputs per (b, k):
  *     tokens[b][k-1] = x_k
  *     lse[b][k-1]    = ln sum_v exp(y_v)      (of z when T == 0)

@@ -78,32 +78,28 @@ __device__ __forceinline__ float hash_uniform(uint32_t h) {
   return __builtin_fmaf((float)(h >> 9), 0x1.0p-23f, 0x1.0p-24f);
 }
 
-// ---------------------------------------------------------------------------
-// Categorical draws by a two-level exponential race over aligned groups of
-// four vocabulary entries.  Group g = {4g .. 4g+3} with mass S_g draws
-// E_g = -log2(a), a the uniform of element 4g of the row; the largest
-// log2 S_g - log2 E_g wins (an increasing affine map of ln S_g - ln E_g, so
-// the winner is the exponential race's: P(g) = S_g / sum S).  Inside the
-// winner the uniform c of element 4g+1 picks the member by inverse CDF,
-// P(v | g) = w_v / S_g.  A group beats the running key K iff
-// E_g < S_g * 2^(m - K) when its mass is held as S_g * 2^-m, so most groups
-// cost one hash, one log and a compare.
-// ---------------------------------------------------------------------------
-// First member i with c < w0 + .. + wi (c = uniform * group mass); if
-// rounding leaves none, the last member of positive weight.
-__device__ __forceinline__ int group_pick(float c, float w0, float w1, float w2, float w3) {
-  float C = w0;
-  if (c < C) return 0;
-  C += w1;
-  if (c < C) return 1;
-  C += w2;
-  if (c < C) return 2;
-  if (w3 > 0.0f) return 3;
-  return w2 > 0.0f ? 2 : (w1 > 0.0f ? 1 : 0);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------------------
+// Categorical draws by Gumbel-max.  Entry v of a row with weight w_v and
+// uniform u_v has the key ln w_v - ln(-ln u_v); the draw is the lowest index
+// attaining the largest key, so P(v) = w_v / sum w.  With E_v = -log2 u_v
+// (a positive multiple of -ln u_v) the key order is the order of w_v / E_v,
+// so a lane compares a candidate with its leader b as w_v E_b > w_b E_v
+// (one logarithm per entry; the weights are the softmax terms already formed
+// for the log-normaliser) and turns the leader into a log-domain key once,
+// at the end of its range.
+// ---------------------------------------------------------------------------
+// E_v = -log2 u_v.  u_v = (2 (h >> 9) + 1) 2^-24 is formed as the float
+// 1 + (h >> 9) 2^-23 (exponent bits spliced in) minus 1 - 2^-24: the result
+// is exactly representable, so the subtraction is exact.
+__device__ __forceinline__ float gumbel_e(uint32_t klo, uint32_t khi, uint32_t v) {
+  const uint32_t h = elem_hash(klo, khi, v);
+  const float f = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, h, 9u));   // 0x3F800000 | h >> 9
+  return -fast_log2(f - (1.0f - 0x1.0p-24f));
+}
+
 
 // ---------------------------------------------------------------------------
 // Merge rules (deterministic: fixed order, lowest index wins ties).

@@ -15,8 +15,8 @@
 // r/32 bf16 MFMAs per 16-row block, and folds z = U + bias into per-lane
 // running statistics:
 //   draft:    online log-sum-exp of y = z / T (base 2), arg-max of z
-//             (greedy) or the group-race draw from exp(y) (sampling);
-//   residual: the group-race draw from max(0, p_t - p_d) (and from p_t as
+//             (greedy) or the Gumbel-max draw from exp(y) (sampling);
+//   residual: the Gumbel-max draw from max(0, p_t - p_d) (and from p_t as
 //             the empty-residual fallback).
 // With the 16x16x32 MFMA lane l holds rows D[4*(l/16) + i][l % 16]: four
 // consecutive vocabulary entries of one request, so U is read with one
@@ -81,18 +81,17 @@ struct LaneState {
   float m, s;       // log-sum-exp state (draft)
   float key;        // best key
   int idx;          // its vocabulary index
-  float zb;         // z at the best key (sampling draft)
+  float zb;         // draft: y (tempered logit) at the best entry; greedy: z
   float fkey;       // residual: fallback key (draw from p_t)
   int fidx;
-  // draft modes, during the range: the leading group (first entry g, its
-  // four z values) and, sampling, its mass relative to 2^m and its E
+  // greedy draft, during the range: the leading group (first entry g, its
+  // four z values)
   int g;
   float zg[4];
+  // sampling draft and residual, during the range: the leader's weight (the
+  // draft: relative to 2^m) and its E = -log2 u; residual: pb, ebf for the
+  // fallback draw from p_t
   float sb, eb;
-  // residual, the fallback race on p_t: leading group, its four p_t values,
-  // its mass and its E (the race on max(0, p_t - p_d) uses g, zg, sb, eb)
-  int gf;
-  float zf[4];
   float pb, ebf;
 };
 
@@ -109,9 +108,6 @@ __device__ __forceinline__ void lane_init(LaneState& st) {
   for (int i = 0; i < 4; ++i) st.zg[i] = 0.0f;
   st.sb = 0.0f;
   st.eb = 1.0f;
-  st.gf = -1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st.zf[i] = 0.0f;
   st.pb = 0.0f;
   st.ebf = 1.0f;
 }
@@ -120,17 +116,16 @@ __device__ __forceinline__ void lane_init(LaneState& st) {
 // NTL groups of four consecutive vocabulary entries, z = U + bias straight
 // from the MFMA, whose accumulator was initialised with U) into the state:
 // one max and one rescale per row and step for the online log-sum-exp, and
-// the leading group of the range so far, tracked without branches (with 64
-// lanes per wave some lane nearly always finds a new leader, so a branch
-// would be taken on almost every step).  Only the leading group's four z
-// values are kept; the entry within it is resolved once, at the end of the
-// range (resolve_draft).
+// the leader of the range so far, tracked without branches (with 64 lanes
+// per wave some lane nearly always finds a new leader, so a branch would be
+// taken on almost every step).
 //
-// Greedy: the group with the largest z (first such group on ties).
-// Sampling, the group race (common.hpp): group g of mass S_g relative to 2^m
-// leads while S_g / E_g is the largest, compared as S_g E_b > E_g S_b with
-// the leader's S_b rescaled together with the running max (so no log is
-// taken per group, only E_g = -log2 u).
+// Greedy: the group of four with the largest z (first such group on ties);
+// the entry within it is resolved once, at the end of the range.
+// Sampling, Gumbel-max (common.hpp): entry v with weight w_v = 2^(y2_v - m)
+// (the softmax term) leads while w_v / E_v is the largest, compared as
+// w_v E_b > E_v w_b with the leader's w_b rescaled together with the running
+// max; entries are visited in increasing v, so equal keys keep the lower one.
 template <int MODE, int NTL>
 __device__ __forceinline__ void fold_draft(LaneState& st, const f32x4_t (&z)[NTL], int v0, uint32_t klo,
                                            uint32_t khi, float s2) {
@@ -141,15 +136,13 @@ __device__ __forceinline__ void fold_draft(LaneState& st, const f32x4_t (&z)[NTL
 #pragma unroll
   for (int h = 1; h < NTL; ++h) zmax = fmaxf(zmax, zt[h]);
   const float mn = fmaxf(st.m, zmax * s2);
-  float S[NTL];
+  float e[NTL][4];
   float tot = 0.0f;
 #pragma unroll
   for (int h = 0; h < NTL; ++h) {
-    float e[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = fast_exp2(__builtin_fmaf(z[h][i], s2, -mn));
-    S[h] = (e[0] + e[1]) + (e[2] + e[3]);
-    tot += S[h];
+    for (int i = 0; i < 4; ++i) e[h][i] = fast_exp2(__builtin_fmaf(z[h][i], s2, -mn));
+    tot += (e[h][0] + e[h][1]) + (e[h][2] + e[h][3]);
   }
   const float resc = fast_exp2(st.m - mn);
   st.s = __builtin_fmaf(st.s, resc, tot);
@@ -167,47 +160,41 @@ __device__ __forceinline__ void fold_draft(LaneState& st, const f32x4_t (&z)[NTL
     st.sb *= resc;
 #pragma unroll
     for (int h = 0; h < NTL; ++h) {
-      const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + kTileV * h))));
-      const bool lead = S[h] * st.eb > E * st.sb;
-      st.sb = lead ? S[h] : st.sb;
-      st.eb = lead ? E : st.eb;
-      st.g = lead ? v0 + kTileV * h : st.g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.zg[i] = lead ? z[h][i] : st.zg[i];
+      for (int i = 0; i < 4; ++i) {
+        const int v = v0 + kTileV * h + i;
+        const float E = gumbel_e(klo, khi, (uint32_t)v);
+        const bool lead = e[h][i] * st.eb > E * st.sb;
+        st.sb = lead ? e[h][i] : st.sb;
+        st.eb = lead ? E : st.eb;
+        st.idx = lead ? v : st.idx;
+      }
     }
   }
 }
 
-// End of a range: turn the leading group into (key, idx, zb).  Greedy: the
-// lowest entry holding the maximum.  Sampling: the key log2 S_b + m - log2 E_b
-// and the entry drawn within the group by inverting its CDF at u(g + 1) (the
-// weights exp2(z s2) relative to the group's own maximum).
+// End of a range.  Greedy: the lowest entry of the leading group holding the
+// maximum.  Sampling: the leader's key log2 w_b + m - log2 E_b and its
+// tempered logit y = (log2 w_b + m) ln 2.
 template <int MODE>
 __device__ __forceinline__ void resolve_draft(LaneState& st, uint32_t klo, uint32_t khi, float s2) {
-  if (st.g < 0) return;                                  // empty range
   if constexpr (MODE == kModeDraftGreedy) {
+    if (st.g < 0) return;                                // empty range
     int i = 3;
 #pragma unroll
     for (int k = 2; k >= 0; --k) i = (st.zg[k] == st.key) ? k : i;
     st.idx = st.g + i;
     st.zb = st.key;
   } else {
-    const float zm = fmaxf(fmaxf(st.zg[0], st.zg[1]), fmaxf(st.zg[2], st.zg[3]));
-    float e[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) e[k] = fast_exp2((st.zg[k] - zm) * s2);
-    const float S = (e[0] + e[1]) + (e[2] + e[3]);
-    const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(st.g + 1))) * S;
-    const int i = group_pick(c, e[0], e[1], e[2], e[3]);
-    st.key = fast_log2(st.sb) + st.m - fast_log2(st.eb);
-    st.idx = st.g + i;
-    // selects rather than an indexed read (which would put the state in scratch)
-    st.zb = i == 0 ? st.zg[0] : (i == 1 ? st.zg[1] : (i == 2 ? st.zg[2] : st.zg[3]));
+    if (!(st.sb > 0.0f)) return;                         // empty range
+    const float y2 = fast_log2(st.sb) + st.m;
+    st.key = y2 - fast_log2(st.eb);
+    st.zb = y2 * kLn2;
   }
 }
 
-// Residual and acceptance-probability modes: fold four values (one race
-// group) of z = U + bias and of the target row into the state.
+// Residual and acceptance-probability modes: fold four values of
+// z = U + bias and of the target row into the state.
 template <int MODE>
 __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const float4 t, int v0,
                                          uint32_t klo, uint32_t khi, float invT, float ld, float lt) {
@@ -223,51 +210,34 @@ __device__ __forceinline__ void epilogue(LaneState& st, const f32x4_t z, const f
     }
     st.s += acc;
   } else {
-    // residual: weights r_v = max(0, p_t - p_d) with mass R; the fallback
-    // (empty residual) draws from p_t with mass P, sharing the group's
-    // uniforms.  Both races track their leading group without branches
-    // (R E_b > E R_b; the probabilities need no running rescale); the keys
-    // and the entries within the groups are resolved at the end of the range.
+    // residual: Gumbel-max on the weights r_v = max(0, p_t - p_d); the
+    // fallback (empty residual) draws from p_t with the same uniforms.  Both
+    // leaders are tracked without branches (r_v E_b > E_v r_b; the
+    // probabilities need no running rescale); zero weights never lead.
     const float tv[4] = {t.x, t.y, t.z, t.w};
-    float pt[4], r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pt[i] = fast_exp2(__builtin_fmaf(tv[i], invT, -lt) * kLog2e);
+      const float pt = fast_exp2(__builtin_fmaf(tv[i], invT, -lt) * kLog2e);
       const float pd = fast_exp2(__builtin_fmaf(z[i], invT, -ld) * kLog2e);
-      r[i] = fmaxf(pt[i] - pd, 0.0f);
-    }
-    const float R = (r[0] + r[1]) + (r[2] + r[3]);
-    const float P = (pt[0] + pt[1]) + (pt[2] + pt[3]);
-    const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)v0)));
-    const bool lr = R * st.eb > E * st.sb;
-    st.sb = lr ? R : st.sb;
-    st.eb = lr ? E : st.eb;
-    st.g = lr ? v0 : st.g;
-    const bool lf = P * st.ebf > E * st.pb;
-    st.pb = lf ? P : st.pb;
-    st.ebf = lf ? E : st.ebf;
-    st.gf = lf ? v0 : st.gf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st.zg[i] = lr ? r[i] : st.zg[i];
-      st.zf[i] = lf ? pt[i] : st.zf[i];
+      const float r = fmaxf(pt - pd, 0.0f);
+      const int v = v0 + i;
+      const float E = gumbel_e(klo, khi, (uint32_t)v);
+      const bool lr = r * st.eb > E * st.sb;
+      st.sb = lr ? r : st.sb;
+      st.eb = lr ? E : st.eb;
+      st.idx = lr ? v : st.idx;
+      const bool lf = pt * st.ebf > E * st.pb;
+      st.pb = lf ? pt : st.pb;
+      st.ebf = lf ? E : st.ebf;
+      st.fidx = lf ? v : st.fidx;
     }
   }
 }
 
-// End of a residual range: the keys log2 R_b - log2 E_b (and for p_t) and the
-// entries drawn within the leading groups at u(g + 1).
-__device__ __forceinline__ void resolve_resid(LaneState& st, uint32_t klo, uint32_t khi) {
-  if (st.g >= 0) {
-    const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(st.g + 1))) * st.sb;
-    st.key = fast_log2(st.sb) - fast_log2(st.eb);
-    st.idx = st.g + group_pick(c, st.zg[0], st.zg[1], st.zg[2], st.zg[3]);
-  }
-  if (st.gf >= 0) {
-    const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(st.gf + 1))) * st.pb;
-    st.fkey = fast_log2(st.pb) - fast_log2(st.ebf);
-    st.fidx = st.gf + group_pick(c, st.zf[0], st.zf[1], st.zf[2], st.zf[3]);
-  }
+// End of a residual range: the keys log2 r_b - log2 E_b (and for p_t).
+__device__ __forceinline__ void resolve_resid(LaneState& st) {
+  if (st.sb > 0.0f) st.key = fast_log2(st.sb) - fast_log2(st.eb);
+  if (st.pb > 0.0f) st.fkey = fast_log2(st.pb) - fast_log2(st.ebf);
 }
 
 template <int MODE>
@@ -539,7 +509,7 @@ struct WaveRows {
       if constexpr (MODE == kModeDraftGreedy || MODE == kModeDraftSample)
         resolve_draft<MODE>(st[nb], klo[nb], khi[nb], a.s2);
       else if constexpr (MODE == kModeResidual)
-        resolve_resid(st[nb], klo[nb], khi[nb]);
+        resolve_resid(st[nb]);
       lane_merge<MODE>(st[nb], 16);
       lane_merge<MODE>(st[nb], 32);
       if (q == 0 && ok[nb]) {
@@ -1180,7 +1150,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_draft_impl(const Comb
     const int64_t o = (int64_t)b * a.gamma + k - 1;
     a.tokens[o] = idx;
     a.lse[o] = (p.m + fast_log2(p.s)) * kLn2;
-    a.ytok[o] = a.greedy ? p.key : p.zb * a.invT;
+    a.ytok[o] = a.greedy ? p.key : p.zb;   // sampling partials carry y itself
   }
   if (a.bar && b == 0 && k == 1 && threadIdx.x == 0) *a.bar = 0u;   // grid barrier of the whole-draft kernel
   if (a.best && threadIdx.x < kBestGroups) {

@@ -9,7 +9,7 @@
 // positions are checked in order, the first rejected one is replaced by a
 // target token and the rest dropped, so the output law is the target's.
 // Row statistics (log-sum-exp of t/T; greedy arg-max; the bonus row's
-// group-race draw from exp(t/T)) need the whole vocabulary and are formed here; the accept tests need
+// Gumbel-max draw from exp(t/T)) need the whole vocabulary and are formed here; the accept tests need
 // only t at the drafted token, read directly by the decision kernel.  The
 // residual draw at the first rejection reuses the MFMA sweep (sweep.hip).
 #include "common.hpp"
@@ -49,10 +49,18 @@ __device__ __forceinline__ void wave_row_reduce(RowState& st) {
   }
 }
 
-// KEYMODE 0: no key, 1: arg-max of t, 2: group-race draw from exp(t/T) (the
-// four values of a float4 form one aligned race group).
+// Leader of a thread's Gumbel-max draw over its part of a chunk: weight
+// relative to 2^m, E = -log2 u, index.
+struct RowLead {
+  float wb, eb;
+  int idx;
+};
+
+// KEYMODE 0: no key, 1: arg-max of t, 2: Gumbel-max draw from exp(t/T)
+// (common.hpp; entries visited in increasing index, the leader's weight
+// rescaled with the running max).
 template <int KEYMODE>
-__device__ __forceinline__ void row_fold(RowState& st, const float4 x, int v0, float s2, uint32_t klo,
+__device__ __forceinline__ void row_fold(RowState& st, RowLead& ld, const float4 x, int v0, float s2, uint32_t klo,
                                          uint32_t khi) {
   const float xv[4] = {x.x, x.y, x.z, x.w};
   float y2[4];
@@ -64,7 +72,8 @@ __device__ __forceinline__ void row_fold(RowState& st, const float4 x, int v0, f
 #pragma unroll
   for (int i = 0; i < 4; ++i) e[i] = fast_exp2(y2[i] - mn);
   const float S = (e[0] + e[1]) + (e[2] + e[3]);
-  st.s = st.s * fast_exp2(st.m - mn) + S;
+  const float resc = fast_exp2(st.m - mn);
+  st.s = st.s * resc + S;
   st.m = mn;
   if constexpr (KEYMODE == 1) {
 #pragma unroll
@@ -75,30 +84,38 @@ __device__ __forceinline__ void row_fold(RowState& st, const float4 x, int v0, f
       }
     }
   } else if constexpr (KEYMODE == 2) {
-    const float E = -fast_log2(hash_uniform(elem_hash(klo, khi, (uint32_t)v0)));
-    if (E < S * fast_exp2(mn - st.key)) {
-      const float key = fast_log2(S) + mn - fast_log2(E);
-      if (key > st.key) {
-        const float c = hash_uniform(elem_hash(klo, khi, (uint32_t)(v0 + 1))) * S;
-        st.key = key;
-        st.idx = v0 + group_pick(c, e[0], e[1], e[2], e[3]);
-      }
+    ld.wb *= resc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float E = gumbel_e(klo, khi, (uint32_t)(v0 + i));
+      const bool lead = e[i] * ld.eb > E * ld.wb;
+      ld.wb = lead ? e[i] : ld.wb;
+      ld.eb = lead ? E : ld.eb;
+      ld.idx = lead ? v0 + i : ld.idx;
     }
   }
 }
 
 // One chunk of kRowsPer float4 per thread: every load is issued before the
-// first is used; float4 indices at or past c1 are skipped.
+// first is used; float4 indices at or past c1 are skipped.  A Gumbel-max
+// leader becomes the key log2 w_b + m - log2 E_b at the end.
 template <int KEYMODE>
 __device__ __forceinline__ void row_chunk(RowState& st, const float4* p, int c0, int c1, float s2, uint32_t klo,
                                           uint32_t khi) {
   float4 x[kRowsPer];
 #pragma unroll
   for (int i = 0; i < kRowsPer; ++i) x[i] = p[min(c0 + (int)threadIdx.x + i * kRowsThreads, c1 - 1)];
+  RowLead ld{0.0f, 1.0f, 0x7fffffff};
 #pragma unroll
   for (int i = 0; i < kRowsPer; ++i) {
     const int c = c0 + (int)threadIdx.x + i * kRowsThreads;
-    if (c < c1) row_fold<KEYMODE>(st, x[i], 4 * c, s2, klo, khi);
+    if (c < c1) row_fold<KEYMODE>(st, ld, x[i], 4 * c, s2, klo, khi);
+  }
+  if constexpr (KEYMODE == 2) {
+    if (ld.wb > 0.0f) {
+      st.key = fast_log2(ld.wb) + st.m - fast_log2(ld.eb);
+      st.idx = ld.idx;
+    }
   }
 }
 
