@@ -376,19 +376,24 @@ def main():
         # dominant kernel: the draft sweep -- one launch per position, or the
         # whole-draft kernel (Markov head, bf16, r = 256, B <= 128): one
         # launch for all gamma positions, W2 read once and held in registers
-        sw = per_kernel["draft_sweep"]
-        whole = gru is None and G > 1 and round(sw["launches_per_step"]) == 1
-        pos_per_launch = G if whole else 1
+        # the chained draft (every position in one launch, W2 streamed per
+        # position), else the per-position sweeps or the whole-draft kernel
+        chained = "draft_chain" in per_kernel
+        sw = per_kernel["draft_chain"] if chained else per_kernel["draft_sweep"]
+        whole = not chained and gru is None and G > 1 and round(sw["launches_per_step"]) == 1
+        pos_per_launch = G if (whole or chained) else 1
         # the library's timing events, attached to each dispatch
         # (hipExtLaunchKernel), bracket the kernel's execution alone
         sweep_timing = "library timing events attached to each sweep dispatch, averaged over the timed steps"
         if whole:
             b_sweep = G * (4 * B * V + wbytes * B * r) + wbytes * r * V
-            if os.environ.get("DSPARK_PERSIST_COOP") == "1":
+            if os.environ.get("DSPARK_PERSIST_COOP") != "0":
                 # no dispatch-attached events for a cooperative launch: stream
                 # events around it, which include the ordering gap before it
                 sweep_timing = ("library timing events recorded on the stream around each cooperative launch, "
                                 "averaged over the timed steps")
+        elif chained:
+            b_sweep = G * sweep_bytes(B, V, r, wbytes, None)
         else:
             b_sweep = sweep_bytes(B, V, r, wbytes, 4 if gru is not None else None)
         if gru is None and G >= 3:
@@ -450,7 +455,9 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": measured_traffic(wl.name, B, V, r, T),
-                    "kernel": ("draft_persist (MFMA Markov bias + vocabulary sweep, all positions in one "
+                    "kernel": ("draft_chain (MFMA Markov bias + vocabulary sweep, every position in one "
+                               "launch of persistent workgroups)" if chained else
+                               "draft_persist (MFMA Markov bias + vocabulary sweep, all positions in one "
                                "launch, W2 held in registers)" if whole else
                                "draft_sweep (MFMA Markov bias + vocabulary sweep, one position)" if gru is None
                                else "draft_sweep (MFMA GRU-state bias + vocabulary sweep, one position)"),

@@ -22,8 +22,10 @@
  *    the context's workspace has grown to the shape), so a caller may capture
  *    them into a HIP graph after one call of the same shapes on the context;
  *    a replay re-runs the captured arguments (pointers, seed).  Neither the
- *    cooperative launch (DSPARK_PERSIST_COOP=1) nor the library's own graph
- *    of the draft loop (DSPARK_GRAPH=1) is meant for capture.
+ *    cooperative launch of the whole-draft kernel (the default for small
+ *    batches: capture those with DSPARK_PERSIST=0, or DSPARK_PERSIST_COOP=0
+ *    on an otherwise idle device) nor the library's own graph of the draft
+ *    loop (DSPARK_GRAPH=1) is meant for capture.
  *  - Row-major layouts; strides are in elements.  Logit rows (U, target) are
  *    contiguous over the vocabulary and 16-byte aligned.
  *  - Tokens and request ids are 32-bit.  Request ids are read as unsigned.
@@ -95,7 +97,7 @@ int dspark_check(dspark_ctx* ctx, hipStream_t stream);
  * While enabled, every kernel the context launches carries a start and a
  * stop HIP event attached to its dispatch (they bracket the kernel's
  * execution, not the queue's ordering gap before it; a cooperative launch of
- * the whole-draft kernel, DSPARK_PERSIST_COOP=1, is bracketed by events
+ * the whole-draft kernel, the default for small batches, is bracketed by events
  * recorded on the stream around it instead, which include that gap), and
  * the draft loop is
  * launched kernel by kernel even where a graph was requested.  dspark_timing_read waits
@@ -116,7 +118,8 @@ enum {
   DSPARK_K_GRU = 9,            /* GRU head: s_0 fill and state updates */
   DSPARK_K_DIAG = 10,          /* diagnostic passes (dspark_accept_prob) */
   DSPARK_K_STS = 11,           /* temperature fit: the pass of one position */
-  DSPARK_K_COUNT = 12
+  DSPARK_K_DRAFT_CHAIN = 12,   /* chained draft: every position in one launch */
+  DSPARK_K_COUNT = 13
 };
 int dspark_timing_enable(dspark_ctx* ctx, int enable);
 int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
@@ -153,25 +156,36 @@ int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
  * Logits must be finite.  Errors: DSPARK_EINVAL for shapes/pointers/
  * alignment/temperature < 0 or non-finite.
  *
- * Execution: one vocabulary sweep per position, each taking x_{k-1} from the
- * previous sweep, then one merge.  For bf16 weights with r = 256, small
- * batches (B <= 48 by default) and V <= 16 * 10 * 4 * (compute units), the
- * whole draft instead runs as one launch of one workgroup per compute unit
- * that keeps W2 in registers and separates positions with a grid barrier;
- * the results are the same function of the inputs (tokens and ytok
- * bit-identical, lse to rounding).  Its workgroups must all be resident to
- * pass a barrier: on an otherwise idle device they are; if concurrent
- * kernels hold compute units, the waiting workgroups start as those kernels
- * finish.  Two such draft launches running at once on one device (calls on
- * different streams) can each hold part of it and wait for each other.  The
- * barrier's wait is bounded (about a second): a wait that does not complete
- * gives up, the kernel ends and dspark_check reports DSPARK_EDEVICE.  Issue
- * draft calls on one stream per device, or use the cooperative launch
- * (co-residency guaranteed by the runtime).  Environment, read when the
- * context is created: DSPARK_PERSIST=0 never uses this kernel, =2 uses it
- * for every eligible batch up to 128 requests; DSPARK_PERSIST_COOP=1
- * launches it cooperatively (~15 us more per call), for callers that share
- * the device with other work. */
+ * Execution (every path computes the same function of the inputs: tokens
+ * and ytok bit-identical, lse to rounding):
+ *  - bf16 weights, r in {128, 256}, 65 <= B <= 128 (default): the chained
+ *    draft, one launch for every position.  Persistent workgroups claim
+ *    (position, vocabulary chunk) items from a ticket counter in position
+ *    order; an item of position k starts streaming its U and W2 tiles, waits
+ *    until every item of position k - 1 has published its chunk winners,
+ *    then takes x_{k-1} and sweeps.  Items are claimed in dependency order
+ *    by running workgroups, so the launch makes progress however many of its
+ *    workgroups are resident (concurrent kernels on other streams only slow
+ *    it down).  Its waits are bounded all the same (about a second): a wait
+ *    that gives up lets the item run on, the results are invalid and
+ *    dspark_check reports DSPARK_EDEVICE.  DSPARK_CHAIN=0 selects the
+ *    per-position sweeps instead.
+ *  - bf16 weights, r = 256, B <= 48 (default) and V <= 16 * 10 * 4 * (compute
+ *    units): the whole-draft kernel, one launch of one workgroup per compute
+ *    unit that keeps W2 in registers and separates positions with a grid
+ *    barrier.  Its workgroups must all be resident to pass a barrier, so by
+ *    default it is launched cooperatively (co-residency guaranteed by the
+ *    runtime, also when other streams run kernels; ~15 us more per call).
+ *    DSPARK_PERSIST_COOP=0 launches it plainly, for callers that own an
+ *    otherwise idle device: there, if concurrent kernels hold compute units,
+ *    the waiting workgroups start as those kernels finish, and two such
+ *    launches at once can wait for each other until the bounded barrier
+ *    gives up (DSPARK_EDEVICE from dspark_check).  DSPARK_PERSIST=0 never
+ *    uses this kernel, =2 uses it for every eligible batch up to 128
+ *    requests (ahead of the chained draft).
+ *  - otherwise: one vocabulary sweep per position, each taking x_{k-1} from
+ *    the previous sweep, then one merge.
+ * Environment variables are read when the context is created. */
 int dspark_draft_markov(dspark_ctx* ctx, hipStream_t stream,
                         int B, int gamma, int V, int r, dspark_dtype wdtype,
                         const float* U, int64_t u_stride_b, int64_t u_stride_k,

@@ -60,11 +60,19 @@ struct dspark_ctx {
   // B = 16, 1.3x at 32, 1.1x at 40-48, even at 56-64, 0.75x at 128).
   int persist_max_b = 48;
   int coop = -1;
-  // launch it cooperatively (co-residency guaranteed by the runtime, ~15 us
-  // more per call here) instead of as a plain launch of one workgroup per CU
-  bool persist_coop = false;
+  // launch it cooperatively (co-residency guaranteed by the runtime, also
+  // under concurrent kernels; ~15 us more per call here); false: a plain
+  // launch of one workgroup per CU, for callers that own an idle device
+  bool persist_coop = true;
   int bar_test = 0;               // failure injection (tests): barriers time out
   unsigned int* bar = nullptr;    // its grid barrier counter (inside dev_err's block)
+  // chained draft kernel (Markov head, bf16, r in {128, 256}, one request quad
+  // of three or four 32-row groups): every position in one launch; its ticket
+  // and per-position counters (inside dev_err's block, 33 words)
+  bool use_chain = true;
+  unsigned int* chain = nullptr;  // 65 words: tickets, then per-position counters from word 32
+  unsigned int* chain_flags = nullptr;   // one 128-byte line per workgroup (kChainMaxGrid)
+  int chain_wg_per_cu = -1;       // resident workgroups per CU (-1 = not yet asked)
   // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
   int draft_nt = 2, draft_depth = 1;
   // the GRU head's sweep holds its state as hi + lo fragments, so its
@@ -396,6 +404,33 @@ bool use_persist(dspark_ctx* c, int B, int V, int r, int wdtype) {
   return c->coop == 1;
 }
 
+// Chained draft eligibility: Markov head, bf16, r in {128, 256}, a batch of
+// three or four 32-row groups (65..128 requests: one request quad, the
+// shared-tile layout), and the kernel's ring shape.
+const void* chain_kernel_for(dspark_ctx* c, int B, int r, int wdtype, int mode) {
+  if (!c->use_chain || wdtype != DSPARK_BF16 || B < 65 || B > 128) return nullptr;
+  const void* fn = draft_chain_kernel(r, mode, c->draft_depth, c->draft_nt);
+  if (!fn) return nullptr;
+  if (c->chain_wg_per_cu < 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      nb = 0;
+    }
+    c->chain_wg_per_cu = nb;
+  }
+  if (c->chain_wg_per_cu < 1) return nullptr;
+  if (!c->chain_flags) {
+    const size_t bytes = (size_t)kChainMaxGrid * 128;
+    if (hipMalloc(&c->chain_flags, bytes) != hipSuccess || hipMemset(c->chain_flags, 0, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      c->chain_flags = nullptr;
+      return nullptr;
+    }
+  }
+  return fn;
+}
+
 }  // namespace
 
 // The draft loop of either head: gamma sweeps (+ gamma - 1 GRU updates and
@@ -477,6 +512,23 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
              : klaunch(c, DSPARK_K_DRAFT_SWEEP, draft_persist_kernel(mode), dim3(c->cu_count), dim3(256), &sa, stream);
     if (rc) return rc;
     return klaunch(c, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), &ca, stream);
+  }
+  const void* cfn = gru ? nullptr : chain_kernel_for(c, B, r, (int)wdtype, mode);
+  if (cfn) {
+    // every position in one launch of persistent workgroups, then the merge
+    // (which also clears the launch's counters)
+    sa.best = c->best;
+    sa.chain = c->chain;
+    sa.chain_flags = c->chain_flags;
+    sa.bar_test = c->bar_test;
+    ca.chain = c->chain;
+    const long items = (long)gamma * pl.n_vc;
+    const long resident = (long)c->chain_wg_per_cu * c->cu_count;
+    const int grid = (int)std::min(std::min(items, resident), (long)kChainMaxGrid);
+    std::vector<KernelNode> nodes(2);
+    set_node(nodes[0], DSPARK_K_DRAFT_CHAIN, cfn, dim3(grid), dim3(256), sa);
+    set_node(nodes[1], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
+    return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 16, grid, pl.n_vc);
   }
   const int hs = gru ? 1 : 0;
   const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, hs ? c->gru_depth : c->draft_depth,
@@ -860,22 +912,29 @@ int dspark_create(dspark_ctx** out, int device) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
     c->cu_count = prop.multiProcessorCount;
-  if (hipMalloc(&c->dev_err, 256) != hipSuccess || hipMemset(c->dev_err, 0, 256) != hipSuccess) {
+  if (hipMalloc(&c->dev_err, 1024) != hipSuccess || hipMemset(c->dev_err, 0, 1024) != hipSuccess) {
     (void)hipGetLastError();
     delete c;
     return DSPARK_EHIP;
   }
   c->bar = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(c->dev_err) + 128);
+  c->chain = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(c->dev_err) + 512);
+  // chained draft kernel (every position in one launch, 65..128 requests):
+  // "0" switches it off (per-position sweeps)
+  const char* ch = getenv("DSPARK_CHAIN");
+  if (ch && ch[0] == '0' && ch[1] == 0) c->use_chain = false;
   // whole-draft kernel: "0" never, "1" small batches (default), "2" every
   // eligible batch (up to 128 requests)
   const char* pk = getenv("DSPARK_PERSIST");
   if (pk && pk[0] == '0' && pk[1] == 0) c->persist_max_b = 0;
   if (pk && pk[0] == '2' && pk[1] == 0) c->persist_max_b = 128;
-  // failure injection for tests: every grid barrier of the whole-draft kernel
-  // waits for one arrival too many and gives up after 64 polls (the kernel
-  // still ends; the call's results are invalid and the error flag is raised)
+  // whole-draft kernel: "0" launches it plainly instead of cooperatively
   const char* pc = getenv("DSPARK_PERSIST_COOP");
-  if (pc && pc[0] == '1' && pc[1] == 0) c->persist_coop = true;
+  if (pc && pc[0] == '0' && pc[1] == 0) c->persist_coop = false;
+  // failure injection for tests: every grid barrier of the whole-draft kernel
+  // and every wait of the chained draft waits for a release that never comes
+  // and gives up after 64 polls (the kernels still end; the call's results
+  // are invalid and the error flag is raised)
   const char* bt = getenv("DSPARK_BARRIER_TEST");
   if (bt && bt[0] == '1' && bt[1] == 0) c->bar_test = 1;
   // The draft loop goes kernel by kernel by default: on this runtime a
@@ -950,6 +1009,7 @@ void dspark_destroy(dspark_ctx* c) {
     if (c->best) (void)hipFree(c->best);
     if (c->sts_buf) (void)hipFree(c->sts_buf);
     if (c->dev_err) (void)hipFree(c->dev_err);
+    if (c->chain_flags) (void)hipFree(c->chain_flags);
   }
   delete c;
 }

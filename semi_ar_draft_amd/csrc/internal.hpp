@@ -58,6 +58,12 @@ struct SweepArgs {
   // arrival too many and gives up after 64 polls)
   unsigned int* bar;
   int bar_test;
+  // chained draft: [0] ticket counter, [32 + k] finished items of position
+  // k (zero at launch; the draft combine clears them); per-workgroup release
+  // flags (word 32 b of workgroup b: the last position released, zero at
+  // launch and cleared again by the launch's last item)
+  unsigned int* chain;
+  unsigned int* chain_flags;
   int32_t* err;
 };
 
@@ -68,6 +74,7 @@ struct CombineArgs {
   const int2* pi;
   unsigned long long* best;      // draft: [gamma][kBestGroups][B] running bests, cleared here
   unsigned int* bar;             // draft: the whole-draft kernel's barrier counter, reset here (nullable)
+  unsigned int* chain;           // draft: the chained kernel's counters, reset here (nullable)
   int32_t* tokens;               // draft: [B][gamma]
   float* lse;
   float* ytok;
@@ -200,6 +207,12 @@ const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs)
 // cooperative launch); n_vc = 4 * grid.  nullptr for other modes.
 constexpr int kPersistTiles = 10;
 const void* draft_persist_kernel(int mode);
+// Chained draft (Markov head, bf16, B <= 128, r in {128, 256}): every
+// position in one launch of persistent workgroups claiming (position, chunk)
+// items in order; ring shapes (depth, nt) in {(1, 2), (2, 1)} for r = 256,
+// (1, 2) for r = 128.  nullptr otherwise.
+const void* draft_chain_kernel(int r, int mode, int depth, int nt);
+constexpr int kChainMaxGrid = 2048;   // workgroups of a chained draft launch (release flags)
 const void* combine_draft_kernel();
 const void* combine_resid_kernel();
 const void* combine_alpha_kernel();

@@ -327,6 +327,10 @@ struct WaveRows {
   // the residual's normalisers.  In the draft the previous token is the
   // maximum over the previous position's slot groups: the four lanes of a
   // row (q = 0..3) read a quarter of the groups each and share the maximum.
+  // kCoherent: the previous position's slots were written by workgroups of
+  // the same launch (the chained draft kernel), so they are read with
+  // agent-scope atomic loads rather than through the caches.
+  template <bool kCoherent = false>
   __device__ __forceinline__ void setup_rest(const SweepArgs& a, int q) {
     // loads that do not depend on the previous token go out first (the
     // error-flag atomic below would otherwise keep them behind the chain)
@@ -362,7 +366,9 @@ struct WaveRows {
         if (ok[nb]) {
 #pragma unroll
           for (int i = 0; i < kBestGroups / 4; ++i) {
-            const unsigned long long v = a.best_prev[(int64_t)(q * (kBestGroups / 4) + i) * a.B + rows[nb]];
+            const unsigned long long* sp = a.best_prev + (int64_t)(q * (kBestGroups / 4) + i) * a.B + rows[nb];
+            const unsigned long long v =
+                kCoherent ? __hip_atomic_load(sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *sp;
             pb[nb] = v > pb[nb] ? v : pb[nb];
           }
         }
@@ -854,6 +860,213 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
   w.finish(a, st, q, vc);
 }
 
+// Chained draft (Markov head, bf16, one request quad: B <= 128): every
+// position in one launch.  The work items (position k, vocabulary chunk) are
+// those of the per-position shared-tile sweep, claimed from one ticket
+// counter in (k, chunk) order by a grid of persistent workgroups.  An item
+// of position k first issues its first D ring steps (U and W2 do not depend
+// on the tokens), then waits until every item of position k - 1 has
+// published its chunk winners, then takes x_{k-1} from the slot groups,
+// gathers the W1 rows and runs the sweep.  Items are claimed in dependency
+// order and a workgroup finishes its item before it claims the next, so
+// every item waited on is held by a running workgroup: the launch never
+// depends on how many of its workgroups are resident (concurrent kernels
+// only slow it down).  The wait is bounded all the same (it raises the
+// barrier error bit and lets the item run on).
+//
+// Counters (zero at launch; the draft combine clears them): chain[0] the
+// ticket counter, chain[32 + k] the finished items of position k (another
+// cache line).  The workgroup whose item completes position k releases the
+// waiting workgroups by writing k into each one's own flag word (flags[32 b],
+// one 128-byte line per workgroup): hundreds of workgroups polling one
+// counter slowed the streaming of the ones still working (straggling items
+// took twice the median time).  The item that completes the last position
+// writes 0 into every flag, so each launch (a graph replay too) starts from
+// zeroed flags.
+constexpr unsigned kChainSpinLimit = 1u << 20;
+
+template <int R, int MODE, int D, int NT>
+__global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
+  using WR = WaveRows<uint16_t, R, MODE, 0>;
+  using FragT = typename WR::FragT;
+  constexpr int NS = WR::NS;
+  constexpr int NB = D + 1;
+  constexpr int kRowBytes = R * 2;
+  constexpr int kCPR = kRowBytes / 16;
+  constexpr int kTileBytes = kTileV * kRowBytes;
+  constexpr int kW2Bytes = NT * kTileBytes;
+  constexpr int kW2Inst = kW2Bytes / (kWavesPerBlock * 1024);
+  constexpr int kFPR = 4 * NT;
+  constexpr int kRPI = 16 / NT;
+  constexpr int kSwzShift = 2 / NT;
+  constexpr int kUInst = kRowsPerWave / kRPI;
+  constexpr int kWaveRowBytes = kRowsPerWave * kFPR * 16;
+  constexpr int kG = kW2Inst + kUInst;
+  constexpr int kUOff = kW2Bytes;
+  constexpr int kSlotBytes = kW2Bytes + kWavesPerBlock * kWaveRowBytes;
+  static_assert(NT == 1 || NT == 2, "steps of one or two tiles");
+  static_assert(MODE == kModeDraftGreedy || MODE == kModeDraftSample, "draft modes only");
+  static_assert(D >= 1 && (D - 1) * kG < 64, "ring depth");
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NB * kSlotBytes];
+  // the claimed ticket is handed to every wave through the last word of the
+  // ring (one more LDS word would cost the second workgroup per CU): that
+  // word is first overwritten by the loop's first load into the last slot,
+  // which follows a barrier every wave reaches after reading it
+  int* const s_item = reinterpret_cast<int*>(ring + NB * kSlotBytes - 4);
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int q = lane >> 4;
+  const int j = lane & 15;
+  const int per_pos = a0.n_vc;
+  const int total = per_pos * a0.gamma;
+  const int n_steps = (a0.n_tiles + NT - 1) / NT;
+  const unsigned char* W2b = static_cast<const unsigned char*>(a0.W2);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8_t*)ring;
+  const uint32_t w2_lds = __builtin_amdgcn_readfirstlane(wid * kW2Inst * 1024);
+  const uint32_t u_lds = __builtin_amdgcn_readfirstlane(kUOff + wid * kWaveRowBytes);
+
+  if (threadIdx.x == 0)
+    *s_item = (int)__hip_atomic_fetch_add(a0.chain, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int item = *s_item;
+  while (item < total) {                                  // uniform over the block
+    const int k = item / per_pos + 1;
+    const int vc = item - (k - 1) * per_pos;
+    SweepArgs a = a0;
+    a.k = k;
+    a.pf = a0.pf + (size_t)(k - 1) * a0.B * a0.n_vc;
+    a.pi = a0.pi + (size_t)(k - 1) * a0.B * a0.n_vc;
+    a.best = a0.best + (size_t)(k - 1) * kBestGroups * a0.B;
+    a.best_prev = k > 1 ? a0.best + (size_t)(k - 2) * kBestGroups * a0.B : nullptr;
+    WR w;
+    w.setup_rows(a, wid, j);
+    const bool wave_active = __any(w.ok[0] || w.ok[1]);
+    LaneState st[2];
+    lane_init(st[0]);
+    lane_init(st[1]);
+    const int t0 = min(NT * (int)((int64_t)n_steps * vc / a.n_vc), a.n_tiles);
+    const int t1 = min(NT * (int)((int64_t)n_steps * (vc + 1) / a.n_vc), a.n_tiles);
+
+    int64_t uoff_d[kUInst];
+    int ucol_d[kUInst];
+#pragma unroll
+    for (int m = 0; m < kUInst; ++m) {
+      const int row = m * kRPI + lane / kFPR;
+      ucol_d[m] = 4 * ((lane % kFPR) ^ ((row >> kSwzShift) & (kFPR - 1)));
+      uoff_d[m] = __shfl(w.uoff[row >> 4], row & 15, 64);
+    }
+    auto issue = [&](int t, int sidx) {
+      const uint32_t base = ring_lds + sidx * kSlotBytes;
+#pragma unroll
+      for (int p = 0; p < kW2Inst; ++p) {
+        const int P = (wid * kW2Inst + p) * 64 + lane;
+        const int r = P / kCPR;
+        const int c = (P % kCPR) ^ (r & 15);
+        const int tc = min(t + r / kTileV, t1 - 1);
+        dma16(W2b + (int64_t)tc * kTileBytes + (r % kTileV) * kRowBytes + c * 16, base + w2_lds + p * 1024);
+      }
+      int vcol[kUInst];
+#pragma unroll
+      for (int m = 0; m < kUInst; ++m) vcol[m] = min(t * kTileV + ucol_d[m], t1 * kTileV - 4);
+#pragma unroll
+      for (int m = 0; m < kUInst; ++m) dma16(a.U + uoff_d[m] + vcol[m], base + u_lds + m * 1024);
+    };
+    auto load_tile = [&](int h, const unsigned char* sl, FragT (&A)[NS], float4 (&uu)[2]) {
+      const unsigned char* row = sl + (h * kTileV + j) * kRowBytes;
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) A[s2] = *reinterpret_cast<const FragT*>(row + (((4 * s2 + q) ^ j) * 16));
+      const int col = (4 * h + q) ^ ((j >> kSwzShift) & (kFPR - 1));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int off = wid * kWaveRowBytes + ((nb * 16 + j) * kFPR + col) * 16;
+        uu[nb] = *reinterpret_cast<const float4*>(sl + kUOff + off);
+      }
+    };
+    auto compute = [&](int t, const unsigned char* sl) {
+      if constexpr (NT == 2) {
+        f32x4_t acc[NT][2];
+        FragT A[NS];
+        float4 uu[2];
+        load_tile(0, sl, A, uu);
+        w.mma_tile(acc[0], A, uu);
+        if (t + 1 < t1) {                                  // uniform over the block
+          load_tile(1, sl, A, uu);
+          w.mma_tile(acc[1], A, uu);
+          w.template fold<2>(a, st, acc, t, q);
+        } else {
+          const f32x4_t acc1[1][2] = {{acc[0][0], acc[0][1]}};
+          w.template fold<1>(a, st, acc1, t, q);
+        }
+      } else {
+        f32x4_t acc[1][2];
+        FragT A[NS];
+        float4 uu[2];
+        load_tile(0, sl, A, uu);
+        w.mma_tile(acc[0], A, uu);
+        w.template fold<1>(a, st, acc, t, q);
+      }
+    };
+
+    if (t0 < t1) {
+#pragma unroll
+      for (int p = 0; p < D; ++p) issue(t0 + p * NT, p);
+    }
+    // every item of position k - 1 has published its winners
+    if (k > 1) {
+      if (threadIdx.x == 0) {
+        // the host's failure injection waits for a value nobody writes
+        const unsigned want = a0.bar_test ? 0x80u : (unsigned)(k - 1);
+        const unsigned limit = a0.bar_test ? 64u : kChainSpinLimit;
+        const unsigned* flag = a0.chain_flags + 32 * blockIdx.x;
+        unsigned spins = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++spins > limit) {
+            atomicOr(a0.err, kErrBarrier);
+            break;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    w.template setup_rest<true>(a, q);
+    // drain visibly to the compiler: the set-up loads and the first ring
+    // steps are complete, and no wait for them lands inside the loop
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    for (int t = t0; t < t1; t += NB * NT) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int ts = t + u * NT;
+        if (ts >= t1) break;                               // uniform over the block
+        ring_wait_barrier<(D - 1) * kG>();
+        issue(ts + D * NT, (u + D) % NB);
+        if (wave_active) compute(ts, ring + u * kSlotBytes);
+      }
+    }
+    vm_drain();
+    w.finish(a, st, q, vc);
+    vm_drain();                                            // this wave's partials and slot atomics are done
+    __syncthreads();                                       // every wave's; no wave reads the ring any more
+    if (wid == 0) {
+      unsigned before = 0;
+      if (lane == 0) before = __hip_atomic_fetch_add(a0.chain + 32 + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      before = __shfl(before, 0, 64);
+      if (before == (unsigned)per_pos - 1u) {
+        // the last item of position k: release every workgroup (after the
+        // last position: clear the flags for the next launch)
+        const unsigned v = k < a0.gamma ? (unsigned)k : 0u;
+        for (int b = lane; b < (int)gridDim.x; b += 64)
+          __hip_atomic_store(a0.chain_flags + 32 * b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0)
+        *s_item = (int)__hip_atomic_fetch_add(a0.chain, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    item = *s_item;
+  }
+}
+
 // Whole-draft variant (Markov head, bf16 weights, r = 256, B <= 128): one
 // launch runs every position.  Each wave owns up to kPersistTiles 16-wide
 // vocabulary tiles and keeps their W2 fragments (the MFMA A operand) in
@@ -1153,6 +1366,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_draft_impl(const Comb
     a.ytok[o] = a.greedy ? p.key : p.zb;   // sampling partials carry y itself
   }
   if (a.bar && b == 0 && k == 1 && threadIdx.x == 0) *a.bar = 0u;   // grid barrier of the whole-draft kernel
+  if (a.chain && b == 0 && k == 1 && threadIdx.x <= a.gamma)   // chained draft counters
+    a.chain[threadIdx.x == 0 ? 0 : 32 + threadIdx.x] = 0u;
   if (a.best && threadIdx.x < kBestGroups) {
     unsigned long long* slot = a.best + ((int64_t)(k - 1) * kBestGroups + threadIdx.x) * a.B + b;
     __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1286,6 +1501,18 @@ const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs)
   }
   if (wdtype == 1) return hs ? private_for_r<uint16_t, 1>(r, mode) : private_for_r<uint16_t, 0>(r, mode);
   if (wdtype == 0) return hs ? private_for_r<float, 1>(r, mode) : private_for_r<float, 0>(r, mode);
+  return nullptr;
+}
+
+const void* draft_chain_kernel(int r, int mode, int depth, int nt) {
+  if (mode != kModeDraftGreedy && mode != kModeDraftSample) return nullptr;
+  const bool g = mode == kModeDraftGreedy;
+  if (r == 256 && nt == 2 && depth == 1)
+    return g ? (const void*)&draft_chain_impl<256, kModeDraftGreedy, 1, 2> : (const void*)&draft_chain_impl<256, kModeDraftSample, 1, 2>;
+  if (r == 256 && nt == 1 && depth == 2)
+    return g ? (const void*)&draft_chain_impl<256, kModeDraftGreedy, 2, 1> : (const void*)&draft_chain_impl<256, kModeDraftSample, 2, 1>;
+  if (r == 128 && nt == 2 && depth == 1)
+    return g ? (const void*)&draft_chain_impl<128, kModeDraftGreedy, 1, 2> : (const void*)&draft_chain_impl<128, kModeDraftSample, 1, 2>;
   return nullptr;
 }
 

@@ -1,9 +1,11 @@
 """GPU: a whole step (draft, confidence, verify) captured by the caller into
 a HIP graph after one call of the same shape (so the context's workspace
 exists) replays to the eager result, every replay, with other eager work
-and synchronisations between replays -- for the per-position draft path and
-for the whole-draft kernel.  The library records no memset into a graph:
-every clear it needs is a kernel."""
+and synchronisations between replays (and two replays back to back) -- for
+the per-position draft path, the chained draft and the whole-draft kernel
+(plain launch; its default cooperative launch is not meant for capture).
+The library records no memset into a graph: every clear it needs is a
+kernel."""
 import os
 
 import pytest
@@ -16,13 +18,25 @@ from test_gpu_parity import to_dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("B,persist", [(70, "0"), (16, "2")], ids=["per_position", "whole_draft"])
-def test_captured_step_replays_to_the_eager_result(B, persist):
-    os.environ["DSPARK_PERSIST"] = persist
+ENVS = [
+    (70, dict(DSPARK_CHAIN="0")),                                 # per-position sweeps
+    (70, {}),                                                     # chained draft (default at this size)
+    (16, dict(DSPARK_PERSIST="2", DSPARK_PERSIST_COOP="0")),      # whole-draft kernel, plain launch
+]
+
+
+@pytest.mark.parametrize("B,env", ENVS, ids=["per_position", "chained", "whole_draft"])
+def test_captured_step_replays_to_the_eager_result(B, env):
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
     try:
         ctx = dk.Context(0)
     finally:
-        del os.environ["DSPARK_PERSIST"]
+        for k, v in old.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
     wl = synth.WORKLOADS["sample"].with_(B=B, V=4096, d_h=32, d_e=32, sts=True)
     d = to_dev(synth.make_inputs(wl, seed=71))
     G = wl.gamma
@@ -54,7 +68,7 @@ def test_captured_step_replays_to_the_eager_result(B, persist):
             step(5)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        print(f"capturing the step, B={B}, DSPARK_PERSIST={persist}", flush=True)
+        print(f"capturing the step, B={B}, env={env}", flush=True)
         with torch.cuda.graph(g, stream=s):
             step(5)
         torch.cuda.synchronize()
@@ -67,6 +81,13 @@ def test_captured_step_replays_to_the_eager_result(B, persist):
             torch.cuda.synchronize()
             for name, a, b in zip(("tok", "lse", "ytok", "conf", "surv", "acc", "out"), ref, bufs):
                 assert torch.equal(a, b), f"replay {rep}: {name}"
+        for x in bufs:
+            x.zero_()
+        g.replay()                                      # two replays back to back
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("tok", "lse", "ytok", "conf", "surv", "acc", "out"), ref, bufs):
+            assert torch.equal(a, b), f"back-to-back replay: {name}"
         ctx.check()
     finally:
         ctx.close()

@@ -10,9 +10,9 @@ vocabulary tile, a long draft, the full-size sampling workload on sampled
 requests), against the per-position sweeps (greedy full size: z at the
 drafted token and the tokens are bit-identical, the MFMA sums being taken in
 the same order), at the largest vocabulary it covers and one tile past it
-(which falls back to the per-position sweeps), launched cooperatively
-(identical results to the plain launch), and with its barrier made to time
-out from the host (the kernel still ends and the error is reported).
+(which falls back to the per-position sweeps), launched plainly (identical
+results to the default cooperative launch), and with its barrier made to
+time out from the host (the kernel still ends and the error is reported).
 """
 import os
 
@@ -140,16 +140,16 @@ def test_persist_vocabulary_limit(pctx):
         assert np.array_equal(a[2].cpu().numpy(), b[2].cpu().numpy())
 
 
-def test_persist_cooperative_launch_matches_plain(pctx):
+def test_persist_plain_launch_matches_cooperative(pctx):
     wl = synth.WORKLOADS["sample"].with_(B=24, gamma=5, V=20480, conf=False)
     inp = synth.make_inputs(wl, seed=13)
     d = to_dev(inp)
-    cctx = make_ctx(DSPARK_PERSIST="2", DSPARK_PERSIST_COOP="1")
+    pl = make_ctx(DSPARK_PERSIST="2", DSPARK_PERSIST_COOP="0")
     try:
-        print("cooperative launch of the whole-draft kernel", flush=True)
-        n_c, a = draft_launches(cctx, d, 1.0, 8, wl.gamma)
+        print("plain launch of the whole-draft kernel", flush=True)
+        n_c, a = draft_launches(pl, d, 1.0, 8, wl.gamma)
     finally:
-        cctx.close()
+        pl.close()
     n_p, b = draft_launches(pctx, d, 1.0, 8, wl.gamma)
     assert n_c == 1 and n_p == 1
     for x, y in zip(a, b):
