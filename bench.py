@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle step (new seed each pass) until this much time has passed")
     ap.add_argument("--cpu-max-passes", type=int, default=8)
+    ap.add_argument("--cpu-single-sample", type=int, default=32,
+                    help="requests of the batch the single-thread oracle run covers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-diag", action="store_true",
                     help="skip timing the acceptance-probability diagnostic pass")
@@ -504,29 +506,83 @@ def main():
     # every position, W2 once, the bias vectors of every position)
     wbytes = 2 if d["W1"].dtype == torch.bfloat16 else 4
     n_rej_all = float((A < Ks).sum().item()) / args.steps
+    # the blueprint's formula: W2 once per position, every target row up to
+    # K_b + 1, and the residual's rows and W2 pass
+    step_bytes_formula = (G * (4.0 * B * V + wbytes * r * V + (4 if gru is not None else wbytes) * B * r)
+                          + (2.0 * B * G * (wl.d_h + wl.d_e) if has_conf else 0.0)
+                          + 4.0 * V * float((Ks + 1).sum().item()) / args.steps
+                          + (8.0 * V * n_rej_all + wbytes * r * V if (T > 0 and n_rej_all > 0) else 0.0))
     step_bytes = (G * (4.0 * B * V + (4 if gru is not None else wbytes) * B * r) + wbytes * r * V
                   + (2.0 * B * G * (wl.d_h + wl.d_e) if has_conf else 0.0)
                   + 4.0 * V * needed_rows
                   + (8.0 * V * n_rej_all + wbytes * r * V if (T > 0 and n_rej_all > 0) else 0.0))
 
+    # the timed steps 0 and 1 once more (the step is a deterministic function
+    # of its inputs and seed), kept for the comparison with the oracle below
+    gpu_steps = []
+    if not args.no_cpu_baseline and not sched:
+        for i in range(min(2, args.cpu_max_passes)):
+            step(i, log=0)
+            torch.cuda.synchronize()
+            gpu_steps.append({"tok": tok.cpu().numpy(), "lse": lse.cpu().numpy(), "ytok": ytok.cpu().numpy(),
+                              "conf": conf.cpu().numpy(), "surv": surv.cpu().numpy(),
+                              "acc": A_log[0].cpu().numpy(), "out": out.cpu().numpy()})
+        ctx.check()
+
     cpu = None
+    parity = None
     if not args.no_cpu_baseline and not sched:
         import oracle
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+        sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests"))
+        from parity import Report, compare_draft, compare_confidence, compare_verify
         n = min(args.cpu_sample, B)
         rows = list(range(n))
         t = time.time()
         passes = 0
+        refs = []
         while passes < args.cpu_max_passes and (passes == 0 or time.time() - t < args.cpu_seconds):
-            oracle.run_step(inp, seed=args.seed ^ passes, rows=rows)
+            r_ = oracle.run_step(inp, seed=args.seed ^ passes, rows=rows)
+            if passes < len(gpu_steps):
+                refs.append(r_)
             passes += 1
         dt = time.time() - t
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        # one host thread, on a smaller sample of the same batch
+        n1 = min(args.cpu_single_sample, B)
+        with threadpool_limits(limits=1):
+            t1 = time.time()
+            oracle.run_step(inp, seed=args.seed, rows=list(range(n1)))
+            dt1 = time.time() - t1
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+        except OSError:
+            pass
         cpu = {"value": round(passes * n * G / dt, 2), "unit": "verified draft positions/s", "cores": threads,
                "kind": "oracle", "sample": f"{passes} step(s) of {n} of the {B} requests (all {G} positions, "
-               f"draft+confidence+verify), float64 numpy, {dt:.1f}s"}
-        print(f"[bench] cpu oracle: {cpu['value']} positions/s on {threads} threads", file=sys.stderr,
-              flush=True)
+               f"draft+confidence+verify), float64 numpy, {dt:.1f}s",
+               "single_thread": {"value": round(n1 * G / dt1, 2), "cores": 1,
+                                 "sample": f"1 step of {n1} of the {B} requests, {dt1:.1f}s"},
+               "host": {"cpu_model": model, "nproc": os.cpu_count(),
+                        "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}}
+        print(f"[bench] cpu oracle: {cpu['value']} positions/s on {threads} threads, "
+              f"{cpu['single_thread']['value']} on one", file=sys.stderr, flush=True)
+        # the GPU's timed steps 0 and 1 against the oracle's runs of the same
+        # seeds: tokens and accept lengths exact, values within 1e-3 relative,
+        # near-ties (oracle decision margin below 1e-4) counted, not compared
+        rep = Report()
+        for g, ref in zip(gpu_steps, refs):
+            sl = (lambda x: x[:n])
+            rp, taint = compare_draft(sl(g["tok"]), sl(g["lse"]), sl(g["ytok"]), ref.draft, rep=rep)
+            compare_confidence(sl(g["conf"]), sl(g["surv"]), ref.conf, taint, rep=rep)
+            compare_verify(sl(g["acc"]), sl(g["out"]), ref.ver, taint, None, rep=rep)
+        if refs:
+            parity = {"steps_compared": len(refs), "requests": n, "compared": rep.compared,
+                      "near_ties": rep.ties, "max_rel_err": float(f"{rep.max_rel:.3e}"), "parity_ok": rep.ok(),
+                      "problems": rep.problems[:5]}
+            print(f"[bench] parity vs oracle: {rep.summary()}", file=sys.stderr, flush=True)
 
     line = {
         "metric": METRIC,
@@ -549,8 +605,13 @@ def main():
                    "B": B, "gamma": G, "V": V, "r": r, "temperature": T,
                    "positions_per_step": positions / args.steps,
                    "parallelism": "single GPU"},
+        # the least a step must move: W2 once per step, target rows up to the
+        # first rejection (or K_b + 1)
         "step_alg_bytes": step_bytes,
         "step_alg_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        # the blueprint's count: W2 once per position, target rows 1 .. K_b + 1
+        "step_alg_bytes_formula": step_bytes_formula,
+        "step_alg_GBps_formula": round(step_bytes_formula / (ms_per_step * 1e-3) / 1e9, 1),
         "accepted_per_step": float(A.sum().item()) / args.steps,
         # accepted drafts and emitted tokens (accepted + one correction or
         # bonus token per request) per second of the timed steps
@@ -558,6 +619,9 @@ def main():
         "emitted_tokens_per_s": round(float(A.sum().item() + B * args.steps) / (elapsed_ms / 1e3), 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
+        "near_ties": None if parity is None else parity["near_ties"],
+        "parity_ok": None if parity is None else parity["parity_ok"],
         "accept_prob": diag,
         "per_kernel": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                        for k, v in per_kernel.items()},
