@@ -194,6 +194,33 @@ int dspark_draft_markov(dspark_ctx* ctx, hipStream_t stream,
                         float temperature, uint64_t seed,
                         int32_t* tokens, float* lse, float* ytok);
 
+/* Allocation-free variant of dspark_draft_markov, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, same results (bit-identical tokens,
+ * lse and ytok) as dspark_draft_markov with the same context settings, except
+ * that it never uses the whole-draft kernel (small batches run the
+ * per-position sweeps).  Its partials, running-best slot groups and
+ * chained-draft counters live in one file-scope device array of 16 MiB per
+ * GPU (held until the process ends), whose device address is taken once per
+ * device when a context is created there; the call allocates nothing, creates
+ * no event or graph and launches its kernels directly (the context's timing
+ * and graph switches are ignored).  Limits: B * n_chunks * gamma * 24 bytes
+ * of partials within 15,040 KiB (the headline shape B = 128, gamma = 7,
+ * V = 151936 needs 10,752 KiB; gamma <= 9 at B = 128) and B * gamma <= 8192;
+ * a larger shape returns DSPARK_EINVAL with the sizes in the message.
+ * Every call on a GPU, from any context, shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Each call leaves the array's slot groups and
+ * counters zero for the next one.  DSPARK_EHIP if the array's address could
+ * not be taken when the context was created. */
+int dspark_draft_markov_static(dspark_ctx* ctx, hipStream_t stream,
+                               int B, int gamma, int V, int r, dspark_dtype wdtype,
+                               const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                               const void* W1, const void* W2,
+                               const int32_t* anchor, const uint32_t* req_ids,
+                               float temperature, uint64_t seed,
+                               int32_t* tokens, float* lse, float* ytok);
+
 /* Semi-autoregressive draft with the RNN (GRU) head.
  *
  * [blog] "RNN Head：长程依赖"; [summary] section 3 (the state-vector head).

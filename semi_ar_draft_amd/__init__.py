@@ -22,7 +22,7 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 
 EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
-    "dspark_draft_markov", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
+    "dspark_draft_markov", "dspark_draft_markov_static", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
     "dspark_verify_packed", "dspark_accept_prob", "dspark_sts_fit",
     "dspark_timing_enable", "dspark_timing_read",
 )
@@ -67,6 +67,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_draft_markov.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
         _vp, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp, _vp]
+    lib.dspark_draft_markov_static.restype = _i32
+    lib.dspark_draft_markov_static.argtypes = lib.dspark_draft_markov.argtypes
     lib.dspark_draft_rnn.restype = _i32
     lib.dspark_draft_rnn.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -194,7 +196,9 @@ class Context:
 
     # -- dspark_draft_markov ------------------------------------------------
     def draft_markov(self, U, W1, W2, anchor, req_ids, temperature: float, seed: int, gamma: int,
-                     out=None, stream=None):
+                     out=None, stream=None, static: bool = False):
+        """dspark_draft_markov, or with static=True dspark_draft_markov_static
+        (the allocation-free variant: its scratch is a fixed per-GPU array)."""
         dev = self.device
         sb, sk = _logits3(U, "U", dev)
         B, rows, V = U.shape
@@ -215,7 +219,8 @@ class Context:
                    torch.empty((B, gamma), dtype=torch.float32, device=dev),
                    torch.empty((B, gamma), dtype=torch.float32, device=dev))
         tokens, lse, ytok = out
-        self._rc(self.lib.dspark_draft_markov(
+        fn = self.lib.dspark_draft_markov_static if static else self.lib.dspark_draft_markov
+        self._rc(fn(
             self._h, _stream(dev, stream), B, gamma, V, r, _wdtype(W1),
             U.data_ptr(), sb, sk, W1.data_ptr(), W2.data_ptr(), anchor.data_ptr(),
             _ptr(req_ids), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,

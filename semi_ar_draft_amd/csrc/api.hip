@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -19,7 +20,52 @@
 
 using namespace dspark;
 
+// Scratch of the allocation-free draft entry point (dspark_draft_markov_static):
+// chained-draft counters and release flags, the running-best slot groups and
+// the chunk partials, at fixed offsets.  One copy per GPU the library runs
+// on, held until the process ends; every call on that GPU shares it.
+constexpr size_t kScratchChainOff = 0;                        // 65 counter words
+constexpr size_t kScratchFlagsOff = 64 << 10;                 // kChainMaxGrid lines of 128 bytes
+constexpr size_t kScratchBestOff = kScratchFlagsOff + (size_t)kChainMaxGrid * 128;
+constexpr size_t kScratchBestBytes = 1 << 20;                 // B * gamma * 16 slots of 8 bytes
+constexpr size_t kScratchPartOff = kScratchBestOff + kScratchBestBytes;
+constexpr size_t kScratchBytes = 16u << 20;
+constexpr size_t kScratchPartBytes = kScratchBytes - kScratchPartOff;
+static_assert(kScratchPartOff % 256 == 0, "scratch regions stay 256-byte aligned");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+// Device address of `scratch` on each device, taken once per device with that
+// device current (the array's name is not a device address in host code).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+int g_scratch_rc[kMaxDevices] = {};        // 0: not yet taken, 1: ready, -1: failed
+
+// Called from dspark_create with `device` current: the address, and the whole
+// array cleared once (everything the calls expect at zero starts there; each
+// call leaves it zero again).
+void scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_rc[device] != 0) return;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p ||
+      hipMemset(p, 0, kScratchBytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    g_scratch_rc[device] = -1;
+    return;
+  }
+  g_scratch_ptr[device] = p;
+  g_scratch_rc[device] = 1;
+}
+
+void* scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_rc[device] == 1 ? g_scratch_ptr[device] : nullptr;
+}
 
 constexpr int kVersion = 101;
 
@@ -316,6 +362,13 @@ hipKernelNodeParams node_params(KernelNode& n, void** holder) {
   return p;
 }
 
+// Launch kernel nodes one after the other with no events and no graph (the
+// allocation-free path: nothing is created).
+int run_direct(dspark_ctx* c, hipStream_t stream, std::vector<KernelNode>& nodes) {
+  for (auto& n : nodes) DSPARK_HIP(c, launch(n.fn, n.grid, n.block, n.args, stream));
+  return DSPARK_OK;
+}
+
 // Run a chain of kernel nodes on `stream`, through a cached graph when
 // enabled.
 int run_chain(dspark_ctx* c, hipStream_t stream, std::vector<KernelNode>& nodes, int B, int gamma, int V,
@@ -407,29 +460,20 @@ bool use_persist(dspark_ctx* c, int B, int V, int r, int wdtype) {
 // Chained draft eligibility: Markov head, bf16, r in {128, 256}, a batch of
 // three or four 32-row groups (65..128 requests: one request quad, the
 // shared-tile layout), and the kernel's ring shape.
-const void* chain_kernel_for(dspark_ctx* c, int B, int r, int wdtype, int mode) {
-  if (!c->use_chain || wdtype != DSPARK_BF16 || B < 65 || B > 128) return nullptr;
-  const void* fn = draft_chain_kernel(r, mode, c->draft_depth, c->draft_nt);
-  if (!fn) return nullptr;
-  if (c->chain_wg_per_cu < 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, 0) != hipSuccess) {
-      (void)hipGetLastError();
-      nb = 0;
-    }
-    c->chain_wg_per_cu = nb;
-  }
-  if (c->chain_wg_per_cu < 1) return nullptr;
-  if (!c->chain_flags) {
-    const size_t bytes = (size_t)kChainMaxGrid * 128;
-    if (hipMalloc(&c->chain_flags, bytes) != hipSuccess || hipMemset(c->chain_flags, 0, bytes) != hipSuccess) {
-      (void)hipGetLastError();
-      c->chain_flags = nullptr;
-      return nullptr;
-    }
-  }
-  return fn;
+const void* chain_kernel_for(const dspark_ctx* c, int B, int r, int wdtype, int mode) {
+  if (!c->use_chain || c->chain_wg_per_cu < 1 || wdtype != DSPARK_BF16 || B < 65 || B > 128) return nullptr;
+  return draft_chain_kernel(r, mode, c->draft_depth, c->draft_nt);
 }
+
+// Where a draft call keeps its partials, slot groups and chained-draft
+// counters: the context's workspace (grown on demand), or the static
+// scratch (the allocation-free entry point: nothing allocated, kernels
+// launched directly -- no graph, no timing events -- and no whole-draft
+// kernel).
+struct DraftMem {
+  bool fixed = false;
+  unsigned char* base = nullptr;
+};
 
 }  // namespace
 
@@ -438,7 +482,8 @@ const void* chain_kernel_for(dspark_ctx* c, int B, int r, int wdtype, int mode) 
 int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
                 const float* U, int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
                 const int32_t* anchor, const GruArgs* gru, const uint32_t* req_ids, float temperature,
-                uint64_t seed, int32_t* tokens, float* lse, float* ytok, float* states) {
+                uint64_t seed, int32_t* tokens, float* lse, float* ytok, float* states,
+                const DraftMem& mem = DraftMem()) {
   int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
   if (rc) return rc;
   if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
@@ -450,15 +495,37 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   const bool greedy = temperature == 0.0f;
   const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
   const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
-  const bool persist = !gru && use_persist(c, B, V, r, (int)wdtype);
+  const bool persist = !gru && !mem.fixed && use_persist(c, B, V, r, (int)wdtype);
   const int n_vc = persist ? kWavesPerBlock * c->cu_count : pl.n_vc;
   const size_t npos = (size_t)B * n_vc;                // partials of one position
   const size_t npart = npos * gamma;
   const size_t off_pi = align256(npart * sizeof(float4));
-  if ((rc = ensure_ws(c, off_pi + align256(npart * sizeof(int2))))) return rc;
-  if ((rc = ensure_best(c, (size_t)B * gamma * kBestGroups))) return rc;
-  float4* pf = reinterpret_cast<float4*>(c->ws);
-  int2* pi = reinterpret_cast<int2*>(static_cast<char*>(c->ws) + off_pi);
+  const size_t part_bytes = off_pi + align256(npart * sizeof(int2));
+  const size_t n_best = (size_t)B * gamma * kBestGroups;
+  float4* pf;
+  int2* pi;
+  unsigned long long* best;
+  unsigned int* chain_ctr = c->chain;
+  unsigned int* chain_flags = c->chain_flags;
+  if (mem.fixed) {
+    if (part_bytes > kScratchPartBytes || n_best * sizeof(unsigned long long) > kScratchBestBytes)
+      return fail(c, DSPARK_EINVAL,
+                  "this draft needs %zu bytes of partials and %zu of slot groups; the allocation-free draft "
+                  "holds at most %zu and %zu (a %zu-byte scratch per GPU)",
+                  part_bytes, n_best * sizeof(unsigned long long), kScratchPartBytes, kScratchBestBytes,
+                  kScratchBytes);
+    pf = reinterpret_cast<float4*>(mem.base + kScratchPartOff);
+    pi = reinterpret_cast<int2*>(mem.base + kScratchPartOff + off_pi);
+    best = reinterpret_cast<unsigned long long*>(mem.base + kScratchBestOff);
+    chain_ctr = reinterpret_cast<unsigned int*>(mem.base + kScratchChainOff);
+    chain_flags = reinterpret_cast<unsigned int*>(mem.base + kScratchFlagsOff);
+  } else {
+    if ((rc = ensure_ws(c, part_bytes))) return rc;
+    if ((rc = ensure_best(c, n_best))) return rc;
+    pf = reinterpret_cast<float4*>(c->ws);
+    pi = reinterpret_cast<int2*>(static_cast<char*>(c->ws) + off_pi);
+    best = c->best;
+  }
 
   SweepArgs sa;
   memset(&sa, 0, sizeof(sa));
@@ -493,7 +560,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   ca.invT = sa.invT;
   ca.pf = pf;
   ca.pi = pi;
-  ca.best = c->best;
+  ca.best = best;
   ca.tokens = tokens;
   ca.lse = lse;
   ca.ytok = ytok;
@@ -502,7 +569,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   if (persist) {
     // every position in one launch of one workgroup per CU, then the merge
     // (which also resets the launch's barrier counter)
-    sa.best = c->best;
+    sa.best = best;
     sa.bar = c->bar;
     sa.bar_test = c->bar_test;
     ca.bar = c->bar;
@@ -517,17 +584,18 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   if (cfn) {
     // every position in one launch of persistent workgroups, then the merge
     // (which also clears the launch's counters)
-    sa.best = c->best;
-    sa.chain = c->chain;
-    sa.chain_flags = c->chain_flags;
+    sa.best = best;
+    sa.chain = chain_ctr;
+    sa.chain_flags = chain_flags;
     sa.bar_test = c->bar_test;
-    ca.chain = c->chain;
+    ca.chain = chain_ctr;
     const long items = (long)gamma * pl.n_vc;
     const long resident = (long)c->chain_wg_per_cu * c->cu_count;
     const int grid = (int)std::min(std::min(items, resident), (long)kChainMaxGrid);
     std::vector<KernelNode> nodes(2);
     set_node(nodes[0], DSPARK_K_DRAFT_CHAIN, cfn, dim3(grid), dim3(256), sa);
     set_node(nodes[1], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
+    if (mem.fixed) return run_direct(c, stream, nodes);
     return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 16, grid, pl.n_vc);
   }
   const int hs = gru ? 1 : 0;
@@ -560,8 +628,8 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
     sa.k = k;
     sa.pf = pf + (size_t)(k - 1) * npos;
     sa.pi = pi + (size_t)(k - 1) * npos;
-    sa.best = c->best + (size_t)(k - 1) * kBestGroups * B;
-    sa.best_prev = (!gru && k > 1) ? c->best + (size_t)(k - 2) * kBestGroups * B : nullptr;
+    sa.best = best + (size_t)(k - 1) * kBestGroups * B;
+    sa.best_prev = (!gru && k > 1) ? best + (size_t)(k - 2) * kBestGroups * B : nullptr;
     KernelNode n;
     set_node(n, DSPARK_K_DRAFT_SWEEP, kfn, dim3(pl.grid), dim3(256), sa);
     nodes.push_back(n);
@@ -575,6 +643,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   KernelNode n;
   set_node(n, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
   nodes.push_back(n);
+  if (mem.fixed) return run_direct(c, stream, nodes);
   return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 4 * hs, pl.grid, pl.n_vc);
 }
 
@@ -919,6 +988,15 @@ int dspark_create(dspark_ctx** out, int device) {
   }
   c->bar = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(c->dev_err) + 128);
   c->chain = reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(c->dev_err) + 512);
+  if (hipMalloc(&c->chain_flags, (size_t)kChainMaxGrid * 128) != hipSuccess ||
+      hipMemset(c->chain_flags, 0, (size_t)kChainMaxGrid * 128) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(c->dev_err);
+    if (c->chain_flags) (void)hipFree(c->chain_flags);
+    delete c;
+    return DSPARK_EHIP;
+  }
+  scratch_setup(device);
   // chained draft kernel (every position in one launch, 65..128 requests):
   // "0" switches it off (per-position sweeps)
   const char* ch = getenv("DSPARK_CHAIN");
@@ -986,6 +1064,16 @@ int dspark_create(dspark_ctx** out, int device) {
       }
     }
     if (ok) memcpy(c->verify_win, tmp, sizeof(tmp));
+  }
+  // resident workgroups per CU of the chained draft (its grid), asked once
+  {
+    int nb = 0;
+    const void* fn = draft_chain_kernel(256, kModeDraftSample, c->draft_depth, c->draft_nt);
+    if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      nb = 0;
+    }
+    c->chain_wg_per_cu = nb;
   }
   *out = c;
   return DSPARK_OK;
@@ -1078,6 +1166,20 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
   if (!anchor) return fail(c, DSPARK_EINVAL, "null pointer argument");
   return draft_chain(c, stream, B, gamma, V, r, wdtype, U, u_stride_b, u_stride_k, W1, W2, anchor, nullptr,
                      req_ids, temperature, seed, tokens, lse, ytok, nullptr);
+}
+
+int dspark_draft_markov_static(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r,
+                               dspark_dtype wdtype, const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                               const void* W1, const void* W2, const int32_t* anchor, const uint32_t* req_ids,
+                               float temperature, uint64_t seed, int32_t* tokens, float* lse, float* ytok) {
+  if (!c) return DSPARK_EINVAL;
+  if (!anchor) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  DraftMem mem;
+  mem.fixed = true;
+  mem.base = static_cast<unsigned char*>(scratch_ptr(c->device));
+  if (!mem.base) return fail(c, DSPARK_EHIP, "the static scratch of device %d has no device address", c->device);
+  return draft_chain(c, stream, B, gamma, V, r, wdtype, U, u_stride_b, u_stride_k, W1, W2, anchor, nullptr,
+                     req_ids, temperature, seed, tokens, lse, ytok, nullptr, mem);
 }
 
 int dspark_draft_rnn(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r, dspark_dtype wdtype,
