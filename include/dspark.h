@@ -205,8 +205,10 @@ int dspark_draft_markov(dspark_ctx* ctx, hipStream_t stream,
  * device when a context is created there; the call allocates nothing, creates
  * no event or graph and launches its kernels directly (the context's timing
  * and graph switches are ignored).  Limits: B * n_chunks * gamma * 24 bytes
- * of partials within 15,040 KiB (the headline shape B = 128, gamma = 7,
- * V = 151936 needs 10,752 KiB; gamma <= 9 at B = 128) and B * gamma <= 8192;
+ * of partials within 15,040 KiB (on a 256-CU part the chained draft cuts
+ * the vocabulary into 256 chunks: the headline shape B = 128, gamma = 7,
+ * V = 151936 needs 5,376 KiB, and gamma <= 19 fits at B = 128) and
+ * B * gamma <= 8192;
  * a larger shape returns DSPARK_EINVAL with the sizes in the message.
  * Every call on a GPU, from any context, shares that GPU's array: calls that
  * overlap on one GPU (other streams, other threads) race and must be

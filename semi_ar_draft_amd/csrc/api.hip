@@ -119,6 +119,18 @@ struct dspark_ctx {
   unsigned int* chain = nullptr;  // 65 words: tickets, then per-position counters from word 32
   unsigned int* chain_flags = nullptr;   // one 128-byte line per workgroup (kChainMaxGrid)
   int chain_wg_per_cu = -1;       // resident workgroups per CU (-1 = not yet asked)
+  // shape of the chained draft: waves per workgroup, request rows per wave
+  // (a request group is their product; two groups of 64 would interleave
+  // their chains), ring steps loaded ahead, and vocabulary chunks per
+  // position (0: one per resident workgroup).  Measured draft calls
+  // (sampling, B = 128, gamma = 7, V = 151936): 8 waves x 16 rows, two steps
+  // ahead, one 8-wave workgroup and one chunk per CU 207-209 us; three or
+  // four steps ahead 215-217; 512 or 384 chunks 263-284 (a workgroup's
+  // second item of a position repeats the set-up); two 4-wave workgroups
+  // per CU with 32 rows per wave 216-224 (the two workgroups of a CU finish
+  // their items several us apart); two groups of 64 requests with 16 rows
+  // per wave 250 (W2 streamed twice per position).
+  int chain_waves = 8, chain_rows = 16, chain_depth = 2, chain_chunks = 0;
   // shared-tile sweeps: 16-wide tiles per ring step and steps loaded ahead
   int draft_nt = 2, draft_depth = 1;
   // the GRU head's sweep holds its state as hi + lo fragments, so its
@@ -462,7 +474,7 @@ bool use_persist(dspark_ctx* c, int B, int V, int r, int wdtype) {
 // shared-tile layout), and the kernel's ring shape.
 const void* chain_kernel_for(const dspark_ctx* c, int B, int r, int wdtype, int mode) {
   if (!c->use_chain || c->chain_wg_per_cu < 1 || wdtype != DSPARK_BF16 || B < 65 || B > 128) return nullptr;
-  return draft_chain_kernel(r, mode, c->draft_depth, c->draft_nt);
+  return draft_chain_kernel(r, mode, c->chain_depth, 2, c->chain_rows, c->chain_waves);
 }
 
 // Where a draft call keeps its partials, slot groups and chained-draft
@@ -496,7 +508,10 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
   const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
   const bool persist = !gru && !mem.fixed && use_persist(c, B, V, r, (int)wdtype);
-  const int n_vc = persist ? kWavesPerBlock * c->cu_count : pl.n_vc;
+  const void* cfn = (gru || persist) ? nullptr : chain_kernel_for(c, B, r, (int)wdtype, mode);
+  const int chain_vc = c->chain_chunks > 0 ? c->chain_chunks : c->chain_wg_per_cu * c->cu_count;
+  const int n_vc = persist ? kWavesPerBlock * c->cu_count
+                           : cfn ? std::max(1, std::min(chain_vc, (pl.n_tiles + 1) / 2)) : pl.n_vc;
   const size_t npos = (size_t)B * n_vc;                // partials of one position
   const size_t npart = npos * gamma;
   const size_t off_pi = align256(npart * sizeof(float4));
@@ -580,7 +595,6 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
     if (rc) return rc;
     return klaunch(c, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), &ca, stream);
   }
-  const void* cfn = gru ? nullptr : chain_kernel_for(c, B, r, (int)wdtype, mode);
   if (cfn) {
     // every position in one launch of persistent workgroups, then the merge
     // (which also clears the launch's counters)
@@ -589,14 +603,15 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
     sa.chain_flags = chain_flags;
     sa.bar_test = c->bar_test;
     ca.chain = chain_ctr;
-    const long items = (long)gamma * pl.n_vc;
+    const int group_rows = c->chain_waves * c->chain_rows;
+    const long items = (long)gamma * n_vc * ((B + group_rows - 1) / group_rows);
     const long resident = (long)c->chain_wg_per_cu * c->cu_count;
     const int grid = (int)std::min(std::min(items, resident), (long)kChainMaxGrid);
     std::vector<KernelNode> nodes(2);
-    set_node(nodes[0], DSPARK_K_DRAFT_CHAIN, cfn, dim3(grid), dim3(256), sa);
+    set_node(nodes[0], DSPARK_K_DRAFT_CHAIN, cfn, dim3(grid), dim3(64 * c->chain_waves), sa);
     set_node(nodes[1], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
     if (mem.fixed) return run_direct(c, stream, nodes);
-    return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 16, grid, pl.n_vc);
+    return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 16, grid, n_vc);
   }
   const int hs = gru ? 1 : 0;
   const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, hs ? c->gru_depth : c->draft_depth,
@@ -1001,6 +1016,18 @@ int dspark_create(dspark_ctx** out, int device) {
   // "0" switches it off (per-position sweeps)
   const char* ch = getenv("DSPARK_CHAIN");
   if (ch && ch[0] == '0' && ch[1] == 0) c->use_chain = false;
+  // its shape: "<waves>,<rows per wave>,<depth>,<chunks>" (e.g. 8,16,3,256)
+  const char* cs = getenv("DSPARK_CHAIN_SHAPE");
+  if (cs) {
+    int wv = 0, rw = 0, dp = 0, ck = 0;
+    if (sscanf(cs, "%d,%d,%d,%d", &wv, &rw, &dp, &ck) == 4 && draft_chain_kernel(256, kModeDraftSample, dp, 2, rw, wv) &&
+        ck >= 0 && ck <= 4096) {
+      c->chain_waves = wv;
+      c->chain_rows = rw;
+      c->chain_depth = dp;
+      c->chain_chunks = ck;
+    }
+  }
   // whole-draft kernel: "0" never, "1" small batches (default), "2" every
   // eligible batch (up to 128 requests)
   const char* pk = getenv("DSPARK_PERSIST");
@@ -1068,8 +1095,8 @@ int dspark_create(dspark_ctx** out, int device) {
   // resident workgroups per CU of the chained draft (its grid), asked once
   {
     int nb = 0;
-    const void* fn = draft_chain_kernel(256, kModeDraftSample, c->draft_depth, c->draft_nt);
-    if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, 0) != hipSuccess) {
+    const void* fn = draft_chain_kernel(256, kModeDraftSample, c->chain_depth, 2, c->chain_rows, c->chain_waves);
+    if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * c->chain_waves, 0) != hipSuccess) {
       (void)hipGetLastError();
       nb = 0;
     }

@@ -208,10 +208,13 @@ const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs)
 constexpr int kPersistTiles = 10;
 const void* draft_persist_kernel(int mode);
 // Chained draft (Markov head, bf16, B <= 128, r in {128, 256}): every
-// position in one launch of persistent workgroups claiming (position, chunk)
-// items in order; ring shapes (depth, nt) in {(1, 2), (2, 1)} for r = 256,
-// (1, 2) for r = 128.  nullptr otherwise.
-const void* draft_chain_kernel(int r, int mode, int depth, int nt);
+// position in one launch of persistent workgroups of `waves` waves claiming
+// (position, request group, chunk) items in order; a group is waves x
+// rows_per_wave requests.  Shapes (waves, rows_per_wave, depth, nt): (4, 32,
+// 1, 2) and (4, 32, 2, 1) for r = 256, (4, 32, 1, 2) for r = 128; (4, 16, 1,
+// 2) for both; (8, 16, 2..4, 2) for r = 256, (8, 16, 2, 2) for r = 128.
+// nullptr otherwise.
+const void* draft_chain_kernel(int r, int mode, int depth, int nt, int rows_per_wave, int waves);
 constexpr int kChainMaxGrid = 2048;   // workgroups of a chained draft launch (release flags)
 const void* combine_draft_kernel();
 const void* combine_resid_kernel();

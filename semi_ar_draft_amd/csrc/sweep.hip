@@ -286,28 +286,29 @@ __device__ __forceinline__ int xcd_logical_block(int p, int n) {
 // from): 0 = the Markov head's W1 row of the previous token; 1 = the GRU
 // head's fp32 state s_{k-1} of the request (hstate [gamma][B][r]), split
 // into hi + lo bf16 fragments for bf16 weights.
-template <typename WT, int R, int MODE, int HS = 0>
+template <typename WT, int R, int MODE, int HS = 0, int NBW = 2>
 struct WaveRows {
   using F = Frag<WT, R>;
   using FragT = typename F::T;
   static constexpr int NS = F::NS;
   static constexpr bool kLo = HS == 1 && F::kSplit;
-  bool ok[2];
-  int rows[2];
-  int64_t uoff[2], toff[2];
-  uint32_t klo[2], khi[2];
-  float ld[2], lt[2];
-  FragT H[2][NS];
-  FragT Hlo[2][kLo ? NS : 1];
+  static constexpr int kRows = 16 * NBW;            // request rows of the wave
+  bool ok[NBW];
+  int rows[NBW];
+  int64_t uoff[NBW], toff[NBW];
+  uint32_t klo[NBW], khi[NBW];
+  float ld[NBW], lt[NBW];
+  FragT H[NBW][NS];
+  FragT Hlo[NBW][kLo ? NS : 1];
 
-  int kk[2];
+  int kk[NBW];
 
   // Row identities and stream offsets (the residual reads its position).
   __device__ __forceinline__ void setup_rows(const SweepArgs& a, int rg, int j) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int b = rg * kRowsPerWave + nb * 16 + j;
-      bool v = rg < a.n_rg && b < a.B;
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int b = rg * kRows + nb * 16 + j;
+      bool v = b < a.B;
       int k = a.k;
       if constexpr (MODE == kModeResidual) {
         k = v ? a.resid_k[b] : 0;
@@ -334,12 +335,14 @@ struct WaveRows {
   __device__ __forceinline__ void setup_rest(const SweepArgs& a, int q) {
     // loads that do not depend on the previous token go out first (the
     // error-flag atomic below would otherwise keep them behind the chain)
-    uint32_t req[2] = {0u, 0u};
-    int given[2] = {0, 0};                               // anchor, or the drafted previous token
+    uint32_t req[NBW];
+    int given[NBW];                                      // anchor, or the drafted previous token
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBW; ++nb) {
       const int b = rows[nb];
       const int k = kk[nb];
+      req[nb] = 0u;
+      given[nb] = 0;
       ld[nb] = lt[nb] = 0.0f;
       if (ok[nb]) {
         if constexpr (MODE == kModeDraftSample || MODE == kModeResidual) req[nb] = a.req ? a.req[b] : (uint32_t)b;
@@ -359,10 +362,12 @@ struct WaveRows {
         }
       }
     }
-    unsigned long long pb[2] = {0ull, 0ull};
+    unsigned long long pb[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) pb[nb] = 0ull;
     if (HS == 0 && MODE != kModeResidual && MODE != kModeAlpha && a.best_prev) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NBW; ++nb) {
         if (ok[nb]) {
 #pragma unroll
           for (int i = 0; i < kBestGroups / 4; ++i) {
@@ -380,7 +385,7 @@ struct WaveRows {
       }
     }
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBW; ++nb) {
       const int b = rows[nb];
       const int k = kk[nb];
       int prev = 0;
@@ -463,29 +468,29 @@ struct WaveRows {
   }
 
   // z = U + bias of one tile for both blocks (U initialises the accumulators).
-  __device__ __forceinline__ void mma_tile(f32x4_t (&acc)[2], const FragT (&A)[NS], const float4 (&uu)[2]) const {
+  __device__ __forceinline__ void mma_tile(f32x4_t (&acc)[NBW], const FragT (&A)[NS], const float4 (&uu)[NBW]) const {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[nb] = f32x4_t{uu[nb].x, uu[nb].y, uu[nb].z, uu[nb].w};
+    for (int nb = 0; nb < NBW; ++nb) acc[nb] = f32x4_t{uu[nb].x, uu[nb].y, uu[nb].z, uu[nb].w};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[nb] = F::mma(A[s], H[nb][s], acc[nb]);
+      for (int nb = 0; nb < NBW; ++nb) acc[nb] = F::mma(A[s], H[nb][s], acc[nb]);
     }
     if constexpr (kLo) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[nb] = F::mma(A[s], Hlo[nb][s], acc[nb]);
+        for (int nb = 0; nb < NBW; ++nb) acc[nb] = F::mma(A[s], Hlo[nb][s], acc[nb]);
       }
     }
   }
 
   // Draft modes: fold NTL consecutive tiles (acc[h][nb], tile t + h).
   template <int NTL>
-  __device__ __forceinline__ void fold(const SweepArgs& a, LaneState (&st)[2], const f32x4_t (&acc)[NTL][2], int t,
+  __device__ __forceinline__ void fold(const SweepArgs& a, LaneState (&st)[NBW], const f32x4_t (&acc)[NTL][NBW], int t,
                                        int q) const {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBW; ++nb) {
       f32x4_t z[NTL];
 #pragma unroll
       for (int h = 0; h < NTL; ++h) z[h] = acc[h][nb];
@@ -494,24 +499,24 @@ struct WaveRows {
   }
 
   // One tile: z = U + bias, then fold.
-  __device__ __forceinline__ void compute(const SweepArgs& a, LaneState (&st)[2], int t, int q,
-                                          const FragT (&A)[NS], const float4 (&uu)[2],
-                                          const float4 (&tt)[2]) const {
-    f32x4_t acc[1][2];
+  __device__ __forceinline__ void compute(const SweepArgs& a, LaneState (&st)[NBW], int t, int q,
+                                          const FragT (&A)[NS], const float4 (&uu)[NBW],
+                                          const float4 (&tt)[NBW]) const {
+    f32x4_t acc[1][NBW];
     mma_tile(acc[0], A, uu);
     if constexpr (MODE == kModeDraftGreedy || MODE == kModeDraftSample) {
       fold<1>(a, st, acc, t, q);
     } else {
       const int vb = t * kTileV + 4 * q;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NBW; ++nb)
         epilogue<MODE>(st[nb], acc[0][nb], tt[nb], vb, klo[nb], khi[nb], a.invT, ld[nb], lt[nb]);
     }
   }
 
-  __device__ __forceinline__ void finish(const SweepArgs& a, LaneState (&st)[2], int q, int vc) const {
+  __device__ __forceinline__ void finish(const SweepArgs& a, LaneState (&st)[NBW], int q, int vc) const {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBW; ++nb) {
       if constexpr (MODE == kModeDraftGreedy || MODE == kModeDraftSample)
         resolve_draft<MODE>(st[nb], klo[nb], khi[nb], a.s2);
       else if constexpr (MODE == kModeResidual)
@@ -874,42 +879,53 @@ __global__ __launch_bounds__(256) void sweep_shared_impl(const SweepArgs a) {
 // only slow it down).  The wait is bounded all the same (it raises the
 // barrier error bit and lets the item run on).
 //
+// The requests form one or two groups of 64 or 128 rows (NBW = 1 or 2
+// 16-row blocks per wave); each group is its own chain of positions, and
+// tickets interleave the groups (position-major), so while one group waits
+// for its previous position the other group's items keep the device
+// streaming.
+//
 // Counters (zero at launch; the draft combine clears them): chain[0] the
-// ticket counter, chain[32 + k] the finished items of position k (another
-// cache line).  The workgroup whose item completes position k releases the
-// waiting workgroups by writing k into each one's own flag word (flags[32 b],
-// one 128-byte line per workgroup): hundreds of workgroups polling one
-// counter slowed the streaming of the ones still working (straggling items
-// took twice the median time).  The item that completes the last position
-// writes 0 into every flag, so each launch (a graph replay too) starts from
-// zeroed flags.
+// ticket counter, chain[32 + kg] the finished items of (position, group) kg
+// (another cache line).  The workgroup whose item completes (k, g) releases
+// the waiting workgroups by writing k into word g of each one's own flag line
+// (flags[32 b + g], one 128-byte line per workgroup): hundreds of workgroups
+// polling one counter slowed the streaming of the ones still working
+// (straggling items took twice the median time).  The item that completes a
+// group's last position writes 0 into that group's flags, so each launch (a
+// graph replay too) starts from zeroed flags.
 constexpr unsigned kChainSpinLimit = 1u << 20;
 
-template <int R, int MODE, int D, int NT>
-__global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
-  using WR = WaveRows<uint16_t, R, MODE, 0>;
+template <int R, int MODE, int D, int NT, int NBW, int NW>
+__global__ __launch_bounds__(64 * NW) void draft_chain_impl(const SweepArgs a0) {
+  using WR = WaveRows<uint16_t, R, MODE, 0, NBW>;
   using FragT = typename WR::FragT;
   constexpr int NS = WR::NS;
   constexpr int NB = D + 1;
+  constexpr int kRowsW = WR::kRows;                     // request rows per wave
+  constexpr int kRowsItem = NW * kRowsW;    // request rows per item (one group)
   constexpr int kRowBytes = R * 2;
   constexpr int kCPR = kRowBytes / 16;
   constexpr int kTileBytes = kTileV * kRowBytes;
   constexpr int kW2Bytes = NT * kTileBytes;
-  constexpr int kW2Inst = kW2Bytes / (kWavesPerBlock * 1024);
+  constexpr int kW2Inst = kW2Bytes / (NW * 1024);
   constexpr int kFPR = 4 * NT;
   constexpr int kRPI = 16 / NT;
   constexpr int kSwzShift = 2 / NT;
-  constexpr int kUInst = kRowsPerWave / kRPI;
-  constexpr int kWaveRowBytes = kRowsPerWave * kFPR * 16;
+  constexpr int kUInst = kRowsW / kRPI;
+  constexpr int kWaveRowBytes = kRowsW * kFPR * 16;
   constexpr int kG = kW2Inst + kUInst;
   constexpr int kUOff = kW2Bytes;
-  constexpr int kSlotBytes = kW2Bytes + kWavesPerBlock * kWaveRowBytes;
+  constexpr int kSlotBytes = kW2Bytes + NW * kWaveRowBytes;
   static_assert(NT == 1 || NT == 2, "steps of one or two tiles");
+  static_assert(NBW == 1 || NBW == 2, "one or two 16-row blocks per wave");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(kW2Bytes % (NW * 1024) == 0, "W2 step must split into 1 KB loads per wave");
   static_assert(MODE == kModeDraftGreedy || MODE == kModeDraftSample, "draft modes only");
   static_assert(D >= 1 && (D - 1) * kG < 64, "ring depth");
   __shared__ __attribute__((aligned(16))) unsigned char ring[NB * kSlotBytes];
   // the claimed ticket is handed to every wave through the last word of the
-  // ring (one more LDS word would cost the second workgroup per CU): that
+  // ring (one more LDS word could cost a resident workgroup per CU): that
   // word is first overwritten by the loop's first load into the last slot,
   // which follows a barrier every wave reaches after reading it
   int* const s_item = reinterpret_cast<int*>(ring + NB * kSlotBytes - 4);
@@ -918,8 +934,9 @@ __global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
   const int wid = threadIdx.x >> 6;
   const int q = lane >> 4;
   const int j = lane & 15;
-  const int per_pos = a0.n_vc;
-  const int total = per_pos * a0.gamma;
+  const int n_grp = (a0.B + kRowsItem - 1) / kRowsItem;   // request groups, independent chains
+  const int per_kg = a0.n_vc;                               // items of one (position, group)
+  const int total = per_kg * n_grp * a0.gamma;
   const int n_steps = (a0.n_tiles + NT - 1) / NT;
   const unsigned char* W2b = static_cast<const unsigned char*>(a0.W2);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8_t*)ring;
@@ -931,8 +948,10 @@ __global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
   __syncthreads();
   int item = *s_item;
   while (item < total) {                                  // uniform over the block
-    const int k = item / per_pos + 1;
-    const int vc = item - (k - 1) * per_pos;
+    const int kg = item / per_kg;                         // (position, group), position-major
+    const int k = kg / n_grp + 1;
+    const int g = kg - (k - 1) * n_grp;
+    const int vc = item - kg * per_kg;
     SweepArgs a = a0;
     a.k = k;
     a.pf = a0.pf + (size_t)(k - 1) * a0.B * a0.n_vc;
@@ -940,11 +959,14 @@ __global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
     a.best = a0.best + (size_t)(k - 1) * kBestGroups * a0.B;
     a.best_prev = k > 1 ? a0.best + (size_t)(k - 2) * kBestGroups * a0.B : nullptr;
     WR w;
-    w.setup_rows(a, wid, j);
-    const bool wave_active = __any(w.ok[0] || w.ok[1]);
-    LaneState st[2];
-    lane_init(st[0]);
-    lane_init(st[1]);
+    w.setup_rows(a, g * NW + wid, j);
+    bool any_ok = false;
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) any_ok = any_ok || w.ok[nb];
+    const bool wave_active = __any(any_ok);
+    LaneState st[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) lane_init(st[nb]);
     const int t0 = min(NT * (int)((int64_t)n_steps * vc / a.n_vc), a.n_tiles);
     const int t1 = min(NT * (int)((int64_t)n_steps * (vc + 1) / a.n_vc), a.n_tiles);
 
@@ -972,22 +994,22 @@ __global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
 #pragma unroll
       for (int m = 0; m < kUInst; ++m) dma16(a.U + uoff_d[m] + vcol[m], base + u_lds + m * 1024);
     };
-    auto load_tile = [&](int h, const unsigned char* sl, FragT (&A)[NS], float4 (&uu)[2]) {
+    auto load_tile = [&](int h, const unsigned char* sl, FragT (&A)[NS], float4 (&uu)[NBW]) {
       const unsigned char* row = sl + (h * kTileV + j) * kRowBytes;
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) A[s2] = *reinterpret_cast<const FragT*>(row + (((4 * s2 + q) ^ j) * 16));
       const int col = (4 * h + q) ^ ((j >> kSwzShift) & (kFPR - 1));
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NBW; ++nb) {
         const int off = wid * kWaveRowBytes + ((nb * 16 + j) * kFPR + col) * 16;
         uu[nb] = *reinterpret_cast<const float4*>(sl + kUOff + off);
       }
     };
     auto compute = [&](int t, const unsigned char* sl) {
       if constexpr (NT == 2) {
-        f32x4_t acc[NT][2];
+        f32x4_t acc[NT][NBW];
         FragT A[NS];
-        float4 uu[2];
+        float4 uu[NBW];
         load_tile(0, sl, A, uu);
         w.mma_tile(acc[0], A, uu);
         if (t + 1 < t1) {                                  // uniform over the block
@@ -995,13 +1017,15 @@ __global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
           w.mma_tile(acc[1], A, uu);
           w.template fold<2>(a, st, acc, t, q);
         } else {
-          const f32x4_t acc1[1][2] = {{acc[0][0], acc[0][1]}};
+          f32x4_t acc1[1][NBW];
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) acc1[0][nb] = acc[0][nb];
           w.template fold<1>(a, st, acc1, t, q);
         }
       } else {
-        f32x4_t acc[1][2];
+        f32x4_t acc[1][NBW];
         FragT A[NS];
-        float4 uu[2];
+        float4 uu[NBW];
         load_tile(0, sl, A, uu);
         w.mma_tile(acc[0], A, uu);
         w.template fold<1>(a, st, acc, t, q);
@@ -1012,13 +1036,13 @@ __global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
 #pragma unroll
       for (int p = 0; p < D; ++p) issue(t0 + p * NT, p);
     }
-    // every item of position k - 1 has published its winners
+    // every item of (k - 1, g) has published its winners
     if (k > 1) {
       if (threadIdx.x == 0) {
         // the host's failure injection waits for a value nobody writes
         const unsigned want = a0.bar_test ? 0x80u : (unsigned)(k - 1);
         const unsigned limit = a0.bar_test ? 64u : kChainSpinLimit;
-        const unsigned* flag = a0.chain_flags + 32 * blockIdx.x;
+        const unsigned* flag = a0.chain_flags + 32 * blockIdx.x + g;
         unsigned spins = 0;
         while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
           __builtin_amdgcn_s_sleep(2);
@@ -1050,14 +1074,15 @@ __global__ __launch_bounds__(256) void draft_chain_impl(const SweepArgs a0) {
     __syncthreads();                                       // every wave's; no wave reads the ring any more
     if (wid == 0) {
       unsigned before = 0;
-      if (lane == 0) before = __hip_atomic_fetch_add(a0.chain + 32 + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        before = __hip_atomic_fetch_add(a0.chain + 32 + kg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       before = __shfl(before, 0, 64);
-      if (before == (unsigned)per_pos - 1u) {
-        // the last item of position k: release every workgroup (after the
-        // last position: clear the flags for the next launch)
+      if (before == (unsigned)per_kg - 1u) {
+        // the last item of (k, g): release every workgroup's wait on group g
+        // (after the last position: clear the group's flags for the next launch)
         const unsigned v = k < a0.gamma ? (unsigned)k : 0u;
         for (int b = lane; b < (int)gridDim.x; b += 64)
-          __hip_atomic_store(a0.chain_flags + 32 * b, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(a0.chain_flags + 32 * b + g, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (lane == 0)
         *s_item = (int)__hip_atomic_fetch_add(a0.chain, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1366,8 +1391,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_draft_impl(const Comb
     a.ytok[o] = a.greedy ? p.key : p.zb;   // sampling partials carry y itself
   }
   if (a.bar && b == 0 && k == 1 && threadIdx.x == 0) *a.bar = 0u;   // grid barrier of the whole-draft kernel
-  if (a.chain && b == 0 && k == 1 && threadIdx.x <= a.gamma)   // chained draft counters
-    a.chain[threadIdx.x == 0 ? 0 : 32 + threadIdx.x] = 0u;
+  if (a.chain && b == 0 && k == 1 && threadIdx.x < 97)   // chained draft counters
+    a.chain[threadIdx.x == 0 ? 0 : 31 + threadIdx.x] = 0u;
   if (a.best && threadIdx.x < kBestGroups) {
     unsigned long long* slot = a.best + ((int64_t)(k - 1) * kBestGroups + threadIdx.x) * a.B + b;
     __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1504,15 +1529,27 @@ const void* sweep_kernel(int wdtype, int r, int mode, int depth, int nt, int hs)
   return nullptr;
 }
 
-const void* draft_chain_kernel(int r, int mode, int depth, int nt) {
+template <int R, int D, int NT, int NBW, int NW>
+const void* chain_for(int mode) {
+  return mode == kModeDraftGreedy ? (const void*)&draft_chain_impl<R, kModeDraftGreedy, D, NT, NBW, NW>
+                                  : (const void*)&draft_chain_impl<R, kModeDraftSample, D, NT, NBW, NW>;
+}
+
+const void* draft_chain_kernel(int r, int mode, int depth, int nt, int rows_per_wave, int waves) {
   if (mode != kModeDraftGreedy && mode != kModeDraftSample) return nullptr;
-  const bool g = mode == kModeDraftGreedy;
-  if (r == 256 && nt == 2 && depth == 1)
-    return g ? (const void*)&draft_chain_impl<256, kModeDraftGreedy, 1, 2> : (const void*)&draft_chain_impl<256, kModeDraftSample, 1, 2>;
-  if (r == 256 && nt == 1 && depth == 2)
-    return g ? (const void*)&draft_chain_impl<256, kModeDraftGreedy, 2, 1> : (const void*)&draft_chain_impl<256, kModeDraftSample, 2, 1>;
-  if (r == 128 && nt == 2 && depth == 1)
-    return g ? (const void*)&draft_chain_impl<128, kModeDraftGreedy, 1, 2> : (const void*)&draft_chain_impl<128, kModeDraftSample, 1, 2>;
+  if (waves == 4 && rows_per_wave == 32) {
+    if (r == 256 && nt == 2 && depth == 1) return chain_for<256, 1, 2, 2, 4>(mode);
+    if (r == 256 && nt == 1 && depth == 2) return chain_for<256, 2, 1, 2, 4>(mode);
+    if (r == 128 && nt == 2 && depth == 1) return chain_for<128, 1, 2, 2, 4>(mode);
+  } else if (waves == 4 && rows_per_wave == 16) {
+    if (r == 256 && nt == 2 && depth == 1) return chain_for<256, 1, 2, 1, 4>(mode);
+    if (r == 128 && nt == 2 && depth == 1) return chain_for<128, 1, 2, 1, 4>(mode);
+  } else if (waves == 8 && rows_per_wave == 16) {
+    if (r == 256 && nt == 2 && depth == 2) return chain_for<256, 2, 2, 1, 8>(mode);
+    if (r == 256 && nt == 2 && depth == 3) return chain_for<256, 3, 2, 1, 8>(mode);
+    if (r == 256 && nt == 2 && depth == 4) return chain_for<256, 4, 2, 1, 8>(mode);
+    if (r == 128 && nt == 2 && depth == 2) return chain_for<128, 2, 2, 1, 8>(mode);
+  }
   return nullptr;
 }
 

@@ -2,10 +2,12 @@
 defaults under concurrent work.
 
 The chained draft is the default for bf16 weights, r in {128, 256} and
-65..128 requests.  Checked here: one draft-chain launch per call; results
-bit-identical to the per-position sweeps (tokens, y at the token, and the
-log-normalisers, which merge the same per-chunk partials in the same order);
-against the oracle at gamma = 1 (no wait), a long draft and r = 128; while a
+65..128 requests.  Checked here: one draft-chain launch per call; the same
+tokens as the per-position sweeps, with y at the token and the
+log-normalisers equal to rounding (one vocabulary chunk per resident
+workgroup instead of the sweeps' finer chunks), and bit-identical to them
+when given the sweeps' chunks and layout; against the oracle at gamma = 1
+(no wait), a long draft and r = 128; while a
 long kernel runs on a second stream (its workgroups then cannot all be
 resident, and items are claimed by whichever run); with every wait made to
 give up from the host (the kernel still ends and the error is reported).
@@ -73,6 +75,10 @@ def launches(ctx, d, T, seed, G):
 
 @pytest.mark.parametrize("T", [0.0, 1.0])
 def test_chain_is_one_launch_and_equals_the_sweeps(ctx, sweeps, T):
+    """The chained draft cuts the vocabulary into one chunk per resident
+    workgroup, the sweeps into more: the same tokens, and y at the token and
+    the log-normalisers to rounding (the same sums in another grouping); a
+    chained draft whose chunks are the sweeps' is bit-identical."""
     wl = synth.WORKLOADS["sample"].with_(B=128, gamma=7, V=40960, conf=False, temperature=T)
     d = to_dev(synth.make_inputs(wl, seed=71))
     print(f"chain vs sweeps T={T}", flush=True)
@@ -80,8 +86,24 @@ def test_chain_is_one_launch_and_equals_the_sweeps(ctx, sweeps, T):
     assert launches(sweeps, d, T, 5, wl.gamma) == (0, wl.gamma)
     a = draft(ctx, d, T, 5, wl.gamma)
     b = draft(sweeps, d, T, 5, wl.gamma)
-    for x, y in zip(a, b):
+    assert np.array_equal(a[0], b[0])
+    assert np.allclose(a[1], b[1], rtol=1e-6, atol=1e-6) and np.allclose(a[2], b[2], rtol=1e-6, atol=1e-6)
+    n_vc = sweeps_chunks(wl)
+    same = make_ctx(DSPARK_CHAIN_SHAPE=f"4,32,1,{n_vc}")
+    try:
+        c = draft(same, d, T, 5, wl.gamma)
+    finally:
+        same.close()
+    for x, y in zip(c, b):
         assert np.array_equal(x, y)
+
+
+def sweeps_chunks(wl):
+    """Vocabulary chunks of the per-position shared-tile sweep at this shape
+    (the library aims at eight waves per CU: 2048 waves / (4 waves x one
+    request quad), at most a chunk per four tiles)."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    return min(8 * cu // 4, (wl.V // 16) // 4)
 
 
 CASES = [

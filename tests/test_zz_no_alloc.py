@@ -73,7 +73,7 @@ def test_static_draft_matches_the_allocating_entry_point():
 
 
 def test_static_draft_refuses_a_shape_beyond_its_scratch():
-    wl = synth.WORKLOADS["sample"].with_(B=128, gamma=16, V=151936, conf=False)
+    wl = synth.WORKLOADS["sample"].with_(B=128, gamma=32, V=151936, conf=False)
     ctx = dk.Context(0)
     try:
         U = torch.zeros((wl.B, wl.gamma, wl.V), device="cuda")
