@@ -347,8 +347,19 @@ def main():
     A = A_log[:args.steps].cpu()
     value = positions / (elapsed_ms / 1e3)
     needed_rows = float(torch.where(A < Ks, A + 1, Ks + 1).sum().item()) / args.steps
-    read_rows = float((torch.clamp(Ks + 1, max=2) + torch.where((A >= 2) & (Ks >= 2), Ks - 1,
-                                                                  torch.zeros_like(Ks))).sum().item()) / args.steps
+    # rows the verify windows read: the library's windows (rows 1-2, 3, then
+    # the rest, or DSPARK_VERIFY_WINDOWS) -- a window reads rows lo..min(hi,
+    # K_b + 1) of the requests that kept every row before it
+    ends = [int(x) for x in os.environ.get("DSPARK_VERIFY_WINDOWS", "2,3").split(",") if x]
+    ends = [e for e in ends if e < G + 1] + [G + 1]
+    read = torch.zeros_like(Ks)
+    lo = 1
+    for hi in ends:
+        pend = (A >= lo - 1) & (Ks >= lo - 1)
+        n = torch.clamp(torch.minimum(torch.full_like(Ks, hi), Ks + 1) - lo + 1, min=0)
+        read += torch.where(pend, n, torch.zeros_like(n))
+        lo = hi + 1
+    read_rows = float(read.sum().item()) / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, "
           f"{value / 1e6:.3f} M positions/s", file=sys.stderr, flush=True)
 

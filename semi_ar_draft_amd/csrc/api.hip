@@ -148,11 +148,25 @@ struct dspark_ctx {
   // passes (allocated zeroed at the first fit)
   unsigned long long* sts_buf = nullptr;
   // verify: last target row of each window but the final one (window k covers
-  // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list
-  int verify_win[8] = {3, 0, 0, 0, 0, 0, 0, 0};
+  // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list.  Rows 1-2, 3,
+  // then 4..K_b+1: measured steps on the headline batch (gamma 7, mean
+  // acceptance 0.62) 361 us, against 364 for {1-2, 3-4, 5-8}, 367 for
+  // {1, 2-3, 4-8} and 368 for {1-3, 4-8} (each window costs a row pass and
+  // a decision launch)
+  int verify_win[8] = {2, 3, 0, 0, 0, 0, 0, 0};
   // later windows walk a list of the pending requests (else one workgroup per
   // row chunk of every request, most of which find it decided)
   bool verify_list = true;
+  // each window's accept decisions taken inside its row pass by the
+  // request's last task, instead of a separate decision launch per window
+  // (DSPARK_VERIFY_FUSED=1).  Measured slower on the headline batch: the
+  // row pass went from 31.9 to 49.0 us per window (each 32 KB task holds its
+  // workgroup for the atomic round trip of its count) against the 4.4 us
+  // decision launch it saves.  Its per-request task counters and
+  // decided-request counter are zero between calls.
+  bool verify_fused = false;
+  unsigned int* vcnt = nullptr;
+  size_t vcnt_n = 0;
   // draft: running best (key, index) per (position, request), zero between calls
   unsigned long long* best = nullptr;
   size_t best_n = 0;
@@ -235,6 +249,24 @@ int ensure_best(dspark_ctx* c, size_t n) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Verify counters (B task counters, then the decided-request counter on its
+// own line): zeroed when (re)allocated; every call leaves them zero.
+int ensure_vcnt(dspark_ctx* c, size_t B) {
+  const size_t n = align256((B + 64) * sizeof(unsigned int)) / sizeof(unsigned int);
+  if (n <= c->vcnt_n) return DSPARK_OK;
+  DSPARK_HIP(c, hipDeviceSynchronize());
+  if (c->vcnt) (void)hipFree(c->vcnt);
+  c->vcnt = nullptr;
+  c->vcnt_n = 0;
+  if (hipMalloc(&c->vcnt, n * sizeof(unsigned int)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, DSPARK_ENOMEM, "allocation of %zu bytes failed", n * sizeof(unsigned int));
+  }
+  DSPARK_HIP(c, hipMemset(c->vcnt, 0, n * sizeof(unsigned int)));
+  c->vcnt_n = n;
+  return DSPARK_OK;
+}
 
 // Vocabulary-sweep plan: aim at eight waves per CU, at least four 16-wide
 // tiles per wave, and a grid that is a multiple of the XCD count.
@@ -771,6 +803,8 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   int* lists[2] = {reinterpret_cast<int*>(ws + off_list),
                    reinterpret_cast<int*>(ws + off_list + align256((size_t)(B + 1) * sizeof(int)))};
 
+  const bool fused = c->verify_fused;
+  if (fused && (rc = ensure_vcnt(c, (size_t)B))) return rc;
   const float invT = greedy ? 1.0f : 1.0f / temperature;
   for (int w = 0; w < n_win; ++w) {
     const int nrows = win_hi[w] - win_lo[w] + 1;
@@ -786,8 +820,11 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
     va.first = w == 0;
     va.vstate = vstate;
     // later windows walk the requests the previous window left pending
-    va.list_in = (w > 0 && c->verify_list) ? lists[(w - 1) % 2] : nullptr;
-    va.list_out = (w + 1 < n_win && c->verify_list) ? lists[w % 2] : nullptr;
+    va.list_in = (w > 0 && (c->verify_list || fused)) ? lists[(w - 1) % 2] : nullptr;
+    va.list_out = (w + 1 < n_win && (c->verify_list || fused)) ? lists[w % 2] : nullptr;
+    va.decide = fused ? 1 : 0;
+    va.dcnt = c->vcnt;
+    va.wcnt = c->vcnt + align256((size_t)B * sizeof(unsigned int)) / sizeof(unsigned int);
     va.T = target;
     va.tsb = t_stride_b;
     va.toffs = toffs;
@@ -813,7 +850,9 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
                                   : dim3(n_chunks, B * nrows);
     if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), rgrid, dim3(kRowsThreads), &va, stream)))
       return rc;
-    if ((rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &va, stream))) return rc;
+    if (!fused &&
+        (rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &va, stream)))
+      return rc;
   }
   if (greedy) return DSPARK_OK;
 
@@ -1008,6 +1047,7 @@ int dspark_create(dspark_ctx** out, int device) {
     (void)hipGetLastError();
     (void)hipFree(c->dev_err);
     if (c->chain_flags) (void)hipFree(c->chain_flags);
+    if (c->vcnt) (void)hipFree(c->vcnt);
     delete c;
     return DSPARK_EHIP;
   }
@@ -1074,6 +1114,8 @@ int dspark_create(dspark_ctx** out, int device) {
   }
   const char* vl = getenv("DSPARK_VERIFY_LIST");
   if (vl && vl[0] == '0' && vl[1] == 0) c->verify_list = false;
+  const char* vf = getenv("DSPARK_VERIFY_FUSED");
+  if (vf && vf[0] == '1' && vf[1] == 0) c->verify_fused = true;
   const char* vw = getenv("DSPARK_VERIFY_WINDOWS");
   if (vw) {
     int tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};

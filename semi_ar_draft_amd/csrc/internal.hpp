@@ -119,6 +119,14 @@ struct VerifyArgs {
   int32_t* resid_k;
   float* resid_lt;
   float* row_lse;                // diagnostic pass: ln sum exp(t/T) of rows 1..gamma, [B][gamma]
+  // decisions inside the row pass (0 for the diagnostic pass): a request's
+  // last finished task merges its rows and decides it; the last request
+  // decided builds list_out.  dcnt [B] counts finished tasks per request,
+  // wcnt[0] the requests decided in the window; both are zero between
+  // windows (each decider clears what it used)
+  int decide;
+  unsigned int* dcnt;
+  unsigned int* wcnt;
   int32_t* err;
 };
 

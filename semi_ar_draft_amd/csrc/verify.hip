@@ -119,6 +119,26 @@ __device__ __forceinline__ void row_chunk(RowState& st, const float4* p, int c0,
   }
 }
 
+// Stores and loads of the values one workgroup hands to another within a
+// launch (chunk partials, request states): agent-scope atomics, which the
+// other XCDs' caches cannot hold stale.
+__device__ __forceinline__ void st_u32(void* p, uint32_t v) {
+  __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_u32(const void* p) {
+  return __hip_atomic_load(static_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_state(int2* p, int2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     (unsigned long long)(uint32_t)v.x | ((unsigned long long)(uint32_t)v.y << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int2 ld_state(const int2* p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_int2((int)(uint32_t)v, (int)(uint32_t)(v >> 32));
+}
+
 // The partial (max, sum, key, index) of one 32 KB chunk of target row
 // (b, k), from the whole workgroup.  Rows past K_b + 1 are skipped (the
 // condition is uniform over the workgroup).
@@ -152,35 +172,18 @@ __device__ __forceinline__ void row_task(const VerifyArgs& a, int b, int k, int 
 #pragma unroll
     for (int w = 1; w < kRowsThreads / 64; ++w) row_merge(acc, red[w]);
     const int64_t o = row * a.n_chunks + chunk;
-    a.pf[o] = make_float4(acc.m, acc.s, acc.key, 0.f);
-    a.pi[o] = acc.idx;
+    if (a.decide) {
+      // read within this launch by the request's decider
+      st_u32(&a.pf[o].x, __float_as_uint(acc.m));
+      st_u32(&a.pf[o].y, __float_as_uint(acc.s));
+      st_u32(&a.pf[o].z, __float_as_uint(acc.key));
+      st_u32(&a.pi[o], (uint32_t)acc.idx);
+    } else {
+      a.pf[o] = make_float4(acc.m, acc.s, acc.key, 0.f);
+      a.pi[o] = acc.idx;
+    }
   }
   __syncthreads();                                       // red is reused by the next task
-}
-
-// Row pass of one window.  Without a work list: one workgroup per (chunk,
-// request, row).  With one (later windows): a fixed grid walks the tasks
-// (pending request, row, chunk) of the listed requests, so the requests
-// already decided cost no workgroups.
-__global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArgs a) {
-  __shared__ RowState red[kRowsThreads / 64];
-  const int nrows = a.hi - a.lo + 1;
-  if (a.list_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.list_out[0] = 0;
-  if (!a.list_in) {
-    const int chunk = blockIdx.x;
-    const int b = blockIdx.y / nrows;
-    const int k = a.lo + blockIdx.y % nrows;
-    if (!a.first && a.vstate[b].y == 0) return;   // request already decided
-    row_task(a, b, k, chunk, red);
-    return;
-  }
-  const int per = nrows * a.n_chunks;
-  const int n_tasks = a.list_in[0] * per;
-  for (int t = blockIdx.x; t < n_tasks; t += gridDim.x) {
-    const int i = t / per;
-    const int rem = t - i * per;
-    row_task(a, a.list_in[1 + i], a.lo + rem / a.n_chunks, rem % a.n_chunks, red);
-  }
 }
 
 // One wave per request: merge the chunk partials of its rows lo .. last of
@@ -190,12 +193,14 @@ __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArg
 // drafts, the compensation / bonus token when it is known here, the residual
 // request otherwise; a request that kept every row of the window and has
 // rows left stays pending for the next window.
-__global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  if (!a.first && a.vstate[b].y == 0) return;
+//
+// kCoherent: called inside the row pass (the partials and the request states
+// of this window were written by other workgroups of the same launch).
+template <bool kCoherent>
+__device__ __forceinline__ void decide_request(const VerifyArgs& a, int b, int lane) {
+  const int2 vs0 = a.first ? make_int2(0, 0) : a.vstate[b];   // written by the previous window
   const int kb = clamp_k(a.K, b, a.gamma, a.err, false);
-  const int A0 = a.first ? 0 : a.vstate[b].x;
+  const int A0 = vs0.x;
   const int last = min(a.hi, kb + 1);
   const int n_rows = last - a.lo + 1;                      // >= 1 for a pending request
   const int n_test = max(0, min(last, kb) - a.lo + 1);     // rows with an accept test
@@ -227,8 +232,14 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
     if (r < n_rows) {
       const int64_t base = (row0 + r) * a.n_chunks;
       for (int c = lane & 7; c < a.n_chunks; c += 8) {
-        const float4 q = a.pf[base + c];
-        row_merge(st, RowState{q.x, q.y, q.z, a.pi[base + c]});
+        if constexpr (kCoherent) {
+          const float4* q = &a.pf[base + c];
+          row_merge(st, RowState{__uint_as_float(ld_u32(&q->x)), __uint_as_float(ld_u32(&q->y)),
+                                 __uint_as_float(ld_u32(&q->z)), (int)ld_u32(&a.pi[base + c])});
+        } else {
+          const float4 q = a.pf[base + c];
+          row_merge(st, RowState{q.x, q.y, q.z, a.pi[base + c]});
+        }
       }
     }
 #pragma unroll
@@ -278,8 +289,12 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
     final_tok = __shfl(my_star, kb + 1 - a.lo, 64);        // every draft kept: bonus from row K_b + 1
   } else {
     if (lane == 0) {
-      a.vstate[b] = make_int2(A, a.hi + 1);                // rows left: wait for the next window
-      if (a.list_out) a.list_out[1 + atomicAdd(a.list_out, 1)] = b;
+      if constexpr (kCoherent) {
+        st_state(&a.vstate[b], make_int2(A, a.hi + 1));    // rows left: wait for the next window
+      } else {
+        a.vstate[b] = make_int2(A, a.hi + 1);
+        if (a.list_out) a.list_out[1 + atomicAdd(a.list_out, 1)] = b;
+      }
     }
     return;
   }
@@ -295,7 +310,97 @@ __global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
     a.accept_len[b] = A;
     a.resid_k[b] = resid;
     a.resid_lt[b] = resid_lt;
-    a.vstate[b] = make_int2(A, 0);
+    if constexpr (kCoherent)
+      st_state(&a.vstate[b], make_int2(A, 0));
+    else
+      a.vstate[b] = make_int2(A, 0);
+  }
+}
+
+__global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
+  const int b = blockIdx.x;
+  if (!a.first && a.vstate[b].y == 0) return;
+  decide_request<false>(a, b, threadIdx.x);
+}
+
+// Row pass of one window.  Without a work list: one workgroup per (chunk,
+// request, row).  With one (later windows): a fixed grid walks the tasks
+// (pending request, row, chunk) of the listed requests, so the requests
+// already decided cost no workgroups.
+//
+// With a.decide, each task then counts itself for its request (after its
+// partial has been stored coherently); the request's last task merges the
+// request's rows and decides it (wave 0), and the last request decided in
+// the window writes the list of the requests still pending (list_out).
+// Every request of the window decides once, so the counters are back at
+// zero when the window ends.
+__device__ __forceinline__ void count_and_decide(const VerifyArgs& a, int b, int per, int n_pend, int* sh) {
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0xF70);                   // this task's partial stores have completed
+    sh[0] = (int)__hip_atomic_fetch_add(&a.dcnt[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const bool last_task = sh[0] == per - 1;
+  __syncthreads();
+  if (!last_task) return;                                // uniform over the block
+  if (threadIdx.x < 64) decide_request<true>(a, b, threadIdx.x);
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&a.dcnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0xF70);                   // the request's state has been stored
+    sh[0] = (int)__hip_atomic_fetch_add(a.wcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const bool last_req = sh[0] == n_pend - 1;
+  __syncthreads();
+  if (!last_req) return;
+  if (threadIdx.x == 0) __hip_atomic_store(a.wcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!a.list_out) return;
+  // every request of the window is decided: list the pending ones
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += kRowsThreads) {
+    const int bb = b0 + (int)threadIdx.x;
+    const bool pend = bb < a.B && ld_state(&a.vstate[bb]).y != 0;
+    const uint64_t m = __ballot(pend);
+    if (lane == 0) sh[1 + wid] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wid; ++w) off += sh[1 + w];
+    if (pend) a.list_out[1 + off + __popcll(m & ((1ull << lane) - 1ull))] = bb;
+    int tot = 0;
+    for (int w = 0; w < kRowsThreads / 64; ++w) tot += sh[1 + w];
+    base += tot;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.list_out[0] = base;
+}
+
+__global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArgs a) {
+  __shared__ RowState red[kRowsThreads / 64];
+  __shared__ int sh[1 + kRowsThreads / 64];
+  const int nrows = a.hi - a.lo + 1;
+  const int per = nrows * a.n_chunks;
+  if (!a.decide && a.list_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.list_out[0] = 0;
+  if (!a.list_in) {
+    const int chunk = blockIdx.x;
+    const int b = blockIdx.y / nrows;
+    const int k = a.lo + blockIdx.y % nrows;
+    if (!a.first && a.vstate[b].y == 0) return;   // request already decided
+    row_task(a, b, k, chunk, red);
+    if (a.decide) count_and_decide(a, b, per, a.B, sh);
+    return;
+  }
+  const int n_pend = a.list_in[0];
+  // no request pending: nobody decides, so the (empty) next list is written here
+  if (a.decide && n_pend == 0 && a.list_out && blockIdx.x == 0 && threadIdx.x == 0) a.list_out[0] = 0;
+  const int n_tasks = n_pend * per;
+  for (int t = blockIdx.x; t < n_tasks; t += gridDim.x) {
+    const int i = t / per;
+    const int rem = t - i * per;
+    const int b = a.list_in[1 + i];
+    row_task(a, b, a.lo + rem / a.n_chunks, rem % a.n_chunks, red);
+    if (a.decide) count_and_decide(a, b, per, n_pend, sh);
   }
 }
 
