@@ -204,7 +204,7 @@ def sts_fit_bench(args):
 
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                               "draft_sweep_traffic_B128_V151936_r256_T1.json")
+                               "draft_chain_traffic_B128_V151936_r256_T1.json")
 
 
 STS_TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -212,7 +212,8 @@ STS_TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "
 
 
 def measured_traffic(wl_name, B, V, r, T):
-    """HBM bytes per draft-sweep launch from the committed counter profile."""
+    """HBM bytes per launch of the dominant draft kernel from the committed
+    counter profile."""
     return profile_traffic(TRAFFIC_PROFILE, {"name": wl_name, "B": B, "V": V, "r": r, "temperature": T})
 
 
@@ -467,7 +468,7 @@ def main():
         achieved = sw["alg_GBps"]
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                    "traffic": measured_traffic(wl.name, B, V, r, T),
+                    "traffic": measured_traffic(wl.name, B, V, r, T) if chained else None,
                     "kernel": ("draft_chain (MFMA Markov bias + vocabulary sweep, every position in one "
                                "launch of persistent workgroups)" if chained else
                                "draft_persist (MFMA Markov bias + vocabulary sweep, all positions in one "
