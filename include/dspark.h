@@ -405,7 +405,8 @@ int dspark_verify_packed(dspark_ctx* ctx, hipStream_t stream,
  * and 0 when N == 0.  Ties go to the lowest candidate index.  The result is
  * what dspark_confidence takes as sts_T.
  *
- * N >= 0 samples (at most 2^33); 1 <= gamma <= 32.
+ * 0 <= N < 2^33 samples (a cell's sum of |label - score| in 2^-30 units
+ * then stays below 2^63); 1 <= gamma <= 32.
  * logit:      float [N][stride] (stride >= gamma): the confidence head's
  *             logits l = logit(c) before any temperature, positions 1..gamma
  *             in columns 0..gamma-1.  May be NULL when N == 0.

@@ -1370,7 +1370,7 @@ int dspark_sts_fit(dspark_ctx* c, hipStream_t stream, int64_t N, int gamma, cons
                 kStsMaxBins, kStsMaxCells);
   if (!grid || !T || !index || !ece || (N > 0 && (!logit || !accept_len)))
     return fail(c, DSPARK_EINVAL, "null pointer argument");
-  if (N > (int64_t)1 << 33) return fail(c, DSPARK_EINVAL, "N must be <= 2^33");
+  if (N >= (int64_t)1 << 33) return fail(c, DSPARK_EINVAL, "N must be < 2^33");
   DeviceGuard dg(c->device);
   if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
   int rc;

@@ -247,3 +247,24 @@ def test_sts_fit_two_contexts_on_two_streams():
     finally:
         c1.close()
         c2.close()
+
+
+def test_sts_fit_rejects_sample_counts_from_two_to_the_33():
+    """N < 2^33 keeps every cell's fixed-point sum (2^-30 units) below 2^63;
+    the limit is checked on the host before anything is enqueued (so the
+    small buffers passed here are never read)."""
+    c = dk.Context(0)
+    try:
+        d = synth.sts_calibration_set(10, 3, seed=1)
+        ld, ad = d["logit"].cuda(), d["accept_len"].cuda()
+        grid = synth.sts_grid(8).cuda()
+        T = torch.empty((3,), dtype=torch.float32, device="cuda")
+        idx = torch.empty((3,), dtype=torch.int32, device="cuda")
+        ece = torch.empty((3, 8), dtype=torch.float64, device="cuda")
+        for N in (1 << 33, 1 << 40):
+            rc = c.lib.dspark_sts_fit(c._h, None, N, 3, ld.data_ptr(), 3, ad.data_ptr(), grid.data_ptr(), 8, 10,
+                                      T.data_ptr(), idx.data_ptr(), ece.data_ptr())
+            assert rc == dk.DSPARK_EINVAL
+            assert b"2^33" in c.lib.dspark_last_error(c._h)
+    finally:
+        c.close()
