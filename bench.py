@@ -452,6 +452,14 @@ def main():
             vr["needed_rows_per_step"] = needed_rows
             vr["read_rows_per_step"] = read_rows
             vr["alg_GBps"] = vb / (vr["us_per_step"] * 1e-6) / 1e9
+        if "verify_chain" in per_kernel:
+            # one launch reads each request's rows up to its decision: exactly the needed rows
+            vb = 4.0 * V * needed_rows
+            vc = per_kernel["verify_chain"]
+            vc["alg_bytes_per_step"] = vb
+            vc["needed_rows_per_step"] = needed_rows
+            vc["read_rows_per_step"] = needed_rows
+            vc["alg_GBps"] = vb / (vc["us_per_step"] * 1e-6) / 1e9
         if "resid_sweep" in per_kernel:
             n_rej = float((A < Ks).sum().item()) / args.steps
             rb = 8.0 * V * n_rej + wbytes * r * V + wbytes * n_rej * r

@@ -119,7 +119,8 @@ enum {
   DSPARK_K_DIAG = 10,          /* diagnostic passes (dspark_accept_prob) */
   DSPARK_K_STS = 11,           /* temperature fit: the pass of one position */
   DSPARK_K_DRAFT_CHAIN = 12,   /* chained draft: every position in one launch */
-  DSPARK_K_COUNT = 13
+  DSPARK_K_VERIFY_CHAIN = 13,  /* verify chain: every needed target row in one launch */
+  DSPARK_K_COUNT = 14
 };
 int dspark_timing_enable(dspark_ctx* ctx, int enable);
 int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
@@ -333,7 +334,14 @@ int dspark_schedule_async(dspark_ctx* ctx, hipStream_t stream,
  * arguments are those given to / returned by dspark_draft_markov, or by
  * dspark_draft_rnn (states non-NULL; W1 and anchor may then be NULL); K:
  * int32 [B] or NULL (values outside 0..gamma are clamped and flagged).
- * accept_len: int32 [B]; out_tokens: int32 [B][gamma+1]. */
+ * accept_len: int32 [B]; out_tokens: int32 [B][gamma+1].
+ * Execution: target rows after a request's first rejection are not read.
+ * By default the rows are read in windows (rows 1-2 of every request, then
+ * row 3, then the rest, of the requests that kept every draft so far), each
+ * a row pass and a decision launch.  DSPARK_VERIFY_CHAIN=1 reads every
+ * needed row in one launch instead, deciding each request row by row as its
+ * rows complete (rows read DSPARK_VERIFY_AHEAD ahead, default 2; V up to
+ * 524288); the outputs are identical. */
 int dspark_verify(dspark_ctx* ctx, hipStream_t stream,
                   int B, int gamma, int V, int r, dspark_dtype wdtype,
                   const float* target, int64_t t_stride_b, int64_t t_stride_k,

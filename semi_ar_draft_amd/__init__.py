@@ -28,7 +28,7 @@ EXPORTS = (
 )
 KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
                   "verify_rows", "verify_decide", "resid_sweep", "resid_combine", "gru", "diag", "sts_fit",
-                  "draft_chain")
+                  "draft_chain", "verify_chain")
 
 _lib = None
 _vp, _i32, _i64, _u64, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float

@@ -157,16 +157,15 @@ struct dspark_ctx {
   // later windows walk a list of the pending requests (else one workgroup per
   // row chunk of every request, most of which find it decided)
   bool verify_list = true;
-  // each window's accept decisions taken inside its row pass by the
-  // request's last task, instead of a separate decision launch per window
-  // (DSPARK_VERIFY_FUSED=1).  Measured slower on the headline batch: the
-  // row pass went from 31.9 to 49.0 us per window (each 32 KB task holds its
-  // workgroup for the atomic round trip of its count) against the 4.4 us
-  // decision launch it saves.  Its per-request task counters and
-  // decided-request counter are zero between calls.
-  bool verify_fused = false;
-  unsigned int* vcnt = nullptr;
-  size_t vcnt_n = 0;
+  // verify chain: every needed target row of the call in one launch, each
+  // request's rows decided one after another inside it (DSPARK_VERIFY_CHAIN);
+  // its counter block (zero between calls) and resident workgroups per CU
+  bool verify_chain = false;
+  unsigned int* vq = nullptr;
+  size_t vq_n = 0;
+  int vchain_wg_per_cu = 0;
+  int vchain_wg = 0;              // workgroups per CU of its grid (0: as many as are resident)
+  int vchain_ahead = 2;           // rows of a request read ahead of its decisions
   // draft: running best (key, index) per (position, request), zero between calls
   unsigned long long* best = nullptr;
   size_t best_n = 0;
@@ -252,19 +251,19 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Verify counters (B task counters, then the decided-request counter on its
 // own line): zeroed when (re)allocated; every call leaves them zero.
-int ensure_vcnt(dspark_ctx* c, size_t B) {
-  const size_t n = align256((B + 64) * sizeof(unsigned int)) / sizeof(unsigned int);
-  if (n <= c->vcnt_n) return DSPARK_OK;
+int ensure_vq(dspark_ctx* c, size_t words) {
+  if (words <= c->vq_n) return DSPARK_OK;
   DSPARK_HIP(c, hipDeviceSynchronize());
-  if (c->vcnt) (void)hipFree(c->vcnt);
-  c->vcnt = nullptr;
-  c->vcnt_n = 0;
-  if (hipMalloc(&c->vcnt, n * sizeof(unsigned int)) != hipSuccess) {
+  if (c->vq) (void)hipFree(c->vq);
+  c->vq = nullptr;
+  c->vq_n = 0;
+  if (hipMalloc(&c->vq, words * sizeof(unsigned int)) != hipSuccess) {
     (void)hipGetLastError();
-    return fail(c, DSPARK_ENOMEM, "allocation of %zu bytes failed", n * sizeof(unsigned int));
+    return fail(c, DSPARK_ENOMEM, "allocation of %zu bytes failed", words * sizeof(unsigned int));
   }
-  DSPARK_HIP(c, hipMemset(c->vcnt, 0, n * sizeof(unsigned int)));
-  c->vcnt_n = n;
+  DSPARK_HIP(c, hipMemset(c->vq, 0, words * sizeof(unsigned int)));
+  DSPARK_HIP(c, hipDeviceSynchronize());
+  c->vq_n = words;
   return DSPARK_OK;
 }
 
@@ -803,9 +802,54 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
   int* lists[2] = {reinterpret_cast<int*>(ws + off_list),
                    reinterpret_cast<int*>(ws + off_list + align256((size_t)(B + 1) * sizeof(int)))};
 
-  const bool fused = c->verify_fused;
-  if (fused && (rc = ensure_vcnt(c, (size_t)B))) return rc;
+  const bool vchain = c->verify_chain && c->vchain_wg_per_cu > 0 && n_chunks <= 64;
   const float invT = greedy ? 1.0f : 1.0f / temperature;
+  if (vchain) {
+    const int np = std::min(kVqMaxPart, B);
+    const int per_cu = c->vchain_wg > 0 ? std::min(c->vchain_wg, c->vchain_wg_per_cu) : c->vchain_wg_per_cu;
+    const int wp = std::max(1, per_cu * c->cu_count / np);
+    const int qcap = ((B + np - 1) / np) * gamma + (wp + n_chunks - 1) / n_chunks + 4;
+    if ((rc = ensure_vq(c, vq_words(rows, np, qcap)))) return rc;
+    VerifyArgs va;
+    memset(&va, 0, sizeof(va));
+    va.B = B;
+    va.gamma = gamma;
+    va.V = V;
+    va.n_chunks = n_chunks;
+    va.greedy = greedy;
+    va.lo = 1;
+    va.hi = gamma + 1;
+    va.first = 1;                                        // K out of range is reported at row 1
+    va.vq = c->vq;
+    va.n_part = np;
+    va.qcap = qcap;
+    va.bar_test = c->bar_test;
+    va.lookahead = c->vchain_ahead;
+    va.T = target;
+    va.tsb = t_stride_b;
+    va.toffs = toffs;
+    va.t_rows = t_rows;
+    va.tsk = t_stride_k;
+    va.K = K;
+    va.req = req_ids;
+    va.tokens = tokens;
+    va.lse = lse;
+    va.ytok = ytok;
+    va.invT = invT;
+    va.s2 = greedy ? kLog2e : kLog2e / temperature;
+    va.seed = seed;
+    va.pf = rpf;
+    va.pi = rpi;
+    va.accept_len = accept_len;
+    va.out_tokens = out_tokens;
+    va.resid_k = resid_k;
+    va.resid_lt = resid_lt;
+    va.err = c->dev_err;
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_CHAIN, verify_chain_kernel(), dim3(np * wp), dim3(kRowsThreads), &va,
+                      stream)))
+      return rc;
+    n_win = 0;                                           // no window passes
+  }
   for (int w = 0; w < n_win; ++w) {
     const int nrows = win_hi[w] - win_lo[w] + 1;
     VerifyArgs va;
@@ -820,11 +864,8 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
     va.first = w == 0;
     va.vstate = vstate;
     // later windows walk the requests the previous window left pending
-    va.list_in = (w > 0 && (c->verify_list || fused)) ? lists[(w - 1) % 2] : nullptr;
-    va.list_out = (w + 1 < n_win && (c->verify_list || fused)) ? lists[w % 2] : nullptr;
-    va.decide = fused ? 1 : 0;
-    va.dcnt = c->vcnt;
-    va.wcnt = c->vcnt + align256((size_t)B * sizeof(unsigned int)) / sizeof(unsigned int);
+    va.list_in = (w > 0 && c->verify_list) ? lists[(w - 1) % 2] : nullptr;
+    va.list_out = (w + 1 < n_win && c->verify_list) ? lists[w % 2] : nullptr;
     va.T = target;
     va.tsb = t_stride_b;
     va.toffs = toffs;
@@ -850,8 +891,7 @@ int verify_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
                                   : dim3(n_chunks, B * nrows);
     if ((rc = klaunch(c, DSPARK_K_VERIFY_ROWS, verify_rows_kernel(), rgrid, dim3(kRowsThreads), &va, stream)))
       return rc;
-    if (!fused &&
-        (rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &va, stream)))
+    if ((rc = klaunch(c, DSPARK_K_VERIFY_DECIDE, verify_decide_kernel(), dim3(B), dim3(64), &va, stream)))
       return rc;
   }
   if (greedy) return DSPARK_OK;
@@ -1047,7 +1087,6 @@ int dspark_create(dspark_ctx** out, int device) {
     (void)hipGetLastError();
     (void)hipFree(c->dev_err);
     if (c->chain_flags) (void)hipFree(c->chain_flags);
-    if (c->vcnt) (void)hipFree(c->vcnt);
     delete c;
     return DSPARK_EHIP;
   }
@@ -1114,8 +1153,18 @@ int dspark_create(dspark_ctx** out, int device) {
   }
   const char* vl = getenv("DSPARK_VERIFY_LIST");
   if (vl && vl[0] == '0' && vl[1] == 0) c->verify_list = false;
-  const char* vf = getenv("DSPARK_VERIFY_FUSED");
-  if (vf && vf[0] == '1' && vf[1] == 0) c->verify_fused = true;
+  const char* vc = getenv("DSPARK_VERIFY_CHAIN");
+  if (vc && vc[1] == 0 && (vc[0] == '0' || vc[0] == '1')) c->verify_chain = vc[0] == '1';
+  const char* vca = getenv("DSPARK_VERIFY_AHEAD");
+  if (vca) {
+    const int v = atoi(vca);
+    if (v >= 1 && v <= 8) c->vchain_ahead = v;
+  }
+  const char* vcw = getenv("DSPARK_VERIFY_CHAIN_WG");
+  if (vcw) {
+    const int v = atoi(vcw);
+    if (v >= 1 && v <= 16) c->vchain_wg = v;
+  }
   const char* vw = getenv("DSPARK_VERIFY_WINDOWS");
   if (vw) {
     int tmp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -1144,6 +1193,15 @@ int dspark_create(dspark_ctx** out, int device) {
     }
     c->chain_wg_per_cu = nb;
   }
+  // resident workgroups per CU of the verify chain (its grid)
+  {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, verify_chain_kernel(), kRowsThreads, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      nb = 0;
+    }
+    c->vchain_wg_per_cu = nb;
+  }
   *out = c;
   return DSPARK_OK;
 }
@@ -1167,6 +1225,7 @@ void dspark_destroy(dspark_ctx* c) {
     if (c->sts_buf) (void)hipFree(c->sts_buf);
     if (c->dev_err) (void)hipFree(c->dev_err);
     if (c->chain_flags) (void)hipFree(c->chain_flags);
+    if (c->vq) (void)hipFree(c->vq);
   }
   delete c;
 }

@@ -112,23 +112,38 @@ struct VerifyArgs {
   const float* ytok;
   float invT, s2;                // 1/T and log2(e)/T (greedy: 1 and log2 e)
   uint64_t seed;
-  float4* pf;                    // [B*(gamma+1)][n_chunks]: m2, s, key, -
+  float4* pf;                    // [B*(gamma+1)][n_chunks]: m2, s, key, (verify chain) t at the token
   int* pi;
   int32_t* accept_len;
   int32_t* out_tokens;
   int32_t* resid_k;
   float* resid_lt;
   float* row_lse;                // diagnostic pass: ln sum exp(t/T) of rows 1..gamma, [B][gamma]
-  // decisions inside the row pass (0 for the diagnostic pass): a request's
-  // last finished task merges its rows and decides it; the last request
-  // decided builds list_out.  dcnt [B] counts finished tasks per request,
-  // wcnt[0] the requests decided in the window; both are zero between
-  // windows (each decider clears what it used)
-  int decide;
-  unsigned int* dcnt;
-  unsigned int* wcnt;
+  // verify chain (every row in one launch): its counter block (layout in
+  // verify.hip, zero at launch and left zero), the request partitions and
+  // the row slots per partition; bar_test: every wait for a row gives up
+  // after 64 polls (failure injection from the host)
+  unsigned int* vq;
+  int n_part, qcap, bar_test;
+  int lookahead;                 // rows of a request in flight ahead of its decisions (>= 1)
   int32_t* err;
 };
+// Counter block of the verify chain, in 32-bit words: per partition p a
+// ticket counter, a row-queue tail, a count of decided requests and the last
+// row slot any ticket may wait on, each on its own 128-byte line; an exit
+// counter and an abort flag; one finished-chunk counter per target row
+// (64-byte stride); then the row slots of each partition, one 128-byte line
+// each (a slot is polled by the workgroups holding its tickets).
+constexpr int kVqPartWords = 128;
+constexpr int kVqMaxPart = 8;
+constexpr int kVqExit = kVqMaxPart * kVqPartWords;
+constexpr int kVqAbort = kVqExit + 32;
+constexpr int kVqRows = kVqExit + 128;
+constexpr int kVqRowStride = 16;
+constexpr int kVqSlotStride = 32;
+__host__ __device__ constexpr size_t vq_words(int rows, int n_part, int qcap) {
+  return (size_t)kVqRows + (size_t)kVqRowStride * rows + (size_t)kVqSlotStride * n_part * qcap;
+}
 
 constexpr int kMaxGamma = 32;   // longest draft (positions per request)
 
@@ -230,6 +245,7 @@ const void* combine_alpha_kernel();
 const void* rows_lse_kernel();
 const void* verify_rows_kernel();
 const void* verify_decide_kernel();
+const void* verify_chain_kernel();
 const void* confidence_kernel();
 // temperature fit: one scoring pass per position (its last workgroup selects)
 const void* sts_hist_kernel(int n_slices, int cells);   // 1..4 slices of 64 candidates per lane

@@ -1443,6 +1443,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_resid_impl(const Comb
       tok = 0;
     }
     const int A = a.accept_len[b];
+    if ((unsigned)A > (unsigned)a.gamma) {               // only after a failed verification
+      atomicOr(a.err, kErrK);
+      return;
+    }
     a.out_tokens[(int64_t)b * (a.gamma + 1) + A] = tok;
   }
 }

@@ -99,12 +99,14 @@ __device__ __forceinline__ void row_fold(RowState& st, RowLead& ld, const float4
 // One chunk of kRowsPer float4 per thread: every load is issued before the
 // first is used; float4 indices at or past c1 are skipped.  A Gumbel-max
 // leader becomes the key log2 w_b + m - log2 E_b at the end.
-template <int KEYMODE>
-__device__ __forceinline__ void row_chunk(RowState& st, const float4* p, int c0, int c1, float s2, uint32_t klo,
-                                          uint32_t khi) {
-  float4 x[kRowsPer];
+__device__ __forceinline__ void row_load(float4 (&x)[kRowsPer], const float4* p, int c0, int c1) {
 #pragma unroll
   for (int i = 0; i < kRowsPer; ++i) x[i] = p[min(c0 + (int)threadIdx.x + i * kRowsThreads, c1 - 1)];
+}
+
+template <int KEYMODE>
+__device__ __forceinline__ void row_fold_all(RowState& st, const float4 (&x)[kRowsPer], int c0, int c1, float s2,
+                                             uint32_t klo, uint32_t khi) {
   RowLead ld{0.0f, 1.0f, 0x7fffffff};
 #pragma unroll
   for (int i = 0; i < kRowsPer; ++i) {
@@ -119,6 +121,14 @@ __device__ __forceinline__ void row_chunk(RowState& st, const float4* p, int c0,
   }
 }
 
+template <int KEYMODE>
+__device__ __forceinline__ void row_chunk(RowState& st, const float4* p, int c0, int c1, float s2, uint32_t klo,
+                                          uint32_t khi) {
+  float4 x[kRowsPer];
+  row_load(x, p, c0, c1);
+  row_fold_all<KEYMODE>(st, x, c0, c1, s2, klo, khi);
+}
+
 // Stores and loads of the values one workgroup hands to another within a
 // launch (chunk partials, request states): agent-scope atomics, which the
 // other XCDs' caches cannot hold stale.
@@ -128,17 +138,6 @@ __device__ __forceinline__ void st_u32(void* p, uint32_t v) {
 __device__ __forceinline__ uint32_t ld_u32(const void* p) {
   return __hip_atomic_load(static_cast<const uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_state(int2* p, int2 v) {
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
-                     (unsigned long long)(uint32_t)v.x | ((unsigned long long)(uint32_t)v.y << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int2 ld_state(const int2* p) {
-  const unsigned long long v =
-      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_int2((int)(uint32_t)v, (int)(uint32_t)(v >> 32));
-}
-
 // The partial (max, sum, key, index) of one 32 KB chunk of target row
 // (b, k), from the whole workgroup.  Rows past K_b + 1 are skipped (the
 // condition is uniform over the workgroup).
@@ -172,16 +171,8 @@ __device__ __forceinline__ void row_task(const VerifyArgs& a, int b, int k, int 
 #pragma unroll
     for (int w = 1; w < kRowsThreads / 64; ++w) row_merge(acc, red[w]);
     const int64_t o = row * a.n_chunks + chunk;
-    if (a.decide) {
-      // read within this launch by the request's decider
-      st_u32(&a.pf[o].x, __float_as_uint(acc.m));
-      st_u32(&a.pf[o].y, __float_as_uint(acc.s));
-      st_u32(&a.pf[o].z, __float_as_uint(acc.key));
-      st_u32(&a.pi[o], (uint32_t)acc.idx);
-    } else {
-      a.pf[o] = make_float4(acc.m, acc.s, acc.key, 0.f);
-      a.pi[o] = acc.idx;
-    }
+    a.pf[o] = make_float4(acc.m, acc.s, acc.key, 0.f);
+    a.pi[o] = acc.idx;
   }
   __syncthreads();                                       // red is reused by the next task
 }
@@ -193,10 +184,6 @@ __device__ __forceinline__ void row_task(const VerifyArgs& a, int b, int k, int 
 // drafts, the compensation / bonus token when it is known here, the residual
 // request otherwise; a request that kept every row of the window and has
 // rows left stays pending for the next window.
-//
-// kCoherent: called inside the row pass (the partials and the request states
-// of this window were written by other workgroups of the same launch).
-template <bool kCoherent>
 __device__ __forceinline__ void decide_request(const VerifyArgs& a, int b, int lane) {
   const int2 vs0 = a.first ? make_int2(0, 0) : a.vstate[b];   // written by the previous window
   const int kb = clamp_k(a.K, b, a.gamma, a.err, false);
@@ -232,14 +219,8 @@ __device__ __forceinline__ void decide_request(const VerifyArgs& a, int b, int l
     if (r < n_rows) {
       const int64_t base = (row0 + r) * a.n_chunks;
       for (int c = lane & 7; c < a.n_chunks; c += 8) {
-        if constexpr (kCoherent) {
-          const float4* q = &a.pf[base + c];
-          row_merge(st, RowState{__uint_as_float(ld_u32(&q->x)), __uint_as_float(ld_u32(&q->y)),
-                                 __uint_as_float(ld_u32(&q->z)), (int)ld_u32(&a.pi[base + c])});
-        } else {
-          const float4 q = a.pf[base + c];
-          row_merge(st, RowState{q.x, q.y, q.z, a.pi[base + c]});
-        }
+        const float4 q = a.pf[base + c];
+        row_merge(st, RowState{q.x, q.y, q.z, a.pi[base + c]});
       }
     }
 #pragma unroll
@@ -289,12 +270,8 @@ __device__ __forceinline__ void decide_request(const VerifyArgs& a, int b, int l
     final_tok = __shfl(my_star, kb + 1 - a.lo, 64);        // every draft kept: bonus from row K_b + 1
   } else {
     if (lane == 0) {
-      if constexpr (kCoherent) {
-        st_state(&a.vstate[b], make_int2(A, a.hi + 1));    // rows left: wait for the next window
-      } else {
-        a.vstate[b] = make_int2(A, a.hi + 1);
-        if (a.list_out) a.list_out[1 + atomicAdd(a.list_out, 1)] = b;
-      }
+      a.vstate[b] = make_int2(A, a.hi + 1);              // rows left: wait for the next window
+      if (a.list_out) a.list_out[1 + atomicAdd(a.list_out, 1)] = b;
     }
     return;
   }
@@ -310,97 +287,384 @@ __device__ __forceinline__ void decide_request(const VerifyArgs& a, int b, int l
     a.accept_len[b] = A;
     a.resid_k[b] = resid;
     a.resid_lt[b] = resid_lt;
-    if constexpr (kCoherent)
-      st_state(&a.vstate[b], make_int2(A, 0));
-    else
-      a.vstate[b] = make_int2(A, 0);
+    a.vstate[b] = make_int2(A, 0);
   }
 }
 
 __global__ __launch_bounds__(64) void verify_decide_impl(const VerifyArgs a) {
   const int b = blockIdx.x;
   if (!a.first && a.vstate[b].y == 0) return;
-  decide_request<false>(a, b, threadIdx.x);
+  decide_request(a, b, threadIdx.x);
 }
 
 // Row pass of one window.  Without a work list: one workgroup per (chunk,
 // request, row).  With one (later windows): a fixed grid walks the tasks
 // (pending request, row, chunk) of the listed requests, so the requests
 // already decided cost no workgroups.
-//
-// With a.decide, each task then counts itself for its request (after its
-// partial has been stored coherently); the request's last task merges the
-// request's rows and decides it (wave 0), and the last request decided in
-// the window writes the list of the requests still pending (list_out).
-// Every request of the window decides once, so the counters are back at
-// zero when the window ends.
-__device__ __forceinline__ void count_and_decide(const VerifyArgs& a, int b, int per, int n_pend, int* sh) {
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_s_waitcnt(0xF70);                   // this task's partial stores have completed
-    sh[0] = (int)__hip_atomic_fetch_add(&a.dcnt[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  const bool last_task = sh[0] == per - 1;
-  __syncthreads();
-  if (!last_task) return;                                // uniform over the block
-  if (threadIdx.x < 64) decide_request<true>(a, b, threadIdx.x);
-  if (threadIdx.x == 0) {
-    __hip_atomic_store(&a.dcnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0xF70);                   // the request's state has been stored
-    sh[0] = (int)__hip_atomic_fetch_add(a.wcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  const bool last_req = sh[0] == n_pend - 1;
-  __syncthreads();
-  if (!last_req) return;
-  if (threadIdx.x == 0) __hip_atomic_store(a.wcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!a.list_out) return;
-  // every request of the window is decided: list the pending ones
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  int base = 0;
-  for (int b0 = 0; b0 < a.B; b0 += kRowsThreads) {
-    const int bb = b0 + (int)threadIdx.x;
-    const bool pend = bb < a.B && ld_state(&a.vstate[bb]).y != 0;
-    const uint64_t m = __ballot(pend);
-    if (lane == 0) sh[1 + wid] = __popcll(m);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wid; ++w) off += sh[1 + w];
-    if (pend) a.list_out[1 + off + __popcll(m & ((1ull << lane) - 1ull))] = bb;
-    int tot = 0;
-    for (int w = 0; w < kRowsThreads / 64; ++w) tot += sh[1 + w];
-    base += tot;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) a.list_out[0] = base;
-}
-
 __global__ __launch_bounds__(kRowsThreads) void verify_rows_impl(const VerifyArgs a) {
   __shared__ RowState red[kRowsThreads / 64];
-  __shared__ int sh[1 + kRowsThreads / 64];
   const int nrows = a.hi - a.lo + 1;
   const int per = nrows * a.n_chunks;
-  if (!a.decide && a.list_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.list_out[0] = 0;
+  if (a.list_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.list_out[0] = 0;
   if (!a.list_in) {
     const int chunk = blockIdx.x;
     const int b = blockIdx.y / nrows;
     const int k = a.lo + blockIdx.y % nrows;
     if (!a.first && a.vstate[b].y == 0) return;   // request already decided
     row_task(a, b, k, chunk, red);
-    if (a.decide) count_and_decide(a, b, per, a.B, sh);
     return;
   }
-  const int n_pend = a.list_in[0];
-  // no request pending: nobody decides, so the (empty) next list is written here
-  if (a.decide && n_pend == 0 && a.list_out && blockIdx.x == 0 && threadIdx.x == 0) a.list_out[0] = 0;
-  const int n_tasks = n_pend * per;
+  const int n_tasks = a.list_in[0] * per;
   for (int t = blockIdx.x; t < n_tasks; t += gridDim.x) {
     const int i = t / per;
     const int rem = t - i * per;
     const int b = a.list_in[1 + i];
     row_task(a, b, a.lo + rem / a.n_chunks, rem % a.n_chunks, red);
-    if (a.decide) count_and_decide(a, b, per, n_pend, sh);
+  }
+}
+
+// Verify chain: every needed target row in one launch, each request's rows
+// read one after another and decided as soon as its row is complete, so no
+// row after a request's first rejection is read and no launch separates the
+// rows.  The requests are split into n_part partitions (b mod n_part), each
+// served by the workgroups w with w mod n_part = p (same-address atomics are
+// served one after another, so each partition keeps its own counters).  A
+// partition's work items are (row, 32 KB chunk) tasks claimed from its
+// ticket counter: first the chunks of row 1 of each of its requests, then
+// the chunks of the rows its deciders append to its row queue.  A task's
+// partial is stored coherently and counted on its row's counter; the task
+// that completes a row merges the row's partials (in the order the window
+// path's decision uses) and takes the row's decision: an accepted draft
+// appends the next row to the queue; a rejection, or the bonus row K_b + 1,
+// ends the request.  A workgroup finishes its task before it waits on the
+// next ticket's row, and rows are appended by running workgroups only, so
+// the launch never depends on how many of its workgroups are resident.  When
+// a partition's last request is decided, its ticket counter is marked
+// closed and every row slot a claimed ticket may wait on is filled with a
+// closing code; the last workgroup to exit leaves the counter block at zero
+// for the next launch.  Every wait is bounded (it raises the barrier error
+// bit, and the workgroup then leaves).
+constexpr unsigned kVqClosed = 0x80000000u;
+constexpr unsigned kVqAbandon = 0x10000u;                  // row counter: its request has ended
+constexpr unsigned kVqSpinLimit = 1u << 20;
+
+__device__ __forceinline__ unsigned vq_add(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned vq_ld(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void vq_st(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One task of the verify chain: the partial (max, sum, key, index) of one
+// 32 KB chunk of target row (b, k), as the window pass forms it, plus the
+// target logit at the drafted token x_k when this chunk holds it (slot w of
+// the partial; the decision needs it).  The chunk's loads go out before
+// anything else is read, so the request's length K_b and the token only
+// decide how the loaded values are folded.
+__device__ __forceinline__ void chain_task(const VerifyArgs& a, int b, int k, int chunk, RowState* red,
+                                           float* s_tx) {
+  const float4* p =
+      reinterpret_cast<const float4*>(a.T + target_row(a.toffs, a.t_rows, a.tsb, a.tsk, b, k, a.err));
+  const int nv4 = a.V >> 2;
+  const int c0 = chunk * kRowsThreads * kRowsPer;
+  const int c1 = min(nv4, c0 + kRowsThreads * kRowsPer);
+  float4 x[kRowsPer];
+  row_load(x, p, c0, c1);
+  const int kb = clamp_k(a.K, b, a.gamma, a.err, k == 1 && chunk == 0 && threadIdx.x == 0);
+  int xt = -1;                                             // token tested at this row, if any
+  if (!a.greedy && k <= kb) {
+    xt = a.tokens[(int64_t)b * a.gamma + k - 1];
+    if ((unsigned)xt >= (unsigned)a.V) xt = 0;             // the decision reports it and tests x = 0
+  }
+  RowState st{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+  if (a.greedy) {
+    row_fold_all<1>(st, x, c0, c1, a.s2, 0, 0);
+  } else if (k == kb + 1) {
+    const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
+    const uint64_t key = stream_key(a.seed, req, (uint32_t)k, kBonus);
+    row_fold_all<2>(st, x, c0, c1, a.s2, (uint32_t)key, (uint32_t)(key >> 32));
+  } else {
+    row_fold_all<0>(st, x, c0, c1, a.s2, 0, 0);
+  }
+  if (xt >= 0) {
+    // the thread holding float4 xt / 4 (compile-time register indices only:
+    // a computed index would move x to scratch memory)
+    const int c = xt >> 2;
+    const int e = xt & 3;
+#pragma unroll
+    for (int i = 0; i < kRowsPer; ++i) {
+      if (c < c1 && c == c0 + (int)threadIdx.x + i * kRowsThreads)
+        *s_tx = e == 0 ? x[i].x : e == 1 ? x[i].y : e == 2 ? x[i].z : x[i].w;
+    }
+  }
+  wave_row_reduce(st);
+  const int wid = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wid] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    RowState acc = red[0];
+#pragma unroll
+    for (int w = 1; w < kRowsThreads / 64; ++w) row_merge(acc, red[w]);
+    const int64_t o = ((int64_t)b * (a.gamma + 1) + (k - 1)) * a.n_chunks + chunk;
+    st_u32(&a.pf[o].x, __float_as_uint(acc.m));
+    st_u32(&a.pf[o].y, __float_as_uint(acc.s));
+    st_u32(&a.pf[o].z, __float_as_uint(acc.key));
+    st_u32(&a.pf[o].w, __float_as_uint(*s_tx));
+    st_u32(&a.pi[o], (uint32_t)acc.idx);
+  }
+  __syncthreads();                                       // red and s_tx are reused by the next task
+}
+
+__device__ __forceinline__ unsigned* row_ctr(const VerifyArgs& a, int b, int k) {
+  return a.vq + kVqRows + (size_t)kVqRowStride * ((int64_t)b * (a.gamma + 1) + (k - 1));
+}
+
+// Appends row k of request b to the partition's row queue (one lane).
+__device__ __forceinline__ void chain_enqueue(const VerifyArgs& a, unsigned* part, unsigned* qrow, int b, int k) {
+  const unsigned sl = vq_add(part + 32, 1u);
+  if (sl < (unsigned)a.qcap)
+    vq_st(qrow + kVqSlotStride * sl, (unsigned)((int64_t)b * (a.gamma + 1) + (k - 1)) + 1u);
+  else
+    atomicOr(a.err, kErrBarrier);                          // cannot happen: qcap covers every row
+}
+
+// Decisions of request b from row k on (wave 0 of the workgroup that
+// completed row k; n_chunks <= 64).  A kept draft k adds its share to row
+// k + 1's counter; if that completes the row (its chunks were read ahead),
+// row k + 1 is decided here too.  n_req: requests of the partition, n_init:
+// its row-1 tasks.
+__device__ void chain_decide(const VerifyArgs& a, int b, int k, int lane, unsigned* part, unsigned* qrow, int n_req,
+                             unsigned n_init) {
+  const int kb = clamp_k(a.K, b, a.gamma, a.err, false);
+  const uint32_t req = a.req ? a.req[b] : (uint32_t)b;
+  int32_t* out = a.out_tokens + (int64_t)b * (a.gamma + 1);
+  for (;;) {
+    // loads that do not depend on the row's statistics go out first
+    const bool test = k <= kb;
+    int x = 0;
+    float lpd = 0.f;
+    if (test) {
+      x = a.tokens[(int64_t)b * a.gamma + k - 1];
+      if (!a.greedy) {
+        const int64_t o = (int64_t)b * a.gamma + k - 1;
+        lpd = a.ytok[o] - a.lse[o];
+      }
+    }
+    const int64_t row = (int64_t)b * (a.gamma + 1) + (k - 1);
+    // every chunk's partial at once: lane c loads chunk c
+    float pm = -INFINITY, ps = 0.f, pk = -INFINITY, ptx = 0.f;
+    int pidx = 0x7fffffff;
+    if (lane < a.n_chunks) {
+      const int64_t o = row * a.n_chunks + lane;
+      const float4* q = &a.pf[o];
+      pm = __uint_as_float(ld_u32(&q->x));
+      ps = __uint_as_float(ld_u32(&q->y));
+      pk = __uint_as_float(ld_u32(&q->z));
+      ptx = __uint_as_float(ld_u32(&q->w));
+      pidx = (int)ld_u32(&a.pi[o]);
+    }
+    if (lane == 0) vq_st(row_ctr(a, b, k), 0u);            // the row is complete: its counter is free
+    // merged in the decision kernel's order: lane j < 8 takes chunks j, j + 8,
+    // ... in turn, then a three-level butterfly
+    RowState st{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+    for (int c0 = 0; c0 < a.n_chunks; c0 += 8) {
+      const int c = c0 + (lane & 7);
+      const RowState o{__shfl(pm, c, 64), __shfl(ps, c, 64), __shfl(pk, c, 64), __shfl(pidx, c, 64)};
+      if (lane < 8 && c < a.n_chunks) row_merge(st, o);
+    }
+#pragma unroll
+    for (int mask = 1; mask < 8; mask <<= 1) {
+      RowState o{shfl_xor(st.m, mask), shfl_xor(st.s, mask), shfl_xor(st.key, mask), shfl_xor(st.idx, mask)};
+      row_merge(st, o);
+    }
+    const float lse_r = __shfl((st.m + fast_log2(st.s)) * kLn2, 0, 64);
+    const int star = __shfl(st.idx, 0, 64);
+    bool rej = false;
+    if (test) {                                            // uniform over the wave
+      if ((unsigned)x >= (unsigned)a.V) {
+        if (lane == 0) atomicOr(a.err, kErrToken);
+        x = 0;
+      }
+      if (a.greedy) {
+        rej = x != star;
+      } else {
+        const float tx = __shfl(ptx, (x >> 2) / (kRowsThreads * kRowsPer), 64);
+        const float lpt = tx * a.invT - lse_r;
+        const float rho = fast_exp2((lpt - lpd) * kLog2e);
+        const uint64_t key = stream_key(a.seed, req, (uint32_t)k, kAccept);
+        const float u = hash_uniform(elem_hash((uint32_t)key, (uint32_t)(key >> 32), 0u));
+        rej = !(u < rho);
+      }
+      if (!rej) {
+        // draft k kept: row k + lookahead joins the queue, and row k + 1
+        // (at most K_b + 1) gets its last share unless chunks are missing
+        int next = 0;
+        if (lane == 0) {
+          out[k - 1] = x;
+          if (k + a.lookahead <= kb + 1) chain_enqueue(a, part, qrow, b, k + a.lookahead);
+          next = (vq_add(row_ctr(a, b, k + 1), 1u) & 0xFFFFu) == (unsigned)a.n_chunks;
+        }
+        if (!__shfl(next, 0, 64)) return;
+        ++k;
+        continue;
+      }
+    }
+    // the request ends here: after k - 1 kept drafts (rejection) or all K_b;
+    // rows read ahead of it are abandoned (whoever completes one frees it)
+    const int A = rej ? k - 1 : kb;
+    for (int i = A + 1 + lane; i <= a.gamma; i += 64) out[i] = -1;
+    if (lane == 0) {
+      const int last_ahead = min(k - 1 + a.lookahead, kb + 1);
+      for (int j = k + 1; j <= last_ahead; ++j) {
+        unsigned* cj = row_ctr(a, b, j);
+        if ((vq_add(cj, 1u + kVqAbandon) & 0xFFFFu) == (unsigned)a.n_chunks) vq_st(cj, 0u);
+      }
+      int resid = 0;
+      float resid_lt = 0.f;
+      if (rej && !a.greedy) {
+        resid = k;
+        resid_lt = lse_r;
+      } else {
+        int tok = star;                                    // greedy correction, or the bonus draw
+        if ((unsigned)tok >= (unsigned)a.V) {
+          atomicOr(a.err, kErrToken);
+          tok = 0;
+        }
+        out[A] = tok;
+      }
+      a.accept_len[b] = A;
+      a.resid_k[b] = resid;
+      a.resid_lt[b] = resid_lt;
+      __builtin_amdgcn_s_waitcnt(0xF70);                   // outputs stored before the request counts
+      const unsigned d = vq_add(part + 64, 1u);
+      if (d == (unsigned)n_req - 1u) {
+        // the partition's last request: close its tickets; every row slot a
+        // ticket claimed before the close may wait on gets the closing code
+        const unsigned o = __hip_atomic_fetch_or(part, kVqClosed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned tq = vq_ld(part + 32);
+        const unsigned t_end = o & ~kVqClosed;
+        const unsigned hi = t_end > n_init ? (t_end - n_init + a.n_chunks - 1) / a.n_chunks : 0u;
+        const unsigned lim = min(hi, (unsigned)a.qcap);
+        for (unsigned sl = tq; sl < lim; ++sl) vq_st(qrow + kVqSlotStride * sl, kVqClosed);
+        vq_st(part + 96, max(lim, tq));
+      }
+    }
+    return;
+  }
+}
+
+__global__ __launch_bounds__(kRowsThreads) void verify_chain_impl(const VerifyArgs a) {
+  __shared__ RowState red[kRowsThreads / 64];
+  __shared__ unsigned sh[4];
+  __shared__ float s_tx;
+  const int np = a.n_part;
+  const int p = blockIdx.x % np;
+  const int n_req = (a.B - p + np - 1) / np;               // requests p, p + np, ...
+  const unsigned n_init = (unsigned)n_req * a.n_chunks;
+  const int rows = a.B * (a.gamma + 1);
+  unsigned* const part = a.vq + kVqPartWords * p;          // [0] tickets, [32] tail, [64] decided, [96] slots used
+  unsigned* const qrow = a.vq + kVqRows + (size_t)kVqRowStride * rows + (size_t)kVqSlotStride * p * a.qcap;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+
+  if (threadIdx.x == 0) sh[0] = vq_add(part, 1u);
+  __syncthreads();
+  unsigned t = sh[0];
+  __syncthreads();
+  while (!(t & kVqClosed)) {                               // uniform over the block
+    int b, k, chunk;
+    if (t < n_init) {
+      b = p + np * (int)(t / a.n_chunks);
+      k = 1;
+      chunk = (int)(t % a.n_chunks);
+    } else {
+      const unsigned sl = (t - n_init) / a.n_chunks;
+      chunk = (int)((t - n_init) % a.n_chunks);
+      if (threadIdx.x == 0) {
+        unsigned code = 0;
+        if (sl < (unsigned)a.qcap) {
+          const unsigned limit = a.bar_test ? 64u : kVqSpinLimit;
+          unsigned spins = 0;
+          while ((code = a.bar_test ? 0u : vq_ld(qrow + kVqSlotStride * sl)) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > limit) break;
+          }
+        }
+        if (code == 0u) {                                  // gave up (or an impossible slot)
+          atomicOr(a.err, kErrBarrier);
+          vq_st(a.vq + kVqAbort, 1u);
+          code = kVqClosed;
+        }
+        sh[1] = code;
+      }
+      __syncthreads();
+      const unsigned code = sh[1];
+      __syncthreads();
+      if (code == kVqClosed) break;
+      const int r = (int)(code - 1u);
+      b = r / (a.gamma + 1);
+      k = r - b * (a.gamma + 1) + 1;
+    }
+    // the next ticket, claimed while this task streams
+    unsigned nxt = 0;
+    if (threadIdx.x == 0) {
+      nxt = vq_add(part, 1u);
+      if (k == 1 && chunk == 0) {
+        // rows 2 .. lookahead of the request are read ahead from the start
+        const int kb = clamp_k(a.K, b, a.gamma, a.err, false);
+        for (int j = 2; j <= min(a.lookahead, kb + 1); ++j) chain_enqueue(a, part, qrow, b, j);
+      }
+    }
+    chain_task(a, b, k, chunk, red, &s_tx);
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_s_waitcnt(0xF70);                   // this task's partial is stored
+      // a row is complete with its chunks and, after row 1, the previous
+      // row's share (kept: decide it; abandoned: free its counter)
+      unsigned* ctr = row_ctr(a, b, k);
+      const unsigned old = vq_add(ctr, 1u);
+      const unsigned last = (unsigned)a.n_chunks - (k > 1 ? 0u : 1u);
+      const bool complete = (old & 0xFFFFu) == last;
+      if (complete && (old & kVqAbandon)) vq_st(ctr, 0u);
+      sh[2] = complete && !(old & kVqAbandon);
+      sh[0] = nxt;
+    }
+    __syncthreads();
+    if (sh[2] && wid == 0) chain_decide(a, b, k, lane, part, qrow, n_req, n_init);
+    t = sh[0];
+    __syncthreads();
+  }
+  // leave; the last workgroup out clears what the launch used
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    sh[3] = vq_add(a.vq + kVqExit, 1u) == gridDim.x - 1u;
+  }
+  __syncthreads();
+  if (!sh[3]) return;
+  const bool aborted = vq_ld(a.vq + kVqAbort) != 0u;
+  for (int q = 0; q < np; ++q) {
+    unsigned* pq = a.vq + kVqPartWords * q;
+    unsigned* rq = a.vq + kVqRows + (size_t)kVqRowStride * rows + (size_t)kVqSlotStride * q * a.qcap;
+    const unsigned used = aborted ? (unsigned)a.qcap : max(vq_ld(pq + 96), vq_ld(pq + 32));
+    for (unsigned sl = threadIdx.x; sl < used && sl < (unsigned)a.qcap; sl += kRowsThreads)
+      vq_st(rq + kVqSlotStride * sl, 0u);
+  }
+  // rows read ahead of a request's end whose tickets were never claimed keep
+  // a count: every row counter is cleared here
+  for (int r = threadIdx.x; r < rows; r += kRowsThreads) vq_st(a.vq + kVqRows + kVqRowStride * r, 0u);
+  __syncthreads();
+  if (threadIdx.x < np) {
+    unsigned* pq = a.vq + kVqPartWords * threadIdx.x;
+    vq_st(pq, 0u);
+    vq_st(pq + 32, 0u);
+    vq_st(pq + 64, 0u);
+    vq_st(pq + 96, 0u);
+  }
+  if (threadIdx.x == 0) {
+    vq_st(a.vq + kVqAbort, 0u);
+    vq_st(a.vq + kVqExit, 0u);
   }
 }
 
@@ -424,5 +688,6 @@ __global__ __launch_bounds__(64) void rows_lse_impl(const VerifyArgs a) {
 const void* rows_lse_kernel() { return (const void*)&rows_lse_impl; }
 const void* verify_rows_kernel() { return (const void*)&verify_rows_impl; }
 const void* verify_decide_kernel() { return (const void*)&verify_decide_impl; }
+const void* verify_chain_kernel() { return (const void*)&verify_chain_impl; }
 
 }  // namespace dspark
