@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of one DSpark draft/verify step on one MI355X.
 
-One step = dspark_draft_markov (gamma sequential Markov-head positions) ->
-dspark_confidence -> [dspark_schedule] -> dspark_verify, on seeded synthetic
+One step = dspark_draft_markov_conf (gamma sequential Markov-head positions,
+then the confidence head) -> [dspark_schedule] -> dspark_verify, on seeded synthetic
 inputs already resident in HBM.  The headline workload is B=128 requests,
 gamma=7, V=151936, r=256, temperature 1 with the confidence head (d=4096);
 every request verifies all gamma positions, so one step verifies B*gamma
@@ -305,13 +305,18 @@ def main():
 
     def step(i, log=None):
         seed = args.seed ^ i
-        if gru is None:
+        if gru is None and has_conf:
+            # draft and confidence head; the draft's merge runs in the confidence launch
+            ctx.draft_markov_conf(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, seed, G,
+                                  d["h"], d["E"], d["wc"], d["bc"], d.get("sts_T"),
+                                  out=(tok, lse, ytok, conf, surv))
+        elif gru is None:
             ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, seed, G,
                              out=(tok, lse, ytok))
         else:
             ctx.draft_rnn(d["U"], d["W1"], d["W2"], d["gru"], d["req_ids"], T, seed, G,
                           out=(tok, lse, ytok, states))
-        if has_conf:
+        if has_conf and gru is not None:
             ctx.confidence(d["h"], d["E"], d["anchor"], tok, d["wc"], d["bc"], d.get("sts_T"),
                            out=(conf, surv))
         K = None
@@ -466,10 +471,13 @@ def main():
             per_kernel["resid_sweep"]["alg_bytes"] = rb
             per_kernel["resid_sweep"]["rows"] = n_rej
             per_kernel["resid_sweep"]["alg_GBps"] = rb / (per_kernel["resid_sweep"]["avg_us"] * 1e-6) / 1e9
-        if "confidence" in per_kernel:
-            cb = 2.0 * B * G * (wl.d_h + wl.d_e)
-            per_kernel["confidence"]["alg_bytes"] = cb
-            per_kernel["confidence"]["alg_GBps"] = cb / (per_kernel["confidence"]["avg_us"] * 1e-6) / 1e9
+        for name in ("confidence", "conf_merge"):
+            if name in per_kernel:
+                # h rows and gathered E rows (the fused launch also reads the draft's
+                # chunk partials, 24 bytes per request, position and chunk: not counted)
+                cb = 2.0 * B * G * (wl.d_h + wl.d_e)
+                per_kernel[name]["alg_bytes"] = cb
+                per_kernel[name]["alg_GBps"] = cb / (per_kernel[name]["avg_us"] * 1e-6) / 1e9
         for v in per_kernel.values():
             if "alg_GBps" in v:
                 v["frac_hbm"] = v["alg_GBps"] / HBM_PEAK_GBPS

@@ -120,7 +120,8 @@ enum {
   DSPARK_K_STS = 11,           /* temperature fit: the pass of one position */
   DSPARK_K_DRAFT_CHAIN = 12,   /* chained draft: every position in one launch */
   DSPARK_K_VERIFY_CHAIN = 13,  /* verify chain: every needed target row in one launch */
-  DSPARK_K_COUNT = 14
+  DSPARK_K_CONF_MERGE = 14,    /* draft merge + confidences (dspark_draft_markov_conf) */
+  DSPARK_K_COUNT = 15
 };
 int dspark_timing_enable(dspark_ctx* ctx, int enable);
 int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
@@ -269,6 +270,31 @@ int dspark_confidence(dspark_ctx* ctx, hipStream_t stream,
                       const int32_t* anchor, const int32_t* tokens,
                       const void* wc, float bc, const float* sts_T,
                       float* conf, float* surv);
+
+/* Markov-head draft followed by the confidence head, in fewer launches.
+ *
+ * The same results as dspark_draft_markov (tokens, lse, ytok, bit for bit)
+ * then dspark_confidence on those tokens (conf, surv, bit for bit), with the
+ * draft's merge of its chunk partials done by the confidence launch: one
+ * workgroup per (request, position k) merges position k in the draft
+ * combine's order and forms the confidence whose previous token is x_k
+ * (c_{k+1}; c_1 from the anchor in the workgroup of k = gamma), and the
+ * last of a request's workgroups to finish forms its survival products.
+ * One launch fewer per step.  Arguments: those of dspark_draft_markov, then
+ * d_h, d_e, h, E, wc, bc, sts_T as for dspark_confidence, then the outputs
+ * of both; the limits and errors of both apply.  The context keeps a block
+ * of per-request counters (allocated on the first call with a batch larger
+ * than any before, left at zero by every call), so calls that overlap on
+ * one context race, as for the draft's own workspace. */
+int dspark_draft_markov_conf(dspark_ctx* ctx, hipStream_t stream,
+                             int B, int gamma, int V, int r, dspark_dtype wdtype,
+                             const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                             const void* W1, const void* W2, const int32_t* anchor,
+                             const uint32_t* req_ids, float temperature, uint64_t seed,
+                             int d_h, int d_e, const void* h, const void* E,
+                             const void* wc, float bc, const float* sts_T,
+                             int32_t* tokens, float* lse, float* ytok,
+                             float* conf, float* surv);
 
 /* Hardware-aware prefix scheduler: greedy admission with early stop.
  *

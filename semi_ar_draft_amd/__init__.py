@@ -22,13 +22,14 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 
 EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
-    "dspark_draft_markov", "dspark_draft_markov_static", "dspark_draft_rnn", "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
+    "dspark_draft_markov", "dspark_draft_markov_static", "dspark_draft_markov_conf", "dspark_draft_rnn",
+    "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
     "dspark_verify_packed", "dspark_accept_prob", "dspark_sts_fit",
     "dspark_timing_enable", "dspark_timing_read",
 )
 KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
                   "verify_rows", "verify_decide", "resid_sweep", "resid_combine", "gru", "diag", "sts_fit",
-                  "draft_chain", "verify_chain")
+                  "draft_chain", "verify_chain", "conf_merge")
 
 _lib = None
 _vp, _i32, _i64, _u64, _f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
@@ -69,6 +70,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         _vp, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _u64, _vp, _vp, _vp]
     lib.dspark_draft_markov_static.restype = _i32
     lib.dspark_draft_markov_static.argtypes = lib.dspark_draft_markov.argtypes
+    lib.dspark_draft_markov_conf.restype = _i32
+    lib.dspark_draft_markov_conf.argtypes = [
+        _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _f32, _u64,
+        _i32, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.dspark_draft_rnn.restype = _i32
     lib.dspark_draft_rnn.argtypes = [
         _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -226,6 +231,56 @@ class Context:
             _ptr(req_ids), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
             tokens.data_ptr(), lse.data_ptr(), ytok.data_ptr()))
         return tokens, lse, ytok
+
+    # -- dspark_draft_markov_conf ---------------------------------------------
+    def draft_markov_conf(self, U, W1, W2, anchor, req_ids, temperature: float, seed: int, gamma: int,
+                          h, E, wc, bc: float, sts_T=None, out=None, stream=None):
+        """dspark_draft_markov then dspark_confidence on its tokens, with the
+        draft's merge done by the confidence launch.  Returns tokens, lse,
+        ytok, conf, surv."""
+        dev = self.device
+        sb, sk = _logits3(U, "U", dev)
+        B, rows, V = U.shape
+        if rows < gamma:
+            raise ValueError(f"U has {rows} positions, gamma is {gamma}")
+        _need(W1, "W1", None, dev, 2)
+        _need(W2, "W2", W1.dtype, dev, 2)
+        r = W1.shape[1]
+        if W1.shape != (V, r) or W2.shape != (V, r):
+            raise ValueError("W1 and W2 must both be [V][r]")
+        _need(anchor, "anchor", torch.int32, dev, 1)
+        _len(anchor, B, "anchor")
+        if req_ids is not None:
+            _need(req_ids, "req_ids", torch.int32, dev, 1)
+            _len(req_ids, B, "req_ids")
+        _need(h, "h", torch.bfloat16, dev, 3)
+        _need(E, "E", torch.bfloat16, dev, 2)
+        _need(wc, "wc", torch.bfloat16, dev, 1)
+        if tuple(h.shape[:2]) != (B, gamma):
+            raise ValueError("h must be [B][gamma][d_h]")
+        d_h = h.shape[2]
+        if E.shape[0] != V:
+            raise ValueError("E must be [V][d_e]")
+        d_e = E.shape[1]
+        if wc.shape[0] != d_h + d_e:
+            raise ValueError("wc must have d_h + d_e entries")
+        if sts_T is not None:
+            _need(sts_T, "sts_T", torch.float32, dev, 1)
+            _len(sts_T, gamma, "sts_T")
+        if out is None:
+            out = (torch.empty((B, gamma), dtype=torch.int32, device=dev),
+                   torch.empty((B, gamma), dtype=torch.float32, device=dev),
+                   torch.empty((B, gamma), dtype=torch.float32, device=dev),
+                   torch.empty((B, gamma), dtype=torch.float32, device=dev),
+                   torch.empty((B, gamma), dtype=torch.float32, device=dev))
+        tokens, lse, ytok, conf, surv = out
+        self._rc(self.lib.dspark_draft_markov_conf(
+            self._h, _stream(dev, stream), B, gamma, V, r, _wdtype(W1),
+            U.data_ptr(), sb, sk, W1.data_ptr(), W2.data_ptr(), anchor.data_ptr(),
+            _ptr(req_ids), float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF,
+            d_h, d_e, h.data_ptr(), E.data_ptr(), wc.data_ptr(), float(bc), _ptr(sts_T),
+            tokens.data_ptr(), lse.data_ptr(), ytok.data_ptr(), conf.data_ptr(), surv.data_ptr()))
+        return tokens, lse, ytok, conf, surv
 
     # -- dspark_draft_rnn ------------------------------------------------------
     def draft_rnn(self, U, W1, W2, gru: dict, req_ids, temperature: float, seed: int, gamma: int,

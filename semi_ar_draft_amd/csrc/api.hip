@@ -166,6 +166,9 @@ struct dspark_ctx {
   int vchain_wg_per_cu = 0;
   int vchain_wg = 0;              // workgroups per CU of its grid (0: as many as are resident)
   int vchain_ahead = 2;           // rows of a request read ahead of its decisions
+  // per-request counters of dspark_draft_markov_conf (zero between calls)
+  unsigned int* cm_cnt = nullptr;
+  size_t cm_n = 0;
   // draft: running best (key, index) per (position, request), zero between calls
   unsigned long long* best = nullptr;
   size_t best_n = 0;
@@ -251,6 +254,23 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Verify counters (B task counters, then the decided-request counter on its
 // own line): zeroed when (re)allocated; every call leaves them zero.
+int ensure_cm(dspark_ctx* c, size_t n) {
+  if (n <= c->cm_n) return DSPARK_OK;
+  DSPARK_HIP(c, hipDeviceSynchronize());
+  if (c->cm_cnt) (void)hipFree(c->cm_cnt);
+  c->cm_cnt = nullptr;
+  c->cm_n = 0;
+  const size_t m = std::max<size_t>(n, 1024);
+  if (hipMalloc(&c->cm_cnt, m * sizeof(unsigned int)) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(c, DSPARK_ENOMEM, "allocation of %zu bytes failed", m * sizeof(unsigned int));
+  }
+  DSPARK_HIP(c, hipMemset(c->cm_cnt, 0, m * sizeof(unsigned int)));
+  DSPARK_HIP(c, hipDeviceSynchronize());
+  c->cm_n = m;
+  return DSPARK_OK;
+}
+
 int ensure_vq(dspark_ctx* c, size_t words) {
   if (words <= c->vq_n) return DSPARK_OK;
   DSPARK_HIP(c, hipDeviceSynchronize());
@@ -526,7 +546,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
                 const float* U, int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
                 const int32_t* anchor, const GruArgs* gru, const uint32_t* req_ids, float temperature,
                 uint64_t seed, int32_t* tokens, float* lse, float* ytok, float* states,
-                const DraftMem& mem = DraftMem()) {
+                const DraftMem& mem = DraftMem(), CombineArgs* merge_out = nullptr) {
   int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
   if (rc) return rc;
   if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
@@ -624,6 +644,10 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
                             stream)
              : klaunch(c, DSPARK_K_DRAFT_SWEEP, draft_persist_kernel(mode), dim3(c->cu_count), dim3(256), &sa, stream);
     if (rc) return rc;
+    if (merge_out) {                                     // the caller's next launch merges
+      *merge_out = ca;
+      return DSPARK_OK;
+    }
     return klaunch(c, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), &ca, stream);
   }
   if (cfn) {
@@ -638,11 +662,14 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
     const long items = (long)gamma * n_vc * ((B + group_rows - 1) / group_rows);
     const long resident = (long)c->chain_wg_per_cu * c->cu_count;
     const int grid = (int)std::min(std::min(items, resident), (long)kChainMaxGrid);
-    std::vector<KernelNode> nodes(2);
+    std::vector<KernelNode> nodes(merge_out ? 1 : 2);
     set_node(nodes[0], DSPARK_K_DRAFT_CHAIN, cfn, dim3(grid), dim3(64 * c->chain_waves), sa);
-    set_node(nodes[1], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
+    if (merge_out)
+      *merge_out = ca;
+    else
+      set_node(nodes[1], DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
     if (mem.fixed) return run_direct(c, stream, nodes);
-    return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 16, grid, n_vc);
+    return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 16 + (merge_out ? 32 : 0), grid, n_vc);
   }
   const int hs = gru ? 1 : 0;
   const void* kfn = pl.shared ? sweep_kernel((int)wdtype, r, mode, hs ? c->gru_depth : c->draft_depth,
@@ -686,11 +713,16 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
       nodes.push_back(n);
     }
   }
-  KernelNode n;
-  set_node(n, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
-  nodes.push_back(n);
+  if (merge_out) {
+    *merge_out = ca;
+  } else {
+    KernelNode n;
+    set_node(n, DSPARK_K_DRAFT_COMBINE, combine_draft_kernel(), dim3(B, gamma), dim3(256), ca);
+    nodes.push_back(n);
+  }
   if (mem.fixed) return run_direct(c, stream, nodes);
-  return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 4 * hs, pl.grid, pl.n_vc);
+  return run_chain(c, stream, nodes, B, gamma, V, r, (int)wdtype, mode + 4 * hs + (merge_out ? 32 : 0), pl.grid,
+                   pl.n_vc);
 }
 
 int schedule_common(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv, const float* hist,
@@ -1226,6 +1258,7 @@ void dspark_destroy(dspark_ctx* c) {
     if (c->dev_err) (void)hipFree(c->dev_err);
     if (c->chain_flags) (void)hipFree(c->chain_flags);
     if (c->vq) (void)hipFree(c->vq);
+    if (c->cm_cnt) (void)hipFree(c->cm_cnt);
   }
   delete c;
 }
@@ -1331,10 +1364,11 @@ int dspark_draft_rnn(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V,
                      req_ids, temperature, seed, tokens, lse, ytok, states);
 }
 
-int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int d_h, int d_e,
-                      const void* h, const void* E, const int32_t* anchor, const int32_t* tokens,
-                      const void* wc, float bc, const float* sts_T, float* conf, float* surv) {
-  if (!c) return DSPARK_EINVAL;
+namespace {
+
+int check_confidence(dspark_ctx* c, int B, int gamma, int V, int d_h, int d_e, const void* h, const void* E,
+                     const int32_t* anchor, const int32_t* tokens, const void* wc, float bc, float* conf,
+                     float* surv) {
   if (B < 1 || gamma < 1 || gamma > kMaxGamma || V < 1)
     return fail(c, DSPARK_EINVAL, "bad shape B=%d gamma=%d V=%d", B, gamma, V);
   if (d_h < 8 || d_e < 8 || (d_h & 7) || (d_e & 7))
@@ -1344,8 +1378,12 @@ int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V
   if (!aligned16(h) || !aligned16(E) || !aligned16(wc))
     return fail(c, DSPARK_EINVAL, "h, E and wc must be 16-byte aligned");
   if (!std::isfinite(bc)) return fail(c, DSPARK_EINVAL, "bc must be finite");
-  DeviceGuard dg(c->device);
-  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  return DSPARK_OK;
+}
+
+ConfArgs conf_args(dspark_ctx* c, int B, int gamma, int V, int d_h, int d_e, const void* h, const void* E,
+                   const int32_t* anchor, const int32_t* tokens, const void* wc, float bc, const float* sts_T,
+                   float* conf, float* surv) {
   ConfArgs a;
   memset(&a, 0, sizeof(a));
   a.B = B;
@@ -1363,8 +1401,47 @@ int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V
   a.conf = conf;
   a.surv = surv;
   a.err = c->dev_err;
+  return a;
+}
+
+}  // namespace
+
+int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int d_h, int d_e,
+                      const void* h, const void* E, const int32_t* anchor, const int32_t* tokens,
+                      const void* wc, float bc, const float* sts_T, float* conf, float* surv) {
+  if (!c) return DSPARK_EINVAL;
+  int rc = check_confidence(c, B, gamma, V, d_h, d_e, h, E, anchor, tokens, wc, bc, conf, surv);
+  if (rc) return rc;
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  ConfArgs a = conf_args(c, B, gamma, V, d_h, d_e, h, E, anchor, tokens, wc, bc, sts_T, conf, surv);
   // confidences and survival products in one launch, a workgroup per request
   return klaunch(c, DSPARK_K_CONFIDENCE, confidence_kernel(), dim3(B), dim3(1024), &a, stream);
+}
+
+int dspark_draft_markov_conf(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int r,
+                             dspark_dtype wdtype, const float* U, int64_t u_stride_b, int64_t u_stride_k,
+                             const void* W1, const void* W2, const int32_t* anchor, const uint32_t* req_ids,
+                             float temperature, uint64_t seed, int d_h, int d_e, const void* h, const void* E,
+                             const void* wc, float bc, const float* sts_T, int32_t* tokens, float* lse,
+                             float* ytok, float* conf, float* surv) {
+  if (!c) return DSPARK_EINVAL;
+  int rc = check_confidence(c, B, gamma, V, d_h, d_e, h, E, anchor, tokens, wc, bc, conf, surv);
+  if (rc) return rc;
+  CombineArgs m;
+  memset(&m, 0, sizeof(m));
+  if ((rc = draft_chain(c, stream, B, gamma, V, r, wdtype, U, u_stride_b, u_stride_k, W1, W2, anchor, nullptr,
+                        req_ids, temperature, seed, tokens, lse, ytok, nullptr, DraftMem(), &m)))
+    return rc;
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  if ((rc = ensure_cm(c, (size_t)B))) return rc;
+  ConfMergeArgs a;
+  a.m = m;
+  a.f = conf_args(c, B, gamma, V, d_h, d_e, h, E, anchor, tokens, wc, bc, sts_T, conf, surv);
+  a.cnt = c->cm_cnt;
+  // the draft's merge and the confidences, a workgroup per (request, position)
+  return klaunch(c, DSPARK_K_CONF_MERGE, conf_merge_kernel(), dim3(B, gamma), dim3(384), &a, stream);
 }
 
 int dspark_schedule(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv,

@@ -140,6 +140,27 @@ __device__ __forceinline__ T shfl_xor(T v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+// A chunk's draft partial: log-sum-exp state, the leader's key and index, and
+// the tempered logit y at the leader (sampling; greedy: z).
+struct DraftPart {
+  float m, s, key, zb;
+  int idx;
+};
+
+__device__ __forceinline__ void part_merge(DraftPart& a, const DraftPart& b) {
+  softmax_merge(a.m, a.s, b.m, b.s);
+  if (key_beats(b.key, b.idx, a.key, a.idx)) {
+    a.key = b.key;
+    a.idx = b.idx;
+    a.zb = b.zb;
+  }
+}
+
+__device__ __forceinline__ DraftPart part_shfl(const DraftPart& p, int mask) {
+  return DraftPart{shfl_xor(p.m, mask), shfl_xor(p.s, mask), shfl_xor(p.key, mask), shfl_xor(p.zb, mask),
+                   shfl_xor(p.idx, mask)};
+}
+
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
 }

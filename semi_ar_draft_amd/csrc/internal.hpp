@@ -190,6 +190,14 @@ struct ConfArgs {
   int32_t* err;
 };
 
+// The draft's merge of every position's chunk partials (CombineArgs) done by
+// the confidence launch, a workgroup per request (dspark_draft_markov_conf).
+struct ConfMergeArgs {
+  CombineArgs m;
+  ConfArgs f;
+  unsigned int* cnt;             // [B] confidences formed per request, zero at launch and left zero
+};
+
 struct SchedArgs {
   int B, gamma, n_sps;
   const float* surv;
@@ -247,6 +255,7 @@ const void* verify_rows_kernel();
 const void* verify_decide_kernel();
 const void* verify_chain_kernel();
 const void* confidence_kernel();
+const void* conf_merge_kernel();
 // temperature fit: one scoring pass per position (its last workgroup selects)
 const void* sts_hist_kernel(int n_slices, int cells);   // 1..4 slices of 64 candidates per lane
 const void* gru_init_kernel();

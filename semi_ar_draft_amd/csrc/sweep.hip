@@ -1340,25 +1340,6 @@ void draft_persist_impl(const SweepArgs a) {
 
 constexpr int kCombineThreads = 256;
 
-struct DraftPart {
-  float m, s, key, zb;
-  int idx;
-};
-
-__device__ __forceinline__ void part_merge(DraftPart& a, const DraftPart& b) {
-  softmax_merge(a.m, a.s, b.m, b.s);
-  if (key_beats(b.key, b.idx, a.key, a.idx)) {
-    a.key = b.key;
-    a.idx = b.idx;
-    a.zb = b.zb;
-  }
-}
-
-__device__ __forceinline__ DraftPart part_shfl(const DraftPart& p, int mask) {
-  return DraftPart{shfl_xor(p.m, mask), shfl_xor(p.s, mask), shfl_xor(p.key, mask), shfl_xor(p.zb, mask),
-                   shfl_xor(p.idx, mask)};
-}
-
 // One 256-thread workgroup per (request, position), after the whole draft
 // loop: merge the per-chunk partials in a fixed order, write x_k, the
 // log-normaliser and y at x_k, and clear the position's running best (the
