@@ -159,8 +159,9 @@ __global__ __launch_bounds__(kConfMergeThreads) void conf_merge_impl(const ConfM
     } else {
       unsigned long long v = 0ull;
       if (lane < kBestGroups) v = m.best[((int64_t)(k - 1) * kBestGroups + lane) * m.B + b];
+      // over the whole wave: every lane reads its share of the row at x_k
 #pragma unroll
-      for (int mask = 1; mask < kBestGroups; mask <<= 1) {
+      for (int mask = 1; mask < 64; mask <<= 1) {
         const unsigned long long o = __shfl_xor(v, mask, 64);
         v = o > v ? o : v;
       }

@@ -2,7 +2,8 @@
 confidence launch -- against dspark_draft_markov then dspark_confidence:
 tokens, lse, ytok, confidences and survivals bit for bit, through each draft
 path (chained draft, per-position sweeps, whole-draft kernel), sampling and
-greedy, with and without STS temperatures, gamma 1 and 32, one request;
+greedy, with and without STS temperatures, gamma 1 and 32, one request,
+rows of up to 4096 values (the headline width);
 one launch fewer (no draft combine), and a second call on the same context
 (the slot groups, the chained draft's counters and the per-request counters
 are left at zero), also after a call with a larger batch."""
@@ -43,6 +44,10 @@ CASES = [
     ("gamma1", dict(), dict(B=64, gamma=1, V=4096, d_h=64, d_e=64)),
     ("gamma32_greedy", dict(), dict(B=24, gamma=32, V=2048, d_h=32, d_e=64, temperature=0.0, sts=True)),
     ("B1", dict(), dict(B=1, gamma=5, V=3008, d_h=8, d_e=8)),
+    # rows of 4096 values: every lane of a wave reads part of the E row at x_k
+    ("chained_d4096", dict(), dict(B=128, gamma=7, V=16384, d_h=4096, d_e=4096, sts=True)),
+    ("sweeps_B512_d4096", dict(), dict(B=512, gamma=7, V=8192, d_h=4096, d_e=4096, sts=True)),
+    ("whole_draft_d1024", dict(), dict(B=32, gamma=7, V=8192, d_h=1024, d_e=2048)),
 ]
 
 
