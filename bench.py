@@ -353,10 +353,10 @@ def main():
     A = A_log[:args.steps].cpu()
     value = positions / (elapsed_ms / 1e3)
     needed_rows = float(torch.where(A < Ks, A + 1, Ks + 1).sum().item()) / args.steps
-    # rows the verify windows read: the library's windows (rows 1-2, 3, then
+    # rows the verify windows read: the library's windows (rows 1-2, 3-4, then
     # the rest, or DSPARK_VERIFY_WINDOWS) -- a window reads rows lo..min(hi,
     # K_b + 1) of the requests that kept every row before it
-    ends = [int(x) for x in os.environ.get("DSPARK_VERIFY_WINDOWS", "2,3").split(",") if x]
+    ends = [int(x) for x in os.environ.get("DSPARK_VERIFY_WINDOWS", "2,4").split(",") if x]
     ends = [e for e in ends if e < G + 1] + [G + 1]
     read = torch.zeros_like(Ks)
     lo = 1

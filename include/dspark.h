@@ -363,8 +363,9 @@ int dspark_schedule_async(dspark_ctx* ctx, hipStream_t stream,
  * accept_len: int32 [B]; out_tokens: int32 [B][gamma+1].
  * Execution: target rows after a request's first rejection are not read.
  * By default the rows are read in windows (rows 1-2 of every request, then
- * row 3, then the rest, of the requests that kept every draft so far), each
- * a row pass and a decision launch.  DSPARK_VERIFY_CHAIN=1 reads every
+ * rows 3-4, then the rest, of the requests that kept every draft so far),
+ * each a row pass and a decision launch (DSPARK_VERIFY_WINDOWS="e1,e2,..."
+ * sets the last row of each window but the final one).  DSPARK_VERIFY_CHAIN=1 reads every
  * needed row in one launch instead, deciding each request row by row as its
  * rows complete (rows read DSPARK_VERIFY_AHEAD ahead, default 2; V up to
  * 524288); the outputs are identical. */

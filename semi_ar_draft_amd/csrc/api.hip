@@ -148,12 +148,15 @@ struct dspark_ctx {
   // passes (allocated zeroed at the first fit)
   unsigned long long* sts_buf = nullptr;
   // verify: last target row of each window but the final one (window k covers
-  // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list.  Rows 1-2, 3,
-  // then 4..K_b+1: measured steps on the headline batch (gamma 7, mean
-  // acceptance 0.62) 361 us, against 364 for {1-2, 3-4, 5-8}, 367 for
-  // {1, 2-3, 4-8} and 368 for {1-3, 4-8} (each window costs a row pass and
-  // a decision launch)
-  int verify_win[8] = {2, 3, 0, 0, 0, 0, 0, 0};
+  // rows verify_win[k-1]+1 .. verify_win[k]); 0 ends the list.  Rows 1-2,
+  // 3-4, then 5..K_b+1: measured steps on the headline batch (gamma 7, mean
+  // acceptance 0.62), two boxes, alternating runs: 342.4 us against 342.7
+  // for {1-2, 3-5, 6-8}, 345.2 for {1-2, 3, 4-8}, 346.8 for {1-2, 3-4, 5-6,
+  // 7-8}; on another box 355.0 against 358.0 for {1-2, 3, 4-8}, 358.5 for
+  // {1, 2-3, 4-8}, 362 for {1-2, 3-8} and {1-2, 3, 4, 5-8} (each window costs
+  // a row pass and a decision launch; a wider window reads rows that are not
+  // needed)
+  int verify_win[8] = {2, 4, 0, 0, 0, 0, 0, 0};
   // later windows walk a list of the pending requests (else one workgroup per
   // row chunk of every request, most of which find it decided)
   bool verify_list = true;
