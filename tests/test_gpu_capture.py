@@ -3,9 +3,10 @@ a HIP graph after one call of the same shape (so the context's workspace
 exists) replays to the eager result, every replay, with other eager work
 and synchronisations between replays (and two replays back to back) -- for
 the per-position draft path, the chained draft and the whole-draft kernel
-(plain launch; its default cooperative launch is not meant for capture).
-The library records no memset into a graph: every clear it needs is a
-kernel."""
+(plain launch; its default cooperative launch is not meant for capture),
+with the draft and the confidence head as two calls or as the one fused
+call (whose per-request counters every launch leaves at zero).  The library
+records no memset into a graph: every clear it needs is a kernel."""
 import os
 
 import pytest
@@ -25,8 +26,9 @@ ENVS = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
 @pytest.mark.parametrize("B,env", ENVS, ids=["per_position", "chained", "whole_draft"])
-def test_captured_step_replays_to_the_eager_result(B, env):
+def test_captured_step_replays_to_the_eager_result(B, env, fused):
     old = {k: os.environ.get(k) for k in env}
     os.environ.update(env)
     try:
@@ -37,7 +39,7 @@ def test_captured_step_replays_to_the_eager_result(B, env):
                 del os.environ[k]
             else:
                 os.environ[k] = v
-    wl = synth.WORKLOADS["sample"].with_(B=B, V=4096, d_h=32, d_e=32, sts=True)
+    wl = synth.WORKLOADS["sample"].with_(B=B, V=4096, d_h=128 if fused else 32, d_e=1024 if fused else 32, sts=True)
     d = to_dev(synth.make_inputs(wl, seed=71))
     G = wl.gamma
     dev = "cuda"
@@ -51,8 +53,13 @@ def test_captured_step_replays_to_the_eager_result(B, env):
     bufs = (tok, lse, ytok, conf, surv, acc, out)
 
     def step(seed):
-        ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], 1.0, seed, G, out=(tok, lse, ytok))
-        ctx.confidence(d["h"], d["E"], d["anchor"], tok, d["wc"], d["bc"], d["sts_T"], out=(conf, surv))
+        if fused:
+            ctx.draft_markov_conf(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], 1.0, seed, G, d["h"], d["E"],
+                                  d["wc"], d["bc"], d["sts_T"], out=(tok, lse, ytok, conf, surv))
+        else:
+            ctx.draft_markov(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], 1.0, seed, G,
+                             out=(tok, lse, ytok))
+            ctx.confidence(d["h"], d["E"], d["anchor"], tok, d["wc"], d["bc"], d["sts_T"], out=(conf, surv))
         ctx.verify(d["target"], d["U"], d["W1"], d["W2"], d["anchor"], tok, lse, ytok, None, d["req_ids"], 1.0,
                    seed, out=(acc, out))
 
@@ -68,7 +75,7 @@ def test_captured_step_replays_to_the_eager_result(B, env):
             step(5)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        print(f"capturing the step, B={B}, env={env}", flush=True)
+        print(f"capturing the step, B={B}, env={env}, fused={fused}", flush=True)
         with torch.cuda.graph(g, stream=s):
             step(5)
         torch.cuda.synchronize()
