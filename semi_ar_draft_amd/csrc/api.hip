@@ -1431,6 +1431,13 @@ int dspark_draft_markov_conf(dspark_ctx* c, hipStream_t stream, int B, int gamma
   if (!c) return DSPARK_EINVAL;
   int rc = check_confidence(c, B, gamma, V, d_h, d_e, h, E, anchor, tokens, wc, bc, conf, surv);
   if (rc) return rc;
+  {
+    // the counters first: once the draft is enqueued without its combine,
+    // the merge launch below is what leaves the draft's counters at zero
+    DeviceGuard dg(c->device);
+    if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+    if ((rc = ensure_cm(c, (size_t)B))) return rc;
+  }
   CombineArgs m;
   memset(&m, 0, sizeof(m));
   if ((rc = draft_chain(c, stream, B, gamma, V, r, wdtype, U, u_stride_b, u_stride_k, W1, W2, anchor, nullptr,
@@ -1438,7 +1445,6 @@ int dspark_draft_markov_conf(dspark_ctx* c, hipStream_t stream, int B, int gamma
     return rc;
   DeviceGuard dg(c->device);
   if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
-  if ((rc = ensure_cm(c, (size_t)B))) return rc;
   ConfMergeArgs a;
   a.m = m;
   a.f = conf_args(c, B, gamma, V, d_h, d_e, h, E, anchor, tokens, wc, bc, sts_T, conf, surv);
