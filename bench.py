@@ -641,6 +641,11 @@ def main():
         "step_alg_bytes_formula": step_bytes_formula,
         "step_alg_GBps_formula": round(step_bytes_formula / (ms_per_step * 1e-3) / 1e9, 1),
         "accepted_per_step": float(A.sum().item()) / args.steps,
+        # accept lengths of every (timed step, request): entry a counts the
+        # requests that kept exactly a drafts (0 .. gamma), and the same for
+        # the verify lengths K_b the requests were given
+        "accept_hist": [int(x) for x in torch.bincount(A.flatten().long(), minlength=G + 1)[:G + 1]],
+        "verify_len_hist": [int(x) for x in torch.bincount(Ks.flatten().long(), minlength=G + 1)[:G + 1]],
         # accepted drafts and emitted tokens (accepted + one correction or
         # bonus token per request) per second of the timed steps
         "accepted_tokens_per_s": round(float(A.sum().item()) / (elapsed_ms / 1e3), 1),

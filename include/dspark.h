@@ -41,6 +41,10 @@
  *    from dspark_last_error.  Kernels that meet an out-of-range token id or
  *    verify length clamp it and raise a device error flag, reported as
  *    DSPARK_EDEVICE by dspark_check.
+ *  - Tracing: with DSPARK_ROCTX=1 in the environment when the library makes
+ *    its first call, every call below (and dspark_check) is a named host
+ *    range in a profiler's marker trace (roctx, loaded at run time; e.g.
+ *    rocprofv3 --marker-trace).  Without it nothing is loaded.
  */
 #ifndef DSPARK_H
 #define DSPARK_H

@@ -58,7 +58,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{out}")
     tmp = LIB_PATH + ".tmp"
     rc, out = _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC",
-                    *[j[1] for j in jobs], "-o", tmp])
+                    *[j[1] for j in jobs], "-ldl", "-o", tmp])
     if rc != 0:
         raise RuntimeError(f"link failed:\n{out}")
     os.replace(tmp, LIB_PATH)

@@ -1,6 +1,7 @@
 // C ABI of libdspark: context, argument checks, workspace, launch plans
 // (per-position sweeps or, for small batches, the whole-draft kernel) and the
 // HIP-graph cache of the sequential draft loop.
+#include <dlfcn.h>
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -1091,6 +1092,47 @@ int accept_prob_impl(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V,
   return klaunch(c, DSPARK_K_DIAG, combine_alpha_kernel(), dim3(B, gamma), dim3(256), &ca, stream);
 }
 
+// Host trace ranges (roctx) around the entry points, for a profiler's marker
+// trace (rocprofv3 --marker-trace): on when DSPARK_ROCTX=1 is set as the
+// library first makes a call, resolved at run time (no link dependency).
+// Off, a range costs one test of a cached pointer.
+namespace {
+typedef int (*roctx_push_fn)(const char*);
+typedef int (*roctx_pop_fn)();
+struct RoctxApi {
+  roctx_push_fn push = nullptr;
+  roctx_pop_fn pop = nullptr;
+};
+
+RoctxApi roctx_load() {
+  RoctxApi a;
+  const char* e = getenv("DSPARK_ROCTX");
+  if (!e || e[0] != '1') return a;
+  void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+  if (!h) h = dlopen("librocprofiler-sdk-roctx.so", RTLD_NOW | RTLD_LOCAL);
+  if (!h) return a;
+  a.push = reinterpret_cast<roctx_push_fn>(dlsym(h, "roctxRangePushA"));
+  a.pop = reinterpret_cast<roctx_pop_fn>(dlsym(h, "roctxRangePop"));
+  if (!a.push || !a.pop) a = RoctxApi();
+  return a;
+}
+
+const RoctxApi& roctx() {
+  static const RoctxApi a = roctx_load();
+  return a;
+}
+
+struct TraceRange {
+  bool on;
+  explicit TraceRange(const char* name) : on(roctx().push != nullptr) {
+    if (on) roctx().push(name);
+  }
+  ~TraceRange() {
+    if (on) roctx().pop();
+  }
+};
+}  // namespace
+
 extern "C" {
 
 int dspark_version(void) { return kVersion; }
@@ -1269,6 +1311,7 @@ void dspark_destroy(dspark_ctx* c) {
 const char* dspark_last_error(const dspark_ctx* c) { return c ? c->err.c_str() : "null context"; }
 
 int dspark_check(dspark_ctx* c, hipStream_t stream) {
+  TraceRange trace_range("dspark_check");
   if (!c) return DSPARK_EINVAL;
   DeviceGuard dg(c->device);
   if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
@@ -1326,6 +1369,7 @@ int dspark_draft_markov(dspark_ctx* c, hipStream_t stream, int B, int gamma, int
                         dspark_dtype wdtype, const float* U, int64_t u_stride_b, int64_t u_stride_k,
                         const void* W1, const void* W2, const int32_t* anchor, const uint32_t* req_ids,
                         float temperature, uint64_t seed, int32_t* tokens, float* lse, float* ytok) {
+  TraceRange trace_range("dspark_draft_markov");
   if (!c) return DSPARK_EINVAL;
   if (!anchor) return fail(c, DSPARK_EINVAL, "null pointer argument");
   return draft_chain(c, stream, B, gamma, V, r, wdtype, U, u_stride_b, u_stride_k, W1, W2, anchor, nullptr,
@@ -1336,6 +1380,7 @@ int dspark_draft_markov_static(dspark_ctx* c, hipStream_t stream, int B, int gam
                                dspark_dtype wdtype, const float* U, int64_t u_stride_b, int64_t u_stride_k,
                                const void* W1, const void* W2, const int32_t* anchor, const uint32_t* req_ids,
                                float temperature, uint64_t seed, int32_t* tokens, float* lse, float* ytok) {
+  TraceRange trace_range("dspark_draft_markov_static");
   if (!c) return DSPARK_EINVAL;
   if (!anchor) return fail(c, DSPARK_EINVAL, "null pointer argument");
   DraftMem mem;
@@ -1351,6 +1396,7 @@ int dspark_draft_rnn(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V,
                      const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh, const void* s0,
                      const uint32_t* req_ids, float temperature, uint64_t seed, int32_t* tokens, float* lse,
                      float* ytok, float* states) {
+  TraceRange trace_range("dspark_draft_rnn");
   if (!c) return DSPARK_EINVAL;
   if (!W_ih || !W_hh || !b_ih || !b_hh || !s0 || !states)
     return fail(c, DSPARK_EINVAL, "null pointer argument");
@@ -1412,6 +1458,7 @@ ConfArgs conf_args(dspark_ctx* c, int B, int gamma, int V, int d_h, int d_e, con
 int dspark_confidence(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int d_h, int d_e,
                       const void* h, const void* E, const int32_t* anchor, const int32_t* tokens,
                       const void* wc, float bc, const float* sts_T, float* conf, float* surv) {
+  TraceRange trace_range("dspark_confidence");
   if (!c) return DSPARK_EINVAL;
   int rc = check_confidence(c, B, gamma, V, d_h, d_e, h, E, anchor, tokens, wc, bc, conf, surv);
   if (rc) return rc;
@@ -1428,6 +1475,7 @@ int dspark_draft_markov_conf(dspark_ctx* c, hipStream_t stream, int B, int gamma
                              float temperature, uint64_t seed, int d_h, int d_e, const void* h, const void* E,
                              const void* wc, float bc, const float* sts_T, int32_t* tokens, float* lse,
                              float* ytok, float* conf, float* surv) {
+  TraceRange trace_range("dspark_draft_markov_conf");
   if (!c) return DSPARK_EINVAL;
   int rc = check_confidence(c, B, gamma, V, d_h, d_e, h, E, anchor, tokens, wc, bc, conf, surv);
   if (rc) return rc;
@@ -1455,6 +1503,7 @@ int dspark_draft_markov_conf(dspark_ctx* c, hipStream_t stream, int B, int gamma
 
 int dspark_schedule(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv,
                     const float* sps, int n_sps, int32_t* K, int32_t* n_selected, double* theta) {
+  TraceRange trace_range("dspark_schedule");
   if (!c) return DSPARK_EINVAL;
   return schedule_common(c, stream, B, gamma, surv, nullptr, sps, n_sps, K, n_selected, theta);
 }
@@ -1462,6 +1511,7 @@ int dspark_schedule(dspark_ctx* c, hipStream_t stream, int B, int gamma, const f
 int dspark_schedule_async(dspark_ctx* c, hipStream_t stream, int B, int gamma, const float* surv,
                           const float* surv_hist, const float* sps, int n_sps, int32_t* K, int32_t* n_selected,
                           double* theta) {
+  TraceRange trace_range("dspark_schedule_async");
   if (!c) return DSPARK_EINVAL;
   if (!surv_hist) return fail(c, DSPARK_EINVAL, "null pointer argument");
   return schedule_common(c, stream, B, gamma, surv, surv_hist, sps, n_sps, K, n_selected, theta);
@@ -1473,6 +1523,7 @@ int dspark_verify(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, in
                   const int32_t* anchor, const int32_t* tokens, const float* lse, const float* ytok,
                   const float* states, const int32_t* K, const uint32_t* req_ids, float temperature,
                   uint64_t seed, int32_t* accept_len, int32_t* out_tokens) {
+  TraceRange trace_range("dspark_verify");
   if (!c) return DSPARK_EINVAL;
   return verify_common(c, stream, B, gamma, V, r, wdtype, target, t_stride_b, t_stride_k, nullptr, 0, U, u_stride_b,
                        u_stride_k, W1, W2, anchor, tokens, lse, ytok, states, K, req_ids, temperature, seed,
@@ -1484,6 +1535,7 @@ int dspark_accept_prob(dspark_ctx* c, hipStream_t stream, int B, int gamma, int 
                        int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
                        const int32_t* anchor, const int32_t* tokens, const float* lse, const float* states,
                        float temperature, float* alpha) {
+  TraceRange trace_range("dspark_accept_prob");
   if (!c) return DSPARK_EINVAL;
   return accept_prob_impl(c, stream, B, gamma, V, r, wdtype, target, t_stride_b, t_stride_k, U, u_stride_b,
                           u_stride_k, W1, W2, anchor, tokens, lse, states, temperature, alpha);
@@ -1495,6 +1547,7 @@ int dspark_verify_packed(dspark_ctx* c, hipStream_t stream, int B, int gamma, in
                          const int32_t* anchor, const int32_t* tokens, const float* lse, const float* ytok,
                          const float* states, const int32_t* K, const uint32_t* req_ids, float temperature,
                          uint64_t seed, int32_t* accept_len, int32_t* out_tokens) {
+  TraceRange trace_range("dspark_verify_packed");
   if (!c) return DSPARK_EINVAL;
   if (!t_offsets || !K) return fail(c, DSPARK_EINVAL, "the packed layout needs t_offsets and K");
   if (n_rows < 1) return fail(c, DSPARK_EINVAL, "n_rows must be >= 1");
@@ -1506,6 +1559,7 @@ int dspark_verify_packed(dspark_ctx* c, hipStream_t stream, int B, int gamma, in
 int dspark_sts_fit(dspark_ctx* c, hipStream_t stream, int64_t N, int gamma, const float* logit, int64_t stride,
                    const int32_t* accept_len, const float* grid, int n_grid, int n_bins, float* T, int32_t* index,
                    double* ece) {
+  TraceRange trace_range("dspark_sts_fit");
   if (!c) return DSPARK_EINVAL;
   if (N < 0 || gamma < 1 || gamma > kMaxGamma)
     return fail(c, DSPARK_EINVAL, "bad shape N=%lld gamma=%d", (long long)N, gamma);
