@@ -109,3 +109,44 @@ def test_smallest_vocabulary_single_tile(ctx):
         if ov.margin.min() > 1e-4 and ov.final_margin.min() > 1e-4:
             assert np.array_equal(acc.cpu().numpy(), ov.accept_len)
             assert np.array_equal(out.cpu().numpy(), ov.out_tokens)
+
+
+def test_empty_batch_and_gamma_out_of_range_are_refused(ctx, small):
+    """An empty batch (B = 0) and gamma outside 1..32 are argument errors of
+    every call, refused on the host before anything is enqueued."""
+    wl, d = small
+    lib = dk.load_library()
+    B, R, V = d["U"].shape
+    G = wl.gamma
+    i32 = torch.zeros((B, 33), dtype=torch.int32, device="cuda")
+    f32 = torch.zeros((B, 33), device="cuda")
+    draft_args = lambda b, g: (ctx._h, None, b, g, V, wl.r, dk.DSPARK_BF16, d["U"].data_ptr(), R * V, V,
+                               d["W1"].data_ptr(), d["W2"].data_ptr(), d["anchor"].data_ptr(), None, 1.0, 0)
+    for b, g in ((0, G), (B, 0), (B, 33), (-1, G)):
+        assert lib.dspark_draft_markov(*draft_args(b, g), i32.data_ptr(), f32.data_ptr(),
+                                       f32.data_ptr()) == dk.DSPARK_EINVAL, (b, g)
+        assert lib.dspark_draft_markov_static(*draft_args(b, g), i32.data_ptr(), f32.data_ptr(),
+                                              f32.data_ptr()) == dk.DSPARK_EINVAL, (b, g)
+    h = torch.zeros((B, G, 16), dtype=torch.bfloat16, device="cuda")
+    E = torch.zeros((V, 16), dtype=torch.bfloat16, device="cuda")
+    wc = torch.zeros(32, dtype=torch.bfloat16, device="cuda")
+    for b, g in ((0, G), (B, 0), (B, 33)):
+        assert lib.dspark_confidence(ctx._h, None, b, g, V, 16, 16, h.data_ptr(), E.data_ptr(),
+                                     d["anchor"].data_ptr(), i32.data_ptr(), wc.data_ptr(), 0.0, None,
+                                     f32.data_ptr(), f32.data_ptr()) == dk.DSPARK_EINVAL, (b, g)
+        assert lib.dspark_draft_markov_conf(*draft_args(b, g), 16, 16, h.data_ptr(), E.data_ptr(),
+                                            wc.data_ptr(), 0.0, None, i32.data_ptr(), f32.data_ptr(),
+                                            f32.data_ptr(), f32.data_ptr(), f32.data_ptr()) == dk.DSPARK_EINVAL
+        assert lib.dspark_verify(ctx._h, None, b, g, V, wl.r, dk.DSPARK_BF16, d["target"].data_ptr(),
+                                 d["target"].stride(0), d["target"].stride(1), d["U"].data_ptr(), R * V, V,
+                                 d["W1"].data_ptr(), d["W2"].data_ptr(), d["anchor"].data_ptr(),
+                                 i32.data_ptr(), f32.data_ptr(), f32.data_ptr(), None, None, None, 1.0, 0,
+                                 i32.data_ptr(), i32.data_ptr()) == dk.DSPARK_EINVAL, (b, g)
+    sps = torch.ones(4096, device="cuda")
+    K = torch.zeros(B, dtype=torch.int32, device="cuda")
+    n = torch.zeros(1, dtype=torch.int32, device="cuda")
+    th = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for b, g in ((0, G), (B, 0), (B, 33)):
+        assert lib.dspark_schedule(ctx._h, None, b, g, f32.data_ptr(), sps.data_ptr(), 4096, K.data_ptr(),
+                                   n.data_ptr(), th.data_ptr()) == dk.DSPARK_EINVAL, (b, g)
+    ctx.check()   # nothing was enqueued
