@@ -181,7 +181,11 @@ int dspark_timing_read(dspark_ctx* ctx, double* ms, int* launches);
  *    unit that keeps W2 in registers and separates positions with a grid
  *    barrier.  Its workgroups must all be resident to pass a barrier, so by
  *    default it is launched cooperatively (co-residency guaranteed by the
- *    runtime, also when other streams run kernels; ~15 us more per call).
+ *    runtime, also when other streams run kernels; ~20-25 us more per
+ *    call).  When the runtime refuses the cooperative launch (it does while
+ *    another process on the device holds its cooperative-launch resource),
+ *    that call runs on the per-position sweeps instead, with the same
+ *    greedy tokens; the next call tries the whole-draft kernel again.
  *    DSPARK_PERSIST_COOP=0 launches it plainly, for callers that own an
  *    otherwise idle device: there, if concurrent kernels hold compute units,
  *    the waiting workgroups start as those kernels finish, and two such

@@ -108,9 +108,12 @@ struct dspark_ctx {
   int persist_max_b = 48;
   int coop = -1;
   // launch it cooperatively (co-residency guaranteed by the runtime, also
-  // under concurrent kernels; ~15 us more per call here); false: a plain
+  // under concurrent kernels; ~20-25 us more per call here); false: a plain
   // launch of one workgroup per CU, for callers that own an idle device
   bool persist_coop = true;
+  // cooperative launches the runtime refused (each such call ran on the
+  // per-position sweeps instead)
+  long coop_refused = 0;
   int bar_test = 0;               // failure injection (tests): barriers time out
   unsigned int* bar = nullptr;    // its grid barrier counter (inside dev_err's block)
   // chained draft kernel (Markov head, bf16, r in {128, 256}, one request quad
@@ -373,17 +376,31 @@ hipError_t take_event(dspark_ctx* c, hipEvent_t* e) {
 // Cooperative launch (every workgroup resident at once); while timing is
 // enabled it is bracketed by stream events (no dispatch-attached events for
 // this launch type), which include the queue's ordering gap before it.
+// A launch the runtime refuses (e.g. while another process holds the
+// device's cooperative-launch resource) returns kCoopRefused with nothing
+// of the kernel enqueued and the HIP error cleared; the caller takes
+// another path.
+constexpr int kCoopRefused = -1;
+
 int klaunch_coop(dspark_ctx* c, int cls, const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t s) {
   void* params[] = {arg};
   if (!c->timing) {
-    DSPARK_HIP(c, hipLaunchCooperativeKernel(fn, grid, block, params, 0, s));
+    if (hipLaunchCooperativeKernel(fn, grid, block, params, 0, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return kCoopRefused;
+    }
     return DSPARK_OK;
   }
   hipEvent_t a, b;
   DSPARK_HIP(c, take_event(c, &a));
   DSPARK_HIP(c, take_event(c, &b));
   DSPARK_HIP(c, hipEventRecord(a, s));
-  DSPARK_HIP(c, hipLaunchCooperativeKernel(fn, grid, block, params, 0, s));
+  if (hipLaunchCooperativeKernel(fn, grid, block, params, 0, s) != hipSuccess) {
+    (void)hipGetLastError();
+    c->ev_free.push_back(a);                             // recorded, never read: reusable
+    c->ev_free.push_back(b);
+    return kCoopRefused;
+  }
   DSPARK_HIP(c, hipEventRecord(b, s));
   c->pending.push_back({cls, a, b});
   return DSPARK_OK;
@@ -550,7 +567,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
                 const float* U, int64_t u_stride_b, int64_t u_stride_k, const void* W1, const void* W2,
                 const int32_t* anchor, const GruArgs* gru, const uint32_t* req_ids, float temperature,
                 uint64_t seed, int32_t* tokens, float* lse, float* ytok, float* states,
-                const DraftMem& mem = DraftMem(), CombineArgs* merge_out = nullptr) {
+                const DraftMem& mem = DraftMem(), CombineArgs* merge_out = nullptr, bool allow_persist = true) {
   int rc = check_markov_shape(c, B, gamma, V, r, (int)wdtype, temperature);
   if (rc) return rc;
   if ((rc = check_stream_rows(c, "U", U, u_stride_b, u_stride_k, B, gamma, V))) return rc;
@@ -562,7 +579,7 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
   const bool greedy = temperature == 0.0f;
   const int mode = greedy ? kModeDraftGreedy : kModeDraftSample;
   const SweepPlan pl = plan_sweep(c, B, V, r, (int)wdtype);
-  const bool persist = !gru && !mem.fixed && use_persist(c, B, V, r, (int)wdtype);
+  const bool persist = allow_persist && !gru && !mem.fixed && use_persist(c, B, V, r, (int)wdtype);
   const void* cfn = (gru || persist) ? nullptr : chain_kernel_for(c, B, r, (int)wdtype, mode);
   const int chain_vc = c->chain_chunks > 0 ? c->chain_chunks : c->chain_wg_per_cu * c->cu_count;
   const int n_vc = persist ? kWavesPerBlock * c->cu_count
@@ -647,6 +664,13 @@ int draft_chain(dspark_ctx* c, hipStream_t stream, int B, int gamma, int V, int 
              ? klaunch_coop(c, DSPARK_K_DRAFT_SWEEP, draft_persist_kernel(mode), dim3(c->cu_count), dim3(256), &sa,
                             stream)
              : klaunch(c, DSPARK_K_DRAFT_SWEEP, draft_persist_kernel(mode), dim3(c->cu_count), dim3(256), &sa, stream);
+    if (rc == kCoopRefused) {
+      // cooperative launch refused, nothing enqueued: this call runs on the
+      // per-position sweeps (the next call tries the whole-draft kernel again)
+      ++c->coop_refused;
+      return draft_chain(c, stream, B, gamma, V, r, wdtype, U, u_stride_b, u_stride_k, W1, W2, anchor, gru,
+                         req_ids, temperature, seed, tokens, lse, ytok, states, mem, merge_out, false);
+    }
     if (rc) return rc;
     if (merge_out) {                                     // the caller's next launch merges
       *merge_out = ca;

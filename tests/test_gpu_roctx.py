@@ -17,7 +17,7 @@ import sys, torch
 sys.path.insert(0, "tests")
 import synth, semi_ar_draft_amd as dk
 from test_gpu_parity import to_dev
-wl = synth.WORKLOADS["sample"].with_(B=24, V=4096, d_h=64, d_e=256)
+wl = synth.WORKLOADS["sample"].with_(B=64, V=4096, d_h=64, d_e=256)   # not the cooperative path
 d = to_dev(synth.make_inputs(wl, seed=3))
 with dk.Context(0) as ctx:
     tok, lse, ytok, conf, surv = ctx.draft_markov_conf(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"],
