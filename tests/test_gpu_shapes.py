@@ -6,7 +6,9 @@ positions, ragged vocabularies (any multiple of 16), every supported rank,
 both weight types, greedy and several temperatures, with and without the
 confidence head.  bf16 cases with r = 256 and B <= 128 also run with the
 whole-draft kernel forced on (DSPARK_PERSIST=2), so both draft paths meet
-the same cases.
+the same cases.  Cases with the confidence head also run the fused draft +
+confidence call, which must give the two calls' outputs bit for bit (its
+embedding rows of 1024 values keep every lane of a wave busy).
 """
 import os
 
@@ -62,7 +64,7 @@ def pctx():
 @pytest.mark.parametrize("name,over,vary_k", CASES, ids=[c[0] for c in CASES])
 def test_shape(ctx, pctx, name, over, vary_k):
     base = "sample" if over["wdtype"] == "bf16" else "tiny"
-    wl = synth.WORKLOADS[base].with_(**over, d_h=32, d_e=48, peak=None,
+    wl = synth.WORKLOADS[base].with_(**over, d_h=32, d_e=1024, peak=None,
                                       u_std=3.0 if over["wdtype"] == "bf16" else 2.0)
     inp = synth.make_inputs(wl, seed=wl.seed + 101)
     d = to_dev(inp)
@@ -74,6 +76,12 @@ def test_shape(ctx, pctx, name, over, vary_k):
     Kd = None if K is None else torch.from_numpy(K).cuda()
     g = gpu_step(ctx, d, seed=555, K=Kd)
     check_chain(g, inp, 555, K=K)
+    if wl.conf:
+        f = ctx.draft_markov_conf(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], d["temperature"], 555,
+                                  wl.gamma, d["h"], d["E"], d["wc"], d["bc"], d.get("sts_T"))
+        ctx.check()
+        for key, x in zip(("tok", "lse", "ytok", "conf", "surv"), f):
+            assert np.array_equal(x.cpu().numpy(), g[key]), key
     if wl.wdtype == "bf16" and wl.r == 256 and wl.B <= 128 and wl.gamma > 1:
         g2 = gpu_step(pctx, d, seed=555, K=Kd)
         check_chain(g2, inp, 555, K=K)
