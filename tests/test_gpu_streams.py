@@ -3,7 +3,8 @@ between contexts.  The full step on a side stream equals the same step on
 the default stream bit for bit; two contexts used in turn on one stream (the
 whole-draft kernel, whose barrier counter is per context) equal one context;
 two contexts running the per-position path on two streams at once equal the
-same calls run one after the other.  (Two whole-draft launches at once are
+same calls run one after the other, and so do two contexts running the fused
+draft + confidence call (chained draft) on two streams at once.  (Two whole-draft launches at once are
 not run: their workgroups may not all be resident together, which the
 library documents.)"""
 import os
@@ -91,6 +92,37 @@ def test_two_contexts_on_two_streams_at_once():
                 acc, out = ctx.verify(d["target"], d["U"], d["W1"], d["W2"], d["anchor"], tok, lse, ytok, None,
                                       d["req_ids"], d["temperature"], seed)
             res.append(dict(tok=tok, lse=lse, ytok=ytok, conf=conf, surv=surv, acc=acc, out=out))
+        s1.synchronize()
+        s2.synchronize()
+        c1.check(s1)
+        c2.check(s2)
+    finally:
+        c1.close()
+        c2.close()
+    for want, got in ((r1, res[0]), (r2, res[1])):
+        for k, v in got.items():
+            assert np.array_equal(want[k], v.cpu().numpy()), k
+
+
+def test_fused_call_on_two_streams_at_once():
+    """The fused draft + confidence call of two contexts on two streams at
+    once (each context has its own per-request counters) equals the two
+    calls run one after the other on the default stream."""
+    wl = synth.WORKLOADS["sample"].with_(B=100, V=6144, d_h=64, d_e=1024, sts=True)
+    i1 = to_dev(synth.make_inputs(wl, seed=65))
+    i2 = to_dev(synth.make_inputs(wl, seed=66))
+    c1, c2 = _ctx(), _ctx()
+    try:
+        r1 = gpu_step(c1, i1, seed=13)
+        r2 = gpu_step(c2, i2, seed=14)
+        torch.cuda.synchronize()
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        res = []
+        for ctx, d, s, seed in ((c1, i1, s1, 13), (c2, i2, s2, 14)):
+            with torch.cuda.stream(s):
+                f = ctx.draft_markov_conf(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], d["temperature"], seed,
+                                          wl.gamma, d["h"], d["E"], d["wc"], d["bc"], d.get("sts_T"))
+            res.append(dict(zip(("tok", "lse", "ytok", "conf", "surv"), f)))
         s1.synchronize()
         s2.synchronize()
         c1.check(s1)
