@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--sts-fit", action="store_true",
                     help="time the per-position temperature fit on a held-out set of 2^20 drafts "
                          "(gamma 7, 64 candidates, 15 bins) instead of the step benchmark; one JSON line")
+    ap.add_argument("--verify-layout", action="store_true",
+                    help="time one verify call with the target padded to gamma + 1 rows per request against "
+                         "the same call with the target rows packed end to end (scheduled workload, K_b from "
+                         "the GPU scheduler) instead of the step benchmark; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer a few times: the reference kernel of known "
                          "traffic used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -203,6 +207,97 @@ def sts_fit_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def verify_layout_bench(args):
+    """Verification of the scheduled workload (B = 512, gamma = 7, V = 129280)
+    with the target padded to gamma + 1 rows per request (dspark_verify)
+    against the same call on the target rows 1 .. K_b + 1 packed end to end
+    (dspark_verify_packed).  One draft + confidence + schedule gives the
+    tokens and K_b; the packed copy is made outside the timed region; the
+    two layouts are timed in alternating blocks of calls on the same inputs
+    and seed, and their outputs must agree exactly.  value = the packed
+    call's time."""
+    import torch
+    import synth
+    import semi_ar_draft_amd as dk
+
+    wl = synth.WORKLOADS["sched"]
+    inp = synth.make_inputs(wl)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    B, G, V = wl.B, wl.gamma, wl.V
+    dev = torch.device("cuda", 0)
+    ctx = dk.Context(0)
+    tok = torch.empty((B, G), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, G), dtype=torch.float32, device=dev)
+    ytok = torch.empty((B, G), dtype=torch.float32, device=dev)
+    conf = torch.empty((B, G), dtype=torch.float32, device=dev)
+    surv = torch.empty((B, G), dtype=torch.float32, device=dev)
+    K = torch.empty((B,), dtype=torch.int32, device=dev)
+    nsel = torch.empty((1,), dtype=torch.int32, device=dev)
+    theta = torch.empty((1,), dtype=torch.float64, device=dev)
+    T, seed = d["temperature"], args.seed
+    ctx.draft_markov_conf(d["U"], d["W1"], d["W2"], d["anchor"], d["req_ids"], T, seed, G, d["h"], d["E"],
+                          d["wc"], d["bc"], d.get("sts_T"), out=(tok, lse, ytok, conf, surv))
+    ctx.schedule(surv, d["sps"], out=(K, nsel, theta))
+    ctx.check()
+    # rows 1 .. K_b + 1 of every request, in request order
+    Kc = K.cpu().to(torch.int64)
+    offs = torch.zeros(B, dtype=torch.int64)
+    offs[1:] = torch.cumsum(Kc + 1, 0)[:-1]
+    n_rows = int((Kc + 1).sum().item())
+    flat = torch.cat([b * (G + 1) + torch.arange(int(Kc[b]) + 1) for b in range(B)]).to(dev)
+    packed = d["target"].reshape(B * (G + 1), V).index_select(0, flat).contiguous()
+    toffs = offs.to(torch.int32).to(dev)
+    torch.cuda.synchronize()
+    outs = {m: (torch.empty((B,), dtype=torch.int32, device=dev),
+                torch.empty((B, G + 1), dtype=torch.int32, device=dev)) for m in ("padded", "packed")}
+
+    def call(m):
+        if m == "padded":
+            ctx.verify(d["target"], d["U"], d["W1"], d["W2"], d["anchor"], tok, lse, ytok, K, d["req_ids"], T,
+                       seed, out=outs[m])
+        else:
+            ctx.verify_packed(packed, toffs, d["U"], d["W1"], d["W2"], d["anchor"], tok, lse, ytok, K,
+                              d["req_ids"], T, seed, out=outs[m])
+
+    n, rounds = max(args.steps, 1), 3
+    for m in ("padded", "packed"):
+        for _ in range(max(args.warmup, 1)):
+            call(m)
+    ctx.check()
+    torch.cuda.synchronize()
+    us = {"padded": [], "packed": []}
+    for _ in range(rounds):
+        for m in ("padded", "packed"):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                call(m)
+            e1.record()
+            torch.cuda.synchronize()
+            us[m].append(1e3 * e0.elapsed_time(e1) / n)
+    ctx.check()
+    same = all(torch.equal(a, b) for a, b in zip(outs["padded"], outs["packed"]))
+    A = outs["packed"][0].cpu().to(torch.int64)
+    needed = int(torch.where(A < Kc, A + 1, Kc + 1).sum().item())
+    line = {
+        "metric": "verify call time, target rows packed end to end (padded layout beside it)",
+        "value": min(us["packed"]), "unit": "us per verify call", "n_gpus": 1, "steps": n * rounds,
+        "warmup": max(args.warmup, 1), "ms_per_step": min(us["packed"]) / 1e3, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "sched: B=512 gamma=7 V=129280 r=256 T=1, K_b from the GPU scheduler",
+                   "B": B, "gamma": G, "V": V},
+        "padded_us": [round(x, 2) for x in us["padded"]], "packed_us": [round(x, 2) for x in us["packed"]],
+        "K_sum": int(Kc.sum().item()), "packed_rows": n_rows, "padded_rows": B * (G + 1),
+        "needed_rows": needed, "packed_target_bytes": 4 * n_rows * V, "padded_target_bytes": 4 * B * (G + 1) * V,
+        "outputs_identical": same,
+    }
+    ctx.close()
+    print(json.dumps(line), flush=True)
+    if not same:
+        sys.exit(1)
+
+
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "draft_chain_traffic_B128_V151936_r256_T1.json")
 
@@ -257,6 +352,12 @@ def main():
         return
     if args.draft_crossover:
         draft_crossover(args.seed)
+        return
+    if args.verify_layout:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        verify_layout_bench(args)
         return
     if args.sts_fit:
         if args.gpus != 1:

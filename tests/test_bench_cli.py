@@ -23,3 +23,11 @@ def test_sweep_bytes_formula():
     assert bench.sweep_bytes(128, 151936, 256, 2) == 155_648_000
     # GRU head: the fp32 states replace the W1 rows
     assert bench.sweep_bytes(256, 151936, 256, 2, 4) == 4 * 256 * 151936 + 2 * 256 * 151936 + 4 * 256 * 256
+
+
+def test_measurement_modes_refuse_more_than_one_gpu():
+    for mode in ("--verify-layout", "--sts-fit"):
+        p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), mode, "--gpus", "2"],
+                           capture_output=True, text=True, timeout=120)
+        assert p.returncode == 2, mode
+        assert "one GPU" in p.stderr
