@@ -57,6 +57,10 @@ def parse():
                     help="time one verify call with the target padded to gamma + 1 rows per request against "
                          "the same call with the target rows packed end to end (scheduled workload, K_b from "
                          "the GPU scheduler) instead of the step benchmark; one JSON line")
+    ap.add_argument("--schedule", action="store_true",
+                    help="time the synchronous and asynchronous prefix schedulers over batch sizes (gamma 7, "
+                         "4096-entry SPS table), each checked against the oracle, instead of the step "
+                         "benchmark; one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB buffer a few times: the reference kernel of known "
                          "traffic used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -298,6 +302,87 @@ def verify_layout_bench(args):
         sys.exit(1)
 
 
+def schedule_bench(args):
+    """The prefix schedulers alone: dspark_schedule (synchronous, early stop)
+    and dspark_schedule_async (capacity from survivals of an earlier step,
+    global search) on synthetic survival rows (each row gamma = 7 sorted
+    uniforms) and the 4096-entry SPS table of the scheduled workload, over
+    batch sizes up to the library's B * gamma <= 4096.  Each size is first
+    checked against the oracle (K, n exact, theta to 1e-12), then timed over
+    a block of calls between events.  value = the synchronous call at
+    B = 512 (the scheduled workload)."""
+    import numpy as np
+    import torch
+    import synth
+    import oracle
+    import semi_ar_draft_amd as dk
+
+    G = 7
+    sps = synth.sps_table(4096)
+    sps_d = sps.cuda()
+    ctx = dk.Context(0)
+    n = max(args.steps, 1)
+    rows, ok = [], True
+    for B in (128, 512, 585):
+        surv = synth.survival_rows(B, G, seed=900 + B)
+        hist = synth.survival_rows(B, G, seed=1900 + B)
+        sd, hd = surv.cuda(), hist.cuda()
+        out = (torch.empty((B,), dtype=torch.int32, device="cuda"), torch.empty((1,), dtype=torch.int32, device="cuda"),
+               torch.empty((1,), dtype=torch.float64, device="cuda"))
+        rec = {"B": B, "gamma": G}
+        for mode in ("sync", "async"):
+            def call():
+                if mode == "sync":
+                    ctx.schedule(sd, sps_d, out=out)
+                else:
+                    ctx.schedule_async(sd, hd, sps_d, out=out)
+            call()
+            ctx.check()
+            cpu_s = float("inf")
+            for _ in range(3):                                 # the fastest of three oracle calls
+                t0 = time.perf_counter()
+                ref = oracle.schedule(surv.numpy(), sps.numpy()) if mode == "sync" else \
+                    oracle.schedule_async(surv.numpy(), hist.numpy(), sps.numpy())
+                cpu_s = min(cpu_s, time.perf_counter() - t0)
+            same = (np.array_equal(out[0].cpu().numpy().astype(np.int64), ref.K)
+                    and int(out[1].item()) == ref.n_selected
+                    and abs(float(out[2].item()) - ref.theta) <= 1e-12 * abs(ref.theta))
+            ok = ok and same
+            for _ in range(max(args.warmup, 1)):
+                call()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            ctx.check()
+            rec[mode] = {"us_per_call": round(1e3 * e0.elapsed_time(e1) / n, 2), "n_selected": ref.n_selected,
+                         "matches_oracle": same, "oracle_ms_per_call": round(1e3 * cpu_s, 2)}
+        rows.append(rec)
+        print(f"[bench] schedule B={B}: sync {rec['sync']['us_per_call']} us, async {rec['async']['us_per_call']} us",
+              file=sys.stderr, flush=True)
+    ctx.close()
+    v = next(r for r in rows if r["B"] == 512)["sync"]["us_per_call"]
+    line = {
+        "metric": "prefix scheduler call time (B x gamma candidates, 4096-entry SPS table)",
+        "value": v, "unit": "us per call", "n_gpus": 1, "steps": n, "warmup": max(args.warmup, 1),
+        "ms_per_step": v / 1e3, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 survivals, f64 scan", "data": "synthetic",
+        "config": {"workload": "schedule: gamma=7, SPS 4096 entries, B in {128, 512, 585}", "gamma": G},
+        "sizes": rows,
+        "cpu_baseline": {"value": next(r for r in rows if r["B"] == 512)["sync"]["oracle_ms_per_call"] * 1e3,
+                         "unit": "us per call", "cores": 1, "kind": "oracle",
+                         "sample": "one synchronous call at B = 512 on the same input, fastest of three"},
+        "parity_ok": ok,
+    }
+    print(json.dumps(line), flush=True)
+    if not ok:
+        sys.exit(1)
+
+
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "draft_chain_traffic_B128_V151936_r256_T1.json")
 
@@ -352,6 +437,12 @@ def main():
         return
     if args.draft_crossover:
         draft_crossover(args.seed)
+        return
+    if args.schedule:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        schedule_bench(args)
         return
     if args.verify_layout:
         if args.gpus != 1:

@@ -26,7 +26,7 @@ def test_sweep_bytes_formula():
 
 
 def test_measurement_modes_refuse_more_than_one_gpu():
-    for mode in ("--verify-layout", "--sts-fit"):
+    for mode in ("--verify-layout", "--sts-fit", "--schedule"):
         p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), mode, "--gpus", "2"],
                            capture_output=True, text=True, timeout=120)
         assert p.returncode == 2, mode
