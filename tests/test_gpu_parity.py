@@ -97,6 +97,11 @@ SMALL = [
     ("bf16_greedy_gamma32", "greedy", dict(B=20, gamma=32, V=1056, r=32, peak=None)),
     # shared-tile sweeps (B > 64) with a long draft and a ragged last chunk
     ("bf16_sample_shared_gamma16", "sample", dict(B=100, gamma=16, V=2064, d_h=32, d_e=32, sts=True)),
+    # large vocabularies: 2^18 entries through the chained draft (32 verify
+    # chunks per row), and 256000 entries past what the whole-draft kernel's
+    # register tiles cover (the per-position sweeps; a ragged last verify chunk)
+    ("bf16_sample_V262144_chained", "sample", dict(B=70, gamma=2, V=262144, d_h=32, d_e=32)),
+    ("bf16_greedy_V256000", "greedy", dict(B=12, gamma=3, V=256000, peak=None)),
 ]
 
 
