@@ -383,6 +383,31 @@ def schedule_bench(args):
         sys.exit(1)
 
 
+def stream_read_peak(ctx, n_bytes: int = 1 << 30, reps: int = 10) -> float:
+    """Read bandwidth (GB/s) of the library's streaming-read calibration over
+    a buffer four times the 256 MB last-level cache, so that every pass
+    reads from HBM; each call also runs its one-workgroup sum of the
+    partials (~1% of the call)."""
+    import torch
+    n = n_bytes // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    out = torch.empty((1,), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        ctx.stream_read(x, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ctx.stream_read(x, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ctx.check()
+    if float(out.item()) != float(n):
+        raise RuntimeError(f"stream read calibration summed {out.item()} for {n} ones")
+    return n_bytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
+
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "draft_chain_traffic_B128_V151936_r256_T1.json")
 
@@ -670,9 +695,13 @@ def main():
                 cb = 2.0 * B * G * (wl.d_h + wl.d_e)
                 per_kernel[name]["alg_bytes"] = cb
                 per_kernel[name]["alg_GBps"] = cb / (per_kernel[name]["avg_us"] * 1e-6) / 1e9
+        # what a plain read sustains on this part, for scale
+        stream_gbps = stream_read_peak(ctx)
+        print(f"[bench] streaming read: {stream_gbps:.1f} GB/s", file=sys.stderr, flush=True)
         for v in per_kernel.values():
             if "alg_GBps" in v:
                 v["frac_hbm"] = v["alg_GBps"] / HBM_PEAK_GBPS
+                v["frac_stream_read"] = v["alg_GBps"] / stream_gbps
         achieved = sw["alg_GBps"]
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -685,7 +714,9 @@ def main():
                                else "draft_sweep (MFMA GRU-state bias + vocabulary sweep, one position)"),
                     "alg_bytes_per_launch": b_sweep, "avg_launch_us": round(sw["avg_us"], 2),
                     "timing": sweep_timing,
-                    "mfma_util": round(sw["mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 5)}
+                    "mfma_util": round(sw["mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 5),
+                    "stream_read_GBps": round(stream_gbps, 1),
+                    "frac_of_stream_read": round(achieved / stream_gbps, 4)}
         print(f"[bench] kernels: " + ", ".join(f"{k} {v['avg_us']:.1f}us x{v['launches_per_step']:.0f}"
                                              for k, v in per_kernel.items()), file=sys.stderr, flush=True)
 

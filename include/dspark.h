@@ -480,6 +480,22 @@ int dspark_sts_fit(dspark_ctx* ctx, hipStream_t stream, int64_t N, int gamma,
                    const float* grid, int n_grid, int n_bins,
                    float* T, int32_t* index, double* ece);
 
+/* Streaming-read calibration (measurement support, not part of decoding).
+ *
+ * For benchmarks that relate the path's streaming kernels to what a plain
+ * read reaches on the device: out[0] = the float32 sum of x[0 .. n), every
+ * element read once in 16-byte loads (per-workgroup partials, then one
+ * workgroup adds them in a fixed order, so the result is the same on every
+ * call with the same n and device).  Timed over a buffer larger than the
+ * last-level cache it gives the read bandwidth the memory sustains.
+ *
+ * x: device, 16-byte aligned, n >= 0 floats (n = 0 writes 0); out: device,
+ * one float.  Uses the context's workspace for one float per workgroup.
+ * Two launches (timing class DSPARK_K_DIAG).  Errors: DSPARK_EINVAL for a
+ * null or misaligned pointer or n < 0; DSPARK_ENOMEM, DSPARK_EHIP as for
+ * the other calls. */
+int dspark_stream_read(dspark_ctx* ctx, hipStream_t stream, const float* x, int64_t n, float* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ EXPORTS = (
     "dspark_version", "dspark_create", "dspark_destroy", "dspark_last_error", "dspark_check",
     "dspark_draft_markov", "dspark_draft_markov_static", "dspark_draft_markov_conf", "dspark_draft_rnn",
     "dspark_confidence", "dspark_schedule", "dspark_schedule_async", "dspark_verify",
-    "dspark_verify_packed", "dspark_accept_prob", "dspark_sts_fit",
+    "dspark_verify_packed", "dspark_accept_prob", "dspark_sts_fit", "dspark_stream_read",
     "dspark_timing_enable", "dspark_timing_read",
 )
 KERNEL_CLASSES = ("draft_sweep", "draft_combine", "confidence", "survival", "schedule",
@@ -102,6 +102,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_sts_fit.restype = _i32
     lib.dspark_sts_fit.argtypes = [
         _vp, _vp, _i64, _i32, _vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp]
+    lib.dspark_stream_read.restype = _i32
+    lib.dspark_stream_read.argtypes = [_vp, _vp, _vp, _i64, _vp]
     if path is None:
         _lib = lib
     return lib
@@ -537,6 +539,20 @@ class Context:
             accept_len.data_ptr() if N > 0 else None, grid.data_ptr(), n_grid, int(n_bins),
             T.data_ptr(), idx.data_ptr(), ece.data_ptr()))
         return T, idx, ece
+
+    # -- dspark_stream_read (measurement support) -----------------------------------
+    def stream_read(self, x, out=None, stream=None):
+        """The float32 sum of a contiguous float32 tensor, every element read
+        once: the streaming-read calibration.  Returns out (float32 [1])."""
+        dev = self.device
+        _need(x, "x", torch.float32, dev)
+        if out is None:
+            out = torch.empty((1,), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.float32, dev, 1)
+        n = x.numel()
+        self._rc(self.lib.dspark_stream_read(self._h, _stream(dev, stream), x.data_ptr() if n > 0 else None, n,
+                                             out.data_ptr()))
+        return out
 
 
 __all__ = ["Context", "DSparkError", "load_library", "LIB_PATH", "EXPORTS", "KERNEL_CLASSES",

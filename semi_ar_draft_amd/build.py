@@ -16,7 +16,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libdspark.so")
-SOURCES = ["api.hip", "sweep.hip", "verify.hip", "confidence.hip", "schedule.hip", "gru.hip", "sts.hip"]
+SOURCES = ["api.hip", "sweep.hip", "verify.hip", "confidence.hip", "schedule.hip", "gru.hip", "sts.hip",
+           "stream.hip"]
 ARCH = os.environ.get("DSPARK_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [

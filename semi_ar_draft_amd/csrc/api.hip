@@ -1635,4 +1635,30 @@ int dspark_sts_fit(dspark_ctx* c, hipStream_t stream, int64_t N, int gamma, cons
   return DSPARK_OK;
 }
 
+int dspark_stream_read(dspark_ctx* c, hipStream_t stream, const float* x, int64_t n, float* out) {
+  TraceRange trace_range("dspark_stream_read");
+  if (!c) return DSPARK_EINVAL;
+  if (n < 0) return fail(c, DSPARK_EINVAL, "n must be >= 0");
+  if (!out || (n > 0 && !x)) return fail(c, DSPARK_EINVAL, "null pointer argument");
+  if (x && !aligned16(x)) return fail(c, DSPARK_EINVAL, "x must be 16-byte aligned");
+  DeviceGuard dg(c->device);
+  if (!dg.ok) return fail(c, DSPARK_EHIP, "hipSetDevice failed");
+  // sixteen workgroups per CU, fewer when there are not that many float4s
+  const int64_t n4 = n / 4;
+  const int64_t want = (n4 + kStreamThreads - 1) / kStreamThreads;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(16L * c->cu_count, want));
+  int rc;
+  if ((rc = ensure_ws(c, (size_t)grid * sizeof(float)))) return rc;
+  StreamArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.n = n;
+  a.n4 = n4;
+  a.partials = static_cast<float*>(c->ws);
+  a.n_part = grid;
+  a.out = out;
+  if ((rc = klaunch(c, DSPARK_K_DIAG, stream_read_kernel(), dim3(grid), dim3(kStreamThreads), &a, stream))) return rc;
+  return klaunch(c, DSPARK_K_DIAG, stream_sum_kernel(), dim3(1), dim3(kStreamThreads), &a, stream);
+}
+
 }  // extern "C"

@@ -267,4 +267,17 @@ const void* schedule_rank_kernel();
 constexpr int kSchedMaxKeys = 8192;
 constexpr int kSchedThreads = 1024;
 
+// Streaming-read calibration (stream.hip): the sum of n floats (x 16-byte
+// aligned), per-workgroup partials, then one workgroup sums them in order.
+struct StreamArgs {
+  const float* x;
+  int64_t n, n4;                 // floats, whole float4s
+  float* partials;               // [grid] of the read pass
+  int n_part;
+  float* out;
+};
+constexpr int kStreamThreads = 256;
+const void* stream_read_kernel();
+const void* stream_sum_kernel();
+
 }  // namespace dspark

@@ -661,17 +661,32 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 // loads cannot tell the slots of a ring apart and would wait for every load
 // in flight before each LDS read.  The kernels below order these loads
 // explicitly with ring_wait_barrier; the memory clobber keeps the compiler
-// from moving memory accesses across them.
+// from moving memory accesses across them.  kStream: a non-temporal load,
+// for rows read once (U, target rows), so that they do not displace what
+// the caches should keep (W2, re-read by every position, stays in the
+// last-level cache).
+template <bool kStream = false>
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds)
-      : "memory");
+  if constexpr (kStream) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(lds)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(lds)
+        : "memory");
+  }
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight,
@@ -992,7 +1007,7 @@ __global__ __launch_bounds__(64 * NW) void draft_chain_impl(const SweepArgs a0) 
 #pragma unroll
       for (int m = 0; m < kUInst; ++m) vcol[m] = min(t * kTileV + ucol_d[m], t1 * kTileV - 4);
 #pragma unroll
-      for (int m = 0; m < kUInst; ++m) dma16(a.U + uoff_d[m] + vcol[m], base + u_lds + m * 1024);
+      for (int m = 0; m < kUInst; ++m) dma16<true>(a.U + uoff_d[m] + vcol[m], base + u_lds + m * 1024);
     };
     auto load_tile = [&](int h, const unsigned char* sl, FragT (&A)[NS], float4 (&uu)[NBW]) {
       const unsigned char* row = sl + (h * kTileV + j) * kRowBytes;

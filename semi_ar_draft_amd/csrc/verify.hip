@@ -98,10 +98,15 @@ __device__ __forceinline__ void row_fold(RowState& st, RowLead& ld, const float4
 
 // One chunk of kRowsPer float4 per thread: every load is issued before the
 // first is used; float4 indices at or past c1 are skipped.  A Gumbel-max
-// leader becomes the key log2 w_b + m - log2 E_b at the end.
+// leader becomes the key log2 w_b + m - log2 E_b at the end.  The loads are
+// non-temporal: a target row is streamed once here.
 __device__ __forceinline__ void row_load(float4 (&x)[kRowsPer], const float4* p, int c0, int c1) {
 #pragma unroll
-  for (int i = 0; i < kRowsPer; ++i) x[i] = p[min(c0 + (int)threadIdx.x + i * kRowsThreads, c1 - 1)];
+  for (int i = 0; i < kRowsPer; ++i) {
+    const f32x4_t v = __builtin_nontemporal_load(
+        reinterpret_cast<const f32x4_t*>(p + min(c0 + (int)threadIdx.x + i * kRowsThreads, c1 - 1)));
+    x[i] = make_float4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 template <int KEYMODE>
