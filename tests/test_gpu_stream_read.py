@@ -39,3 +39,18 @@ def test_misaligned_pointer_is_refused(ctx):
     with pytest.raises(dk.DSparkError):
         ctx.stream_read(x[1:])
     ctx.check()
+
+
+def test_host_checks_through_the_c_abi(ctx):
+    lib = ctx.lib
+    out = torch.empty((1,), dtype=torch.float32, device="cuda")
+    x = torch.ones(64, dtype=torch.float32, device="cuda")
+    assert lib.dspark_stream_read(ctx._h, None, x.data_ptr(), -1, out.data_ptr()) == dk.DSPARK_EINVAL
+    assert lib.dspark_stream_read(ctx._h, None, x.data_ptr(), 64, None) == dk.DSPARK_EINVAL
+    assert lib.dspark_stream_read(ctx._h, None, None, 64, out.data_ptr()) == dk.DSPARK_EINVAL
+    assert lib.dspark_stream_read(None, None, x.data_ptr(), 64, out.data_ptr()) == dk.DSPARK_EINVAL
+    # n = 0 with no buffer writes 0
+    out.fill_(7.0)
+    assert lib.dspark_stream_read(ctx._h, None, None, 0, out.data_ptr()) == dk.DSPARK_OK
+    ctx.check()
+    assert out.item() == 0.0
