@@ -307,14 +307,14 @@ def schedule_bench(args):
     and dspark_schedule_async (capacity from survivals of an earlier step,
     global search) on synthetic survival rows (each row gamma = 7 sorted
     uniforms) and the 4096-entry SPS table of the scheduled workload, over
-    batch sizes up to the library's B * gamma <= 4096.  Each size is first
-    checked against the oracle (K, n exact, theta to 1e-12), then timed over
-    a block of calls between events.  value = the synchronous call at
-    B = 512 (the scheduled workload)."""
+    batch sizes up to the library's B * gamma <= 4096, each timed over a
+    block of calls between events.  The cpu_baseline leg (unless
+    --no-cpu-baseline) times the oracle on the same inputs and compares its
+    K, n and theta with the library's (exact, theta to 1e-12).  value = the
+    synchronous call at B = 512 (the scheduled workload)."""
     import numpy as np
     import torch
     import synth
-    import oracle
     import semi_ar_draft_amd as dk
 
     G = 7
@@ -336,18 +336,6 @@ def schedule_bench(args):
                     ctx.schedule(sd, sps_d, out=out)
                 else:
                     ctx.schedule_async(sd, hd, sps_d, out=out)
-            call()
-            ctx.check()
-            cpu_s = float("inf")
-            for _ in range(3):                                 # the fastest of three oracle calls
-                t0 = time.perf_counter()
-                ref = oracle.schedule(surv.numpy(), sps.numpy()) if mode == "sync" else \
-                    oracle.schedule_async(surv.numpy(), hist.numpy(), sps.numpy())
-                cpu_s = min(cpu_s, time.perf_counter() - t0)
-            same = (np.array_equal(out[0].cpu().numpy().astype(np.int64), ref.K)
-                    and int(out[1].item()) == ref.n_selected
-                    and abs(float(out[2].item()) - ref.theta) <= 1e-12 * abs(ref.theta))
-            ok = ok and same
             for _ in range(max(args.warmup, 1)):
                 call()
             torch.cuda.synchronize()
@@ -359,13 +347,27 @@ def schedule_bench(args):
             e1.record()
             torch.cuda.synchronize()
             ctx.check()
-            rec[mode] = {"us_per_call": round(1e3 * e0.elapsed_time(e1) / n, 2), "n_selected": ref.n_selected,
-                         "matches_oracle": same, "oracle_ms_per_call": round(1e3 * cpu_s, 2)}
+            rec[mode] = {"us_per_call": round(1e3 * e0.elapsed_time(e1) / n, 2),
+                         "n_selected": int(out[1].item())}
+            if not args.no_cpu_baseline:
+                import oracle
+                cpu_s = float("inf")
+                for _ in range(3):                             # the fastest of three oracle calls
+                    t0 = time.perf_counter()
+                    ref = oracle.schedule(surv.numpy(), sps.numpy()) if mode == "sync" else \
+                        oracle.schedule_async(surv.numpy(), hist.numpy(), sps.numpy())
+                    cpu_s = min(cpu_s, time.perf_counter() - t0)
+                same = (np.array_equal(out[0].cpu().numpy().astype(np.int64), ref.K)
+                        and int(out[1].item()) == ref.n_selected
+                        and abs(float(out[2].item()) - ref.theta) <= 1e-12 * abs(ref.theta))
+                ok = ok and same
+                rec[mode].update({"matches_oracle": same, "oracle_ms_per_call": round(1e3 * cpu_s, 2)})
         rows.append(rec)
         print(f"[bench] schedule B={B}: sync {rec['sync']['us_per_call']} us, async {rec['async']['us_per_call']} us",
               file=sys.stderr, flush=True)
     ctx.close()
-    v = next(r for r in rows if r["B"] == 512)["sync"]["us_per_call"]
+    at512 = next(r for r in rows if r["B"] == 512)["sync"]
+    v = at512["us_per_call"]
     line = {
         "metric": "prefix scheduler call time (B x gamma candidates, 4096-entry SPS table)",
         "value": v, "unit": "us per call", "n_gpus": 1, "steps": n, "warmup": max(args.warmup, 1),
@@ -373,39 +375,14 @@ def schedule_bench(args):
         "dtype": "f32 survivals, f64 scan", "data": "synthetic",
         "config": {"workload": "schedule: gamma=7, SPS 4096 entries, B in {128, 512, 585}", "gamma": G},
         "sizes": rows,
-        "cpu_baseline": {"value": next(r for r in rows if r["B"] == 512)["sync"]["oracle_ms_per_call"] * 1e3,
-                         "unit": "us per call", "cores": 1, "kind": "oracle",
-                         "sample": "one synchronous call at B = 512 on the same input, fastest of three"},
-        "parity_ok": ok,
+        "cpu_baseline": None if args.no_cpu_baseline else
+        {"value": at512["oracle_ms_per_call"] * 1e3, "unit": "us per call", "cores": 1, "kind": "oracle",
+         "sample": "one synchronous call at B = 512 on the same input, fastest of three"},
+        "parity_ok": None if args.no_cpu_baseline else ok,
     }
     print(json.dumps(line), flush=True)
     if not ok:
         sys.exit(1)
-
-
-def stream_read_peak(ctx, n_bytes: int = 1 << 30, reps: int = 10) -> float:
-    """Read bandwidth (GB/s) of the library's streaming-read calibration over
-    a buffer four times the 256 MB last-level cache, so that every pass
-    reads from HBM; each call also runs its one-workgroup sum of the
-    partials (~1% of the call)."""
-    import torch
-    n = n_bytes // 4
-    x = torch.ones(n, dtype=torch.float32, device="cuda")
-    out = torch.empty((1,), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        ctx.stream_read(x, out=out)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        ctx.stream_read(x, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    ctx.check()
-    if float(out.item()) != float(n):
-        raise RuntimeError(f"stream read calibration summed {out.item()} for {n} ones")
-    return n_bytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
 
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
