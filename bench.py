@@ -385,6 +385,31 @@ def schedule_bench(args):
         sys.exit(1)
 
 
+def stream_read_peak(ctx, n_bytes: int = 1 << 30, reps: int = 10) -> float:
+    """Read bandwidth (GB/s) of the library's streaming-read calibration over
+    a buffer four times the 256 MB last-level cache, so that every pass
+    reads from HBM; each call also runs its one-workgroup sum of the
+    partials (~1% of the call)."""
+    import torch
+    n = n_bytes // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    out = torch.empty((1,), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        ctx.stream_read(x, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ctx.stream_read(x, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ctx.check()
+    if float(out.item()) != float(n):
+        raise RuntimeError(f"stream read calibration summed {out.item()} for {n} ones")
+    return n_bytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
+
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "draft_chain_traffic_B128_V151936_r256_T1.json")
 

@@ -31,3 +31,38 @@ def test_measurement_modes_refuse_more_than_one_gpu():
                            capture_output=True, text=True, timeout=120)
         assert p.returncode == 2, mode
         assert "one GPU" in p.stderr
+
+
+def test_every_called_name_is_defined():
+    """Every plain name bench.py calls is a builtin, a module-level name, or
+    bound inside the calling function (its imports, nested defs, assignments)."""
+    import ast
+    import builtins
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    top = set()
+    for n in tree.body:
+        if isinstance(n, (ast.FunctionDef, ast.ClassDef)):
+            top.add(n.name)
+        elif isinstance(n, (ast.Import, ast.ImportFrom)):
+            top.update((a.asname or a.name).split(".")[0] for a in n.names)
+        elif isinstance(n, ast.Assign):
+            top.update(t.id for t in n.targets if isinstance(t, ast.Name))
+    missing = []
+    for fn in [n for n in tree.body if isinstance(n, ast.FunctionDef)]:
+        bound = set()
+        for n in ast.walk(fn):
+            if isinstance(n, (ast.FunctionDef, ast.Lambda)) and n is not fn:
+                if isinstance(n, ast.FunctionDef):
+                    bound.add(n.name)
+            elif isinstance(n, (ast.Import, ast.ImportFrom)):
+                bound.update((a.asname or a.name).split(".")[0] for a in n.names)
+            elif isinstance(n, ast.Name) and isinstance(n.ctx, ast.Store):
+                bound.add(n.id)
+            elif isinstance(n, ast.arg):
+                bound.add(n.arg)
+        for n in ast.walk(fn):
+            if isinstance(n, ast.Call) and isinstance(n.func, ast.Name):
+                name = n.func.id
+                if name not in bound and name not in top and not hasattr(builtins, name):
+                    missing.append(f"{fn.name} calls {name}")
+    assert not missing, missing
