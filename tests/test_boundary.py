@@ -77,6 +77,12 @@ def test_null_context_is_rejected_everywhere():
     assert lib.dspark_draft_rnn(None, None, 1, 1, 16, 32, 1, None, 16, 16, None, None, None, None, None,
                                 None, None, None, 0.0, 0, None, None, None, None) == dk.DSPARK_EINVAL
     assert lib.dspark_sts_fit(None, None, 1, 1, None, 1, None, None, 1, 1, None, None, None) == dk.DSPARK_EINVAL
+    assert lib.dspark_stream_read(None, None, None, 0, None) == dk.DSPARK_EINVAL
+    assert lib.dspark_draft_markov_static(None, None, 1, 1, 16, 32, 1, None, 16, 16, None, None, None,
+                                          None, 0.0, 0, None, None, None) == dk.DSPARK_EINVAL
+    assert lib.dspark_draft_markov_conf(None, None, 1, 1, 16, 32, 1, None, 16, 16, None, None, None, None, 0.0, 0,
+                                        8, 8, None, None, None, 0.0, None, None, None, None, None,
+                                        None) == dk.DSPARK_EINVAL
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU device node is present")
